@@ -1,0 +1,135 @@
+"""fp64 CPU oracle for the selective state-space scan.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  Nothing in the product package imports
+this module, and this module imports nothing from the product package.
+
+Two implementations of the same definition live here:
+
+* ``jscan_oracle.c`` (loaded through ctypes): the sequential fp64 loop, threaded
+  over independent (batch, channel) pairs.  ``prefill`` and ``step`` are written
+  separately in C.
+* ``twin.py``: the same loop in numpy, vectorised over channels only, for
+  small shapes and as a cross-check of the C code.
+
+The definition they follow (see the header of ``jscan_oracle.c``) is the
+state-space recurrence of the "AI Engineering from Scratch" Jamba lesson,
+section "一页讲完 SSM", with data-dependent (selective) parameters, a real
+diagonal A per (channel, state) as in Mamba-1, exp(delta*A) decay, the
+delta*B*x input term, the D skip and the SiLU(z) gate on the whole output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "jscan_oracle.c")
+_LIB = os.path.join(_HERE, "libjscan_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+               "-shared", "-fPIC", "-std=c11", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i64 = ctypes.c_int64
+            lib.oracle_prefill.argtypes = [i64, i64, i64, i64] + [dp] * 10
+            lib.oracle_prefill.restype = None
+            lib.oracle_step.argtypes = [i64, i64, i64] + [dp] * 9
+            lib.oracle_step.restype = None
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
+            _lib = lib
+    return _lib
+
+
+def _f64(a, shape, name):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {a.shape}, expected {shape}")
+    return a
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+def prefill(x, delta, A, B, C, D, z, h0=None, want_state=True):
+    """Sequential fp64 scan.
+
+    x, delta, z: [batch, L, d_inner]; B, C: [batch, L, d_state];
+    A: [d_inner, d_state]; D: [d_inner]; h0: [batch, d_inner, d_state] or None.
+    Returns (y [batch, L, d_inner], hT [batch, d_inner, d_state] or None), float64.
+    """
+    x = np.asarray(x)
+    batch, L, d_inner = x.shape
+    d_state = np.asarray(A).shape[1]
+    if d_state > 256:
+        raise ValueError("oracle supports d_state <= 256")
+    x = _f64(x, (batch, L, d_inner), "x")
+    delta = _f64(delta, (batch, L, d_inner), "delta")
+    z = _f64(z, (batch, L, d_inner), "z")
+    A = _f64(A, (d_inner, d_state), "A")
+    B = _f64(B, (batch, L, d_state), "B")
+    C = _f64(C, (batch, L, d_state), "C")
+    D = _f64(D, (d_inner,), "D")
+    h0 = None if h0 is None else _f64(h0, (batch, d_inner, d_state), "h0")
+    y = np.empty((batch, L, d_inner), dtype=np.float64)
+    hT = np.empty((batch, d_inner, d_state), dtype=np.float64) if want_state else None
+    _load().oracle_prefill(batch, L, d_inner, d_state, _ptr(x), _ptr(delta), _ptr(A),
+                           _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hT))
+    return y, hT
+
+
+def step(state, x, delta, A, B, C, D, z):
+    """One decode token for n_seq sequences.
+
+    state: [n_seq, d_inner, d_state] (not modified; the updated state is returned);
+    x, delta, z: [n_seq, d_inner]; B, C: [n_seq, d_state].
+    Returns (y [n_seq, d_inner], new_state), float64.
+    """
+    state = np.array(state, dtype=np.float64, copy=True, order="C")
+    n_seq, d_inner, d_state = state.shape
+    x = _f64(x, (n_seq, d_inner), "x")
+    delta = _f64(delta, (n_seq, d_inner), "delta")
+    z = _f64(z, (n_seq, d_inner), "z")
+    A = _f64(A, (d_inner, d_state), "A")
+    B = _f64(B, (n_seq, d_state), "B")
+    C = _f64(C, (n_seq, d_state), "C")
+    D = _f64(D, (d_inner,), "D")
+    y = np.empty((n_seq, d_inner), dtype=np.float64)
+    _load().oracle_step(n_seq, d_inner, d_state, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                        _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y))
+    return y, state

@@ -1,0 +1,133 @@
+/*
+ * jscan_oracle.c -- plain, slow, sequential fp64 CPU oracle for the selective
+ * state-space scan (prefill) and its one-token decode update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library it checks.
+ *
+ * What it computes (all arithmetic in double, std C `exp`):
+ *
+ *   Recurrence of a state-space model with a fixed-size state h, per token:
+ *   new state = decay * old state + input term, output = C . state
+ *   ("AI Engineering from Scratch" Jamba lesson, section "一页讲完 SSM": the
+ *   SSM h_t = A h_{t-1} + B x_t, y_t = C h_t; "selective" means A, B, C
+ *   depend on the token, section "关键术语", entry "选择性 SSM").
+ *   A is real and diagonal per (channel d, state n) as in Mamba-1
+ *   (same lesson, section "Mamba-3", complex-state paragraph; exercise 2 says
+ *   Jamba uses Mamba-1).  Discretisation: the decay is exp(delta * A[d][n])
+ *   and the input term is delta * B[n] * x ("Euler" on the input, same lesson,
+ *   Mamba-3 paragraph on exponential-trapezoidal discretisation).  The output
+ *   adds the D skip and is multiplied by SiLU(z) = z / (1 + exp(-z)); the
+ *   pages are silent on where the gate sits and the reading taken is that it
+ *   multiplies the whole output, skip included.
+ *
+ *   For each batch b and channel d:
+ *     h[n] = h0[b][d][n]            (0 when h0 is NULL)
+ *     for t in 0..L-1:
+ *       dt = delta[b][t][d]; xv = x[b][t][d]; acc = 0
+ *       for n in 0..N-1:
+ *         h[n] = exp(dt * A[d][n]) * h[n] + dt * B[b][t][n] * xv
+ *         acc += C[b][t][n] * h[n]
+ *       zv = z[b][t][d]
+ *       y[b][t][d] = (acc + Dv[d] * xv) * zv / (1 + exp(-zv))
+ *     hT[b][d][n] = h[n]            (when hT is not NULL)
+ *
+ * Layouts (dense, row-major):
+ *   x, delta, z, y : [batch][L][d_inner]
+ *   B, C           : [batch][L][d_state]
+ *   A              : [d_inner][d_state];   Dv : [d_inner]
+ *   h0, hT, state  : [batch][d_inner][d_state]
+ *
+ * The prefill loop is parallelised over independent (b, d) channels with
+ * OpenMP; each channel's arithmetic is the sequential loop above, in that
+ * order, so the result does not depend on the thread count.
+ *
+ * oracle_step is written on its own (not by calling oracle_prefill) so that
+ * "the final state of a prefill equals T chained steps" is a real check of
+ * two pieces of code.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* Prefill: the scan over L tokens for every (b, d) channel. */
+void oracle_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                    const double* x, const double* delta, const double* A,
+                    const double* B, const double* C, const double* Dv,
+                    const double* z, const double* h0, double* y, double* hT) {
+  int64_t channels = batch * d_inner;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t bd = 0; bd < channels; ++bd) {
+    int64_t b = bd / d_inner;
+    int64_t d = bd % d_inner;
+    double h[256];
+    for (int64_t n = 0; n < d_state; ++n)
+      h[n] = h0 ? h0[(b * d_inner + d) * d_state + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      int64_t i = (b * L + t) * d_inner + d;     /* element (b, t, d) */
+      const double* Bt = B + (b * L + t) * d_state;
+      const double* Ct = C + (b * L + t) * d_state;
+      double dt = delta[i];
+      double xv = x[i];
+      double acc = 0.0;
+      for (int64_t n = 0; n < d_state; ++n) {
+        h[n] = exp(dt * A[d * d_state + n]) * h[n] + dt * Bt[n] * xv;
+        acc += Ct[n] * h[n];
+      }
+      double zv = z[i];
+      y[i] = (acc + Dv[d] * xv) * zv / (1.0 + exp(-zv));
+    }
+    if (hT)
+      for (int64_t n = 0; n < d_state; ++n)
+        hT[(b * d_inner + d) * d_state + n] = h[n];
+  }
+}
+
+/*
+ * Decode step: one token for each of n_seq independent sequences, the state
+ * updated in place.  x, delta, z, y : [n_seq][d_inner];  B, C : [n_seq][d_state];
+ * state : [n_seq][d_inner][d_state].
+ */
+void oracle_step(int64_t n_seq, int64_t d_inner, int64_t d_state, double* state,
+                 const double* x, const double* delta, const double* A,
+                 const double* B, const double* C, const double* Dv,
+                 const double* z, double* y) {
+  for (int64_t s = 0; s < n_seq; ++s) {
+    for (int64_t d = 0; d < d_inner; ++d) {
+      double* h = state + (s * d_inner + d) * d_state;
+      double dt = delta[s * d_inner + d];
+      double xv = x[s * d_inner + d];
+      double acc = 0.0;
+      for (int64_t n = 0; n < d_state; ++n) {
+        double decay = exp(dt * A[d * d_state + n]);
+        double input = dt * B[s * d_state + n] * xv;
+        h[n] = decay * h[n] + input;
+        acc += C[s * d_state + n] * h[n];
+      }
+      double zv = z[s * d_inner + d];
+      double silu = zv / (1.0 + exp(-zv));
+      y[s * d_inner + d] = (acc + Dv[d] * xv) * silu;
+    }
+  }
+}
