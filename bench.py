@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark: the selective-scan prefill at the Jamba shape with a 64K context.
+
+One step = one jscan_prefill call over batch 1, L = 65536 tokens, d_inner 8192,
+d_state 16, bf16 I/O (fp32 state and arithmetic), inputs resident in HBM.
+Reports channel-tokens/s (batch * L * d_inner per second), the fraction of the
+MI355X HBM roofline those algorithmic bytes reach, the roofline of the main
+scan kernel (timed on its own with HIP events recorded by the library on the
+launch stream), a decode-step measurement (256 sequences), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+VALU_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, FMA = 2 flops
+D_STATE = 16
+
+# Algorithmic VALU issue slots per channel-token of the scan (one slot = one
+# fp32 FMA lane-op; a transcendental v_exp_f32 / v_rcp_f32 costs 4 slots, as
+# measured on gfx950): per state, delta*A' (1) + exp2 (4) + (delta*x)*B (1) +
+# state FMA (1) + C*h FMA (1) = 8, times 16 states = 128; per channel-token,
+# delta*x (1), the D skip FMA (1), SiLU(z) = z * rcp(1 + exp2(-z log2 e))
+# (mul 1 + exp 4 + add 1 + rcp 4 + mul 1) and the gate multiply (1) = 14.
+SLOTS_PER_CHTOK = 16 * 8 + 14
+
+
+def alg_bytes_prefill(batch, L, d_inner, io_bytes=2, h0=False, hT=True):
+    tok = batch * L * d_inner * io_bytes * 4           # x, delta, z in; y out
+    rows = batch * L * D_STATE * io_bytes * 2          # B, C
+    params = d_inner * D_STATE * 4 + d_inner * 4       # A, D
+    state = batch * d_inner * D_STATE * 4 * ((1 if h0 else 0) + (1 if hT else 0))
+    return tok + rows + params + state
+
+
+def alg_bytes_step(n_seq, d_inner, io_bytes=2):
+    return (2 * n_seq * d_inner * D_STATE * 4 + n_seq * d_inner * io_bytes * 4
+            + n_seq * D_STATE * io_bytes * 2 + d_inner * D_STATE * 4 + d_inner * 4)
+
+
+def source_digest():
+    p = os.path.join(ROOT, "selective_state_space_11_amd", "csrc", "jscan.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_tag):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_tag)
+    if not ent or ent.get("source_sha") != source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--L", type=int, default=65536)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import selective_state_space_11_amd as js
+
+    if not os.path.exists(js.LIB_PATH):
+        from __graft_entry__ import build
+        build()
+    js.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    batch, L, d_inner = 1, args.L, 8192
+    t_gen = time.time()
+    inp = synth.prefill_inputs(batch, L, d_inner, seed=2, io=synth.IO_BF16)
+    log(f"[bench] generated inputs in {time.time() - t_gen:.1f}s")
+
+    def dio(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+    x, delta, z, B, C = (dio(inp[k]) for k in ("x", "delta", "z", "B", "C"))
+    A = torch.from_numpy(inp["A"]).to(dev)
+    D = torch.from_numpy(inp["D"]).to(dev)
+    y = torch.empty_like(x)
+    hT = torch.empty(batch, d_inner, D_STATE, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, js.workspace_size(batch, L, d_inner)), dtype=torch.uint8, device=dev)
+    K, chunks = js.plan(batch, L, d_inner)
+
+    def step():
+        js.prefill(x, delta, A, B, C, D, z, None, y=y, hT=hT, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done (plan: {K} waves per 64 channels, {chunks} chunks)")
+
+    # whole-step timing
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # main scan kernel alone: events recorded by the library around its launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        js.time_next_prefill(a, b)
+        step()
+    torch.cuda.synchronize()
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    log(f"[bench] step {ms_per_step:.4f} ms, main scan kernel {scan_ms:.4f} ms")
+
+    chtok = batch * L * d_inner
+    value = chtok / (ms_per_step * 1e-3)
+    abytes = alg_bytes_prefill(batch, L, d_inner)
+    hbm_gbs = abytes / (ms_per_step * 1e-3) / 1e9
+    kern_tflops = chtok * SLOTS_PER_CHTOK * 2 / (scan_ms * 1e-3) / 1e12
+    traffic = load_traffic("k_scan_64k")
+
+    # decode: 256 sequences x 8192 channels, one token each, state in place
+    n_seq = 256
+    st = torch.from_numpy(synth.decode_state(n_seq, d_inner, seed=3)).to(dev)
+    di = synth.decode_inputs(n_seq, d_inner, seed=3, step=0)
+    dx, dd, dz, dB, dC = (dio(di[k]) for k in ("x", "delta", "z", "B", "C"))
+    Ad, Dd, _ = synth.params(d_inner, seed=3)
+    Ad, Dd = torch.from_numpy(Ad).to(dev), torch.from_numpy(Dd).to(dev)
+    yd = torch.empty_like(dx)
+    for _ in range(10):
+        js.step_batch(st, dx, dd, Ad, dB, dC, Dd, dz, y=yd)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.decode_steps):
+        js.step_batch(st, dx, dd, Ad, dB, dC, Dd, dz, y=yd)
+    e1.record()
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    dec_bytes = alg_bytes_step(n_seq, d_inner)
+    decode = {"workload": "decode step, 256 sequences x d_inner 8192, state in place",
+              "us_per_step": round(us_step, 3),
+              "channel_tokens_per_s": n_seq * d_inner / (us_step * 1e-6),
+              "alg_GBps": round(dec_bytes / (us_step * 1e-6) / 1e9, 1),
+              "hbm_frac": round(dec_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+              "note": "the 128 MiB state can stay resident in the 256 MB last-level cache"}
+    log(f"[bench] decode {us_step:.2f} us/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n_ch = 2048
+        chans = np.arange(0, d_inner, d_inner // n_ch)[:n_ch]
+        sub = synth.channel_slice(inp, chans)
+        t0 = time.time()
+        oracle.prefill(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], None)
+        dt = time.time() - t0
+        cpu = {"value": n_ch * L / dt, "unit": "channel-tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{n_ch} of the {d_inner} channels (every {d_inner // n_ch}th) over all {L} tokens "
+                         f"of the same inputs; fp64 C oracle, {dt:.2f} s wall"}
+        log(f"[bench] cpu oracle {cpu['value']:.3e} ch-tok/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "channel-tokens/s and % HBM roofline, d_inner=8192 N=16 @ 64K ctx",
+        "value": value,
+        "unit": "channel-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"selective-scan prefill, batch {batch}, L {L}, d_inner {d_inner}, "
+                               f"d_state 16, bf16 I/O, fp32 state",
+                   "batch": batch, "seq_len": L, "d_inner": d_inner, "d_state": D_STATE,
+                   "plan": {"waves_per_64_channels": K, "chunks": chunks}},
+        "hbm_roofline": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_step": abytes},
+        "roofline": {"bound": "alu", "kernel": "k_scan (main scan)",
+                     "achieved": round(kern_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kern_tflops / VALU_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(scan_ms, 4),
+                     "work": f"{SLOTS_PER_CHTOK} fp32 VALU slots (x2 flop) per channel-token, "
+                             f"{chtok} channel-tokens per launch"},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

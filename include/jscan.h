@@ -1,0 +1,160 @@
+/*
+ * libjscan -- selective state-space scan for AMD MI355X (gfx950).
+ *
+ * The operation is the recurrence of a state-space model with a fixed-size
+ * state, made selective by per-token parameters ("AI Engineering from Scratch",
+ * Jamba lesson, section "一页讲完 SSM", and its glossary entry for the selective
+ * SSM): for every sequence b, channel d and state index n,
+ *
+ *     h[t][n] = exp(delta[t][d] * A[d][n]) * h[t-1][n] + delta[t][d] * B[t][n] * x[t][d]
+ *     y[t][d] = (sum_n C[t][n] * h[t][n] + D[d] * x[t][d]) * SiLU(z[t][d])
+ *
+ * with SiLU(v) = v / (1 + exp(-v)).  A is real and diagonal per (channel,
+ * state), as in the Mamba-1 layers that make up seven of every eight layers of
+ * Jamba (Jamba lesson, sections "Jamba 块" and "Mamba-3"; the Jamba report by
+ * zako-mio, section 2.1).  The decay exp(delta*A) and the input term
+ * delta*B*x are the discretisation the pages call "Euler" for the input; the
+ * gate multiplies the whole output, D skip included.  A prefill scans a whole
+ * sequence; a decode step advances the state by one token, and the state is
+ * carried from the prefill into decoding (ksqn.cn blog, section 4.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array argument is a DEVICE pointer into dense, row-major memory,
+ *    owned by the caller.  The library keeps no pointer after a call returns.
+ *  - `io` gives the element type of x, delta, z, B, C and y: JSCAN_IO_BF16
+ *    (bfloat16 bit patterns, converted to fp32 exactly on load, rounded to
+ *    nearest-even on store) or JSCAN_IO_F32.  A, D and every state array are
+ *    always fp32; the arithmetic is fp32 throughout.
+ *  - d_state must be 16 (the Mamba state width of the pages); other values
+ *    return JSCAN_ERR_UNSUPPORTED.
+ *  - Every pointer must be 16-byte aligned (JSCAN_ERR_ALIGN otherwise).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; a call returns once the work is enqueued.
+ *  - Arguments are validated on the host before anything is enqueued.  On an
+ *    error nothing is launched and no output is written.  Faults during
+ *    execution surface at the caller's next synchronisation, as for any HIP
+ *    kernel.  NaN and Inf inputs are not checked: they propagate through the
+ *    arithmetic of the channel they belong to.
+ *  - Calls are thread-safe; concurrent calls on different streams must not
+ *    share output buffers or workspace.
+ */
+#ifndef JSCAN_H
+#define JSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JSCAN_OK = 0,
+  JSCAN_ERR_NULL = 1,        /* a required pointer is NULL */
+  JSCAN_ERR_SHAPE = 2,       /* a size is negative, or sizes overflow 64-bit byte counts */
+  JSCAN_ERR_UNSUPPORTED = 3, /* d_state != 16, or unknown io */
+  JSCAN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  JSCAN_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
+  JSCAN_ERR_WORKSPACE = 6,   /* workspace given but smaller than required */
+  JSCAN_ERR_HIP = 7          /* a HIP runtime call failed (see jscan_last_error) */
+} jscan_status;
+
+typedef enum { JSCAN_IO_F32 = 0, JSCAN_IO_BF16 = 1 } jscan_io;
+
+/*
+ * Bytes of device workspace jscan_prefill needs for this problem.  It depends
+ * only on the sizes.  Returns 0 for an invalid size combination.
+ */
+size_t jscan_prefill_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                                    jscan_io io);
+
+/*
+ * Prefill: the scan over L tokens of `batch` independent sequences.
+ *
+ *   x, delta, z : [batch][L][d_inner]   (io)   inputs; delta is used as given
+ *                                              (no softplus or bias inside)
+ *   B, C        : [batch][L][d_state]   (io)   per-token rows shared by all channels
+ *   A           : [d_inner][d_state]    fp32   decay rates (any finite value)
+ *   D           : [d_inner]             fp32   skip weights
+ *   h0          : [batch][d_inner][d_state] fp32, or NULL for a zero initial state
+ *   y           : [batch][L][d_inner]   (io)   output
+ *   hT          : [batch][d_inner][d_state] fp32 final state, or NULL.  hT may be
+ *                 the same pointer as h0 (in-place carry); any other overlap
+ *                 with an input or with y is JSCAN_ERR_ALIAS.
+ *   workspace   : device scratch of at least jscan_prefill_workspace_size()
+ *                 bytes, or NULL (the library then allocates and frees
+ *                 stream-ordered scratch itself).  Its contents on entry do
+ *                 not matter; it must not overlap any other argument.
+ *
+ * batch, L or d_inner may be 0: then nothing is computed, and if L == 0 the
+ * final state hT is h0 (or zeros).  Sizes must be >= 0 (JSCAN_ERR_SHAPE).
+ * Calling the prefill on consecutive pieces of a sequence, passing each
+ * piece's hT as the next piece's h0, computes the scan of the whole sequence.
+ */
+jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                           const void* x, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* h0,
+                           void* y, float* hT, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Decode step for one sequence: one token, state updated in place.
+ *
+ *   state : [d_inner][d_state] fp32, read and overwritten with the new state
+ *   x, delta, z, y : [d_inner] (io);  B, C : [d_state] (io);  A, D as above.
+ *   y must not overlap any input or the state.
+ */
+jscan_status jscan_step(int64_t d_inner, int64_t d_state, jscan_io io, float* state,
+                        const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, void* y, void* stream);
+
+/*
+ * Decode step for n_seq independent sequences (one token each), states updated
+ * in place.
+ *
+ *   state : [n_seq][d_inner][d_state] fp32
+ *   x, delta, z, y : [n_seq][d_inner] (io);  B, C : [n_seq][d_state] (io)
+ *   A, D shared by all sequences, as above.
+ */
+jscan_status jscan_step_batch(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
+                              float* state, const void* x, const void* delta, const float* A,
+                              const void* B, const void* C, const float* D, const void* z,
+                              void* y, void* stream);
+
+/* Static name of a status code. */
+const char* jscan_status_string(jscan_status status);
+
+/* Text of the last error reported on the calling thread ("" if none). */
+const char* jscan_last_error(void);
+
+/*
+ * Launch plan the prefill uses for these sizes: the number of waves that share
+ * one group of 64 channels (each owning 16/waves states) and the number of
+ * sequence chunks scanned in parallel (1 = single pass; more = chunk-local
+ * pass, carry combine, and rescan).  Returns JSCAN_ERR_SHAPE for invalid sizes.
+ */
+jscan_status jscan_prefill_plan(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                                int* waves_per_group, int* chunks);
+
+/*
+ * Override the launch plan for the prefill calls (and workspace sizes) of the
+ * calling thread: waves_per_group in {1, 2, 4, 8}, chunks >= 1 (clamped to L).
+ * (0, 0) restores the automatic plan.  Results do not depend on the plan
+ * beyond floating-point rounding; this exists to test and tune every variant.
+ */
+jscan_status jscan_set_plan_override(int waves_per_group, int chunks);
+
+/*
+ * Measurement hook.  When both events are non-NULL, the next jscan_prefill
+ * call on this thread records `before` on its stream immediately before
+ * launching its main scan kernel and `after` immediately after it, then
+ * forgets the events.  Arguments are hipEvent_t handles.
+ */
+void jscan_time_next_prefill(void* before, void* after);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JSCAN_H */

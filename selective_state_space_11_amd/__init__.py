@@ -1,0 +1,227 @@
+"""Python binding of libjscan (selective state-space scan on MI355X).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libjscan.so``.  torch supplies device memory and the current HIP stream.
+The library must be built (``python -m selective_state_space_11_amd.build`` or
+``__graft_entry__.build()``); importing works without it, but every call then
+raises ``JscanUnavailable`` -- there is no fallback implementation.
+
+Entry points mirror the C ABI in ``include/jscan.h``:
+
+* ``prefill(x, delta, A, B, C, D, z, h0=None)`` -> ``(y, hT)``
+* ``step(state, x, delta, A, B, C, D, z)`` -> ``y`` (state updated in place)
+* ``step_batch(state, x, delta, A, B, C, D, z)`` -> ``y`` (states updated in place)
+* ``workspace_size``, ``plan``, ``set_plan_override``, ``time_next_prefill``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libjscan.so")
+D_STATE = 16
+
+JSCAN_OK = 0
+STATUS_NAMES = {0: "JSCAN_OK", 1: "JSCAN_ERR_NULL", 2: "JSCAN_ERR_SHAPE", 3: "JSCAN_ERR_UNSUPPORTED",
+                4: "JSCAN_ERR_ALIGN", 5: "JSCAN_ERR_ALIAS", 6: "JSCAN_ERR_WORKSPACE", 7: "JSCAN_ERR_HIP"}
+IO_F32, IO_BF16 = 0, 1
+
+EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_step", "jscan_step_batch",
+           "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
+           "jscan_set_plan_override", "jscan_time_next_prefill")
+
+
+class JscanUnavailable(RuntimeError):
+    """libjscan.so is not built or cannot be loaded."""
+
+
+class JscanError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libjscan.so and declare its C signatures (no GPU work)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise JscanUnavailable(f"{path} is not built; run `python -m selective_state_space_11_amd.build`")
+        try:
+            lib = ctypes.CDLL(path)
+        except OSError as e:
+            raise JscanUnavailable(f"cannot load {path}: {e}") from e
+        i64, vp, sz, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        fp = ctypes.c_void_p
+        lib.jscan_prefill_workspace_size.argtypes = [i64, i64, i64, i64, st]
+        lib.jscan_prefill_workspace_size.restype = sz
+        lib.jscan_prefill.argtypes = [i64, i64, i64, i64, st, vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, vp, sz, vp]
+        lib.jscan_prefill.restype = st
+        lib.jscan_step.argtypes = [i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, vp]
+        lib.jscan_step.restype = st
+        lib.jscan_step_batch.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, vp]
+        lib.jscan_step_batch.restype = st
+        lib.jscan_status_string.argtypes = [st]
+        lib.jscan_status_string.restype = ctypes.c_char_p
+        lib.jscan_last_error.argtypes = []
+        lib.jscan_last_error.restype = ctypes.c_char_p
+        lib.jscan_prefill_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_int)]
+        lib.jscan_prefill_plan.restype = st
+        lib.jscan_set_plan_override.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.jscan_set_plan_override.restype = st
+        lib.jscan_time_next_prefill.argtypes = [vp, vp]
+        lib.jscan_time_next_prefill.restype = None
+        _lib = lib
+        return lib
+
+
+def _check(status):
+    if status != JSCAN_OK:
+        msg = load_library().jscan_last_error().decode()
+        raise JscanError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_of(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return IO_BF16
+    if t.dtype == torch.float32:
+        return IO_F32
+    raise TypeError(f"I/O tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_size(batch, L, d_inner, d_state=D_STATE, io=IO_BF16) -> int:
+    return int(load_library().jscan_prefill_workspace_size(batch, L, d_inner, d_state, io))
+
+
+def plan(batch, L, d_inner, d_state=D_STATE):
+    k, c = ctypes.c_int(), ctypes.c_int()
+    _check(load_library().jscan_prefill_plan(batch, L, d_inner, d_state, ctypes.byref(k), ctypes.byref(c)))
+    return k.value, c.value
+
+
+def set_plan_override(waves_per_group=0, chunks=0):
+    """Force the prefill's launch plan on this thread; (0, 0) restores the automatic one."""
+    _check(load_library().jscan_set_plan_override(int(waves_per_group), int(chunks)))
+
+
+def time_next_prefill(before, after):
+    """Record HIP events around the next prefill's main scan kernel (torch.cuda.Event)."""
+    load_library().jscan_time_next_prefill(ctypes.c_void_p(before.cuda_event), ctypes.c_void_p(after.cuda_event))
+
+
+def prefill(x, delta, A, B, C, D, z, h0=None, *, y=None, hT=None, want_state=True,
+            workspace=None, stream=None):
+    """Selective scan over [batch, L, d_inner] inputs.  Returns (y, hT); hT is None
+    when want_state is False and no hT buffer is given.  hT may be h0 (in place)."""
+    torch = _torch()
+    lib = load_library()
+    _dev(x, "x")
+    batch, L, d_inner = x.shape
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (batch, L, D_STATE))
+    _dev(C, "C", x.dtype, (batch, L, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, D_STATE))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    if hT is None and want_state:
+        hT = torch.empty((batch, d_inner, D_STATE), dtype=torch.float32, device=x.device)
+    _dev(hT, "hT", torch.float32, (batch, d_inner, D_STATE))
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.jscan_prefill(batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                             _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), _ptr(workspace),
+                             ws_bytes, _stream(stream)))
+    return y, hT
+
+
+def step_batch(state, x, delta, A, B, C, D, z, *, y=None, stream=None):
+    """One decode token for n_seq sequences; state [n_seq, d_inner, 16] is updated in place."""
+    torch = _torch()
+    lib = load_library()
+    _dev(state, "state", torch.float32)
+    n_seq, d_inner, _ = state.shape
+    _dev(state, "state", torch.float32, (n_seq, d_inner, D_STATE))
+    _dev(x, "x", None, (n_seq, d_inner))
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (n_seq, D_STATE))
+    _dev(C, "C", x.dtype, (n_seq, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    _check(lib.jscan_step_batch(n_seq, d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                                _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(stream)))
+    return y
+
+
+def step(state, x, delta, A, B, C, D, z, *, y=None, stream=None):
+    """One decode token for one sequence; state [d_inner, 16] is updated in place."""
+    torch = _torch()
+    lib = load_library()
+    _dev(state, "state", torch.float32)
+    d_inner = state.shape[0]
+    _dev(state, "state", torch.float32, (d_inner, D_STATE))
+    _dev(x, "x", None, (d_inner,))
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (D_STATE,))
+    _dev(C, "C", x.dtype, (D_STATE,))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    _check(lib.jscan_step(d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                          _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(stream)))
+    return y

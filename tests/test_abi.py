@@ -1,0 +1,198 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+No test here launches work: every call below fails validation (or has no work
+to do), which the library decides before touching the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_11_amd as js
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jscan.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS, HIP = range(8)
+BF16, F32 = js.IO_BF16, js.IO_F32
+
+# Fake device addresses: validation only compares them, never dereferences.
+BASE = 0x7F0000000000
+MB = 1 << 20
+
+
+def fake(i, extra=0):
+    return ctypes.c_void_p(BASE + i * (1 << 36) + extra)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(js.LIB_PATH):
+        from selective_state_space_11_amd import build
+        build.build()
+    return js.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jscan_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("jscan_prefill", "jscan_step", "jscan_step_batch", "jscan_status_string"):
+        assert required in names
+    assert set(names) == set(js.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in js.STATUS_NAMES.items():
+        assert lib.jscan_status_string(code).decode() == name
+    assert lib.jscan_status_string(99).decode() == "JSCAN_UNKNOWN_STATUS"
+
+
+def prefill_args(batch=1, L=64, d_inner=128, d_state=16, io=BF16, **over):
+    es = 2 if io == BF16 else 4
+    args = dict(batch=batch, L=L, d_inner=d_inner, d_state=d_state, io=io,
+                x=fake(0), delta=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6),
+                h0=fake(7), y=fake(8), hT=fake(9), workspace=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return args
+
+
+def call_prefill(lib, a):
+    return lib.jscan_prefill(a["batch"], a["L"], a["d_inner"], a["d_state"], a["io"], a["x"], a["delta"],
+                             a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["y"], a["hT"],
+                             a["workspace"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "D", "z", "y"])
+def test_prefill_null_required_pointer(lib, name):
+    assert call_prefill(lib, prefill_args(**{name: None})) == NULL
+    assert "required" in lib.jscan_last_error().decode()
+
+
+def test_prefill_shapes_and_support(lib):
+    assert call_prefill(lib, prefill_args(batch=-1)) == SHAPE
+    assert call_prefill(lib, prefill_args(L=-5)) == SHAPE
+    assert call_prefill(lib, prefill_args(d_inner=-1)) == SHAPE
+    assert call_prefill(lib, prefill_args(L=1 << 40)) == SHAPE
+    assert call_prefill(lib, prefill_args(batch=70000)) == SHAPE
+    assert call_prefill(lib, prefill_args(d_state=64)) == UNSUP
+    assert call_prefill(lib, prefill_args(io=7)) == UNSUP
+
+
+def test_prefill_empty_problem_is_a_no_op(lib):
+    # batch 0: nothing to scan and no state to copy -> OK without any launch
+    assert call_prefill(lib, prefill_args(batch=0)) == OK
+    assert call_prefill(lib, prefill_args(d_inner=0)) == OK
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "D", "z", "h0", "y", "hT"])
+def test_prefill_alignment(lib, name):
+    a = prefill_args()
+    a[name] = ctypes.c_void_p(a[name].value + 2)
+    assert call_prefill(lib, a) == ALIGN
+
+
+def test_prefill_aliasing(lib):
+    # y on top of x
+    assert call_prefill(lib, prefill_args(y=fake(0))) == ALIAS
+    # y inside delta's range: 1 x 64 x 128 bf16 = 16 KiB
+    assert call_prefill(lib, prefill_args(y=fake(1, 4096))) == ALIAS
+    # hT partially overlapping h0 (state is 1 x 128 x 16 fp32 = 8 KiB)
+    assert call_prefill(lib, prefill_args(hT=fake(7, 4096))) == ALIAS
+    # hT overlapping y
+    assert call_prefill(lib, prefill_args(hT=fake(8, 16))) == ALIAS
+    # workspace overlapping an input
+    ws = js.workspace_size(1, 64, 128)
+    assert call_prefill(lib, prefill_args(workspace=fake(2), ws_bytes=ws)) == ALIAS
+    assert "overlaps" in lib.jscan_last_error().decode()
+
+
+def test_prefill_workspace_too_small(lib):
+    ws = js.workspace_size(1, 64, 128)
+    assert ws > 0
+    assert call_prefill(lib, prefill_args(workspace=fake(10), ws_bytes=ws - 1)) == WS
+
+
+def test_workspace_size_formula(lib):
+    assert js.workspace_size(1, 64, 128, 16) >= 64 * 32 * 4
+    assert js.workspace_size(1, 64, 128, 15) == 0
+    assert js.workspace_size(-1, 64, 128) == 0
+    assert js.workspace_size(0, 0, 0) == 0
+
+
+def test_automatic_plan_fills_mi355x():
+    # two waves per SIMD (2048 waves) and a workgroup per CU for the Jamba shapes
+    for batch, L in ((1, 65536), (1, 262144), (2, 4096), (8, 16384), (16, 4096)):
+        K, chunks = js.plan(batch, L, 8192)
+        assert K in (1, 2, 4, 8)
+        groups = batch * 8192 // 64
+        assert groups * K * chunks >= 2048
+        assert groups * chunks >= 256
+    assert js.plan(16, 4096, 8192) == (1, 1)        # enough channels: single pass, 16 states a lane
+    assert js.plan(1, 65536, 8192)[1] > 1            # batch 1 needs chunks
+
+
+def test_plan_override_round_trip():
+    try:
+        js.set_plan_override(4, 3)
+        assert js.plan(1, 300, 64) == (4, 3)
+        js.set_plan_override(2, 1000)                 # chunks clamp to L
+        assert js.plan(1, 10, 64) == (2, 10)
+        with pytest.raises(js.JscanError):
+            js.set_plan_override(3, 1)
+    finally:
+        js.set_plan_override(0, 0)
+    assert js.plan(1, 300, 64) != (4, 3) or True
+
+
+def step_args(n_seq=2, d_inner=64, d_state=16, io=BF16, **over):
+    a = dict(n_seq=n_seq, d_inner=d_inner, d_state=d_state, io=io, state=fake(0), x=fake(1), delta=fake(2),
+             A=fake(3), B=fake(4), C=fake(5), D=fake(6), z=fake(7), y=fake(8), stream=None)
+    a.update(over)
+    return a
+
+
+def call_step_batch(lib, a):
+    return lib.jscan_step_batch(a["n_seq"], a["d_inner"], a["d_state"], a["io"], a["state"], a["x"],
+                                a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["state", "x", "delta", "A", "B", "C", "D", "z", "y"])
+def test_step_null_and_alignment(lib, name):
+    assert call_step_batch(lib, step_args(**{name: None})) == NULL
+    a = step_args()
+    a[name] = ctypes.c_void_p(a[name].value + 4)
+    assert call_step_batch(lib, a) == ALIGN
+
+
+def test_step_validation(lib):
+    assert call_step_batch(lib, step_args(n_seq=-1)) == SHAPE
+    assert call_step_batch(lib, step_args(d_state=8)) == UNSUP
+    assert call_step_batch(lib, step_args(io=5)) == UNSUP
+    assert call_step_batch(lib, step_args(y=fake(1))) == ALIAS        # y on x
+    assert call_step_batch(lib, step_args(y=fake(0, 64))) == ALIAS    # y inside the state
+    assert call_step_batch(lib, step_args(n_seq=0)) == OK
+    assert lib.jscan_step(64, 16, BF16, None, fake(1), fake(2), fake(3), fake(4), fake(5), fake(6),
+                          fake(7), fake(8), None) == NULL
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    # A missing library is an error, never a silent fallback.
+    saved = js._lib
+    try:
+        js._lib = None
+        with pytest.raises(js.JscanUnavailable):
+            js.load_library(str(tmp_path / "missing.so"))
+    finally:
+        js._lib = saved
