@@ -145,7 +145,12 @@ def set_plan_override(waves_per_group=0, chunks=0):
 
 
 def time_next_prefill(before, after):
-    """Record HIP events around the next prefill's main scan kernel (torch.cuda.Event)."""
+    """Record HIP events around the next prefill's main scan kernel (torch.cuda.Event
+    created with enable_timing=True).  torch creates the underlying hipEvent_t
+    lazily, at its first record(); record each once so the handle exists."""
+    for ev in (before, after):
+        if not ev.cuda_event:
+            ev.record()
     load_library().jscan_time_next_prefill(ctypes.c_void_p(before.cuda_event), ctypes.c_void_p(after.cuda_event))
 
 

@@ -14,9 +14,9 @@
 //   (K = 1, 2, 4 or 8); wave g owns states [g*16/K, (g+1)*16/K).  The state
 //   stays in VGPRs for the whole call.  Because a wave owns the same state
 //   indices for all its lanes, the shared per-token rows B_t and C_t are
-//   wave-uniform: they are read with scalar loads into SGPRs and fed to the
-//   VALU as scalar operands, with no LDS traffic and no VGPRs.  For that the
-//   rows are first widened to fp32 into the workspace by a small kernel.
+//   wave-uniform: they are read with scalar loads into SGPRs (bf16 pairs stay
+//   packed and are widened by a scalar shift or mask) and fed to the VALU as
+//   scalar operands, with no LDS traffic and no VGPRs.
 // * With K > 1 the partial outputs sum_n C*h of the K waves are added through
 //   LDS once per block of tokens, and each wave finishes (D skip, SiLU gate,
 //   rounding, store) a 1/K share of the tokens.
@@ -40,7 +40,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
+#include <type_traits>
 
 #include "jscan.h"
 
@@ -50,7 +52,6 @@ constexpr int NSTATE = 16;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kTok = 8;         // tokens per software-pipelined block
 constexpr int kCUs = 256;       // MI355X compute units
-constexpr int kWaveTarget = 2 * 4 * kCUs;   // two waves per SIMD
 constexpr int64_t kMinChunk = 64;           // shortest chunk worth a carry
 
 // ---------------------------------------------------------------- I/O types
@@ -67,18 +68,6 @@ __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_ex
 // denominator is +inf and the result is -0, as in the definition.
 __device__ __forceinline__ float silu(float zv) {
   return zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
-}
-
-// ------------------------------------------------------- B/C row widening
-// bc[r][0..15] = B[r][0..15], bc[r][16..31] = C[r][0..15], fp32.
-template <class T>
-__global__ __launch_bounds__(256) void k_widen_bc(const T* __restrict__ B, const T* __restrict__ C,
-                                                  float* __restrict__ bc, int64_t rows) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * 32) return;
-  const int64_t r = i >> 5;
-  const int k = (int)(i & 31);
-  bc[i] = k < NSTATE ? widen(B[r * NSTATE + k]) : widen(C[r * NSTATE + (k - NSTATE)]);
 }
 
 // ------------------------------------------------- chunk-local end states
@@ -106,22 +95,86 @@ __device__ __forceinline__ void copy_row(float (&dst)[S], const float (&src)[S])
   for (int s = 0; s < S; ++s) dst[s] = src[s];
 }
 
-// One lane per channel, all 16 states.  For chunk c (every chunk but the
-// last) of sequence b: S[b][c][d][n] = state after the chunk when it starts
-// from zero, dsum[b][c][d] = sum of delta over the chunk (accumulated in fp64).
+// S consecutive values of a B or C row, read with scalar loads from a
+// wave-uniform address and kept in SGPRs in the I/O format.  bf16 pairs stay
+// packed (S/2 dwords) and are widened when used (a scalar shift or mask).
+template <class T, int S> struct Row;
+template <int S> struct Row<uint16_t, S> {
+  static_assert(S % 2 == 0, "bf16 rows are read in pairs");
+  uint32_t w[S / 2];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ p) {
+    if constexpr (S % 8 == 0) {
+#pragma unroll
+      for (int q = 0; q < S / 8; ++q) {
+        const uint4 v = reinterpret_cast<const uint4*>(p)[q];
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < S / 2; ++q) w[q] = reinterpret_cast<const uint32_t*>(p)[q];
+    }
+  }
+  __device__ __forceinline__ float operator[](int s) const {
+    return (s & 1) ? __uint_as_float(w[s >> 1] & 0xffff0000u) : __uint_as_float(w[s >> 1] << 16);
+  }
+};
+template <int S> struct Row<float, S> {
+  float w[S];
+  __device__ __forceinline__ void load(const float* __restrict__ p) { load_row(w, p); }
+  __device__ __forceinline__ float operator[](int s) const { return w[s]; }
+};
+
+// Addressing: a wave covers 64 consecutive channels [gbase, gbase + 64).  Row
+// pointers (token t, channel gbase) are wave-uniform and live in SGPRs; a lane
+// adds its own 32-bit offset `lo`.  Lanes past d_inner are clamped onto
+// channel d_inner - 1 (they read valid memory and their results are dropped or
+// duplicate that channel's).
+
+// Streaming loads and stores are buffer instructions: a wave-uniform resource
+// (SGPRs, based at the first row of the current token block), the lane's
+// constant byte offset (VGPR) and the token's row offset (SGPR), so they cost
+// no VALU address arithmetic.  A resource with num_records = 0 makes every
+// load return 0 (out-of-range rule); it stands in for padding tokens' delta.
+constexpr int kBufDword3 = 0x00020000;      // gfx9 raw buffer: 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int records = -1) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, records, kBufDword3);
+}
+__device__ __forceinline__ void buf_load(uint16_t& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  v = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_load(float& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t to_io(float v, uint16_t) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ float to_io(float v, float) { return v; }
+
+// One lane per channel, all 16 states.  Segment s (of the tokens before the
+// last rescan chunk; every segment has seg_len tokens, a multiple of kTok) of
+// sequence b: S[b][s][d][n] = state after the segment when it starts from
+// zero, dsum[b][s][d] = sum of delta over the segment (accumulated in fp64).
 template <class T>
 __global__ __launch_bounds__(256) void k_chunk_state(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const float* __restrict__ bc, float* __restrict__ S, float* __restrict__ dsum,
-    int64_t L, int64_t d_inner, int64_t chunk_len, int n_chunks) {
-  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int c = blockIdx.y;
+    const T* __restrict__ Bm, float* __restrict__ S, float* __restrict__ dsum,
+    int64_t L, int64_t d_inner, int64_t seg_len, int n_segs) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t gbase = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (gbase >= d_inner) return;                       // whole wave past the end
+  const int seg = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const bool valid = d < d_inner;
-  const int64_t dc = valid ? d : d_inner - 1;
+  const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
+  const int64_t d = gbase + lo;
 
   float a2[NSTATE], h[NSTATE];
-  const float4* Ap = reinterpret_cast<const float4*>(A + dc * NSTATE);
+  const float4* Ap = reinterpret_cast<const float4*>(A + d * NSTATE);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float4 v = Ap[q];
@@ -132,52 +185,49 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   for (int n = 0; n < NSTATE; ++n) h[n] = 0.0f;
   double dacc = 0.0;
 
-  const int64_t t0 = (int64_t)c * chunk_len;
-  const int nt = (int)std::min<int64_t>(chunk_len, L - t0);   // >= 1 for every chunk
-  const T* xp = x + (b * L + t0) * d_inner + dc;
-  const T* dp = delta + (b * L + t0) * d_inner + dc;
-  const float* bcrow = bc + (b * L + t0) * 32;
+  const int64_t t0 = (int64_t)seg * seg_len;
+  const int nt = (int)seg_len;
+  const T* xrow = x + (b * L + t0) * d_inner + gbase;
+  const T* drow = delta + (b * L + t0) * d_inner + gbase;
+  const T* brow = Bm + (b * L + t0) * NSTATE;
+  const uint32_t lb = (uint32_t)lo * sizeof(T);      // lane byte offset within a row
+  const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
 
-  auto token = [&](float dt, float xv, const float (&Bv)[NSTATE]) {
-    const float dx = dt * xv;
-    dacc += (double)dt;
+  // Loads of token block bb (always kTok whole tokens: segments are multiples).
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok]) {
+    const int64_t o = (int64_t)bb * d_inner;
+    const auto rd = rsrc(drow + o), rx = rsrc(xrow + o);
 #pragma unroll
-    for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bv[n]);
+    for (int j = 0; j < kTok; ++j) { buf_load(dd[j], rd, lb, j * rowb); buf_load(xx[j], rx, lb, j * rowb); }
   };
-
-  T dr[kTok], xr[kTok];
-#pragma unroll
-  for (int j = 0; j < kTok; ++j) {
-    const int64_t o = (int64_t)std::min(j, nt - 1) * d_inner;
-    dr[j] = dp[o]; xr[j] = xp[o];
-  }
-  float Bc[NSTATE], Bn[NSTATE];
-  load_row(Bc, bcrow);
-  __builtin_amdgcn_s_waitcnt(0);
-  int base = 0;
-  for (; base + kTok <= nt; base += kTok) {
-    T dn[kTok], xn[kTok];
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {   // next block, clamped inside the chunk
-      const int64_t o = (int64_t)std::min(base + kTok + j, nt - 1) * d_inner;
-      dn[j] = dp[o]; xn[j] = xp[o];
-    }
+  Row<T, NSTATE> Bc, Bn;
+  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok]) {
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-      load_row(Bn, bcrow + (int64_t)std::min(base + j + 1, nt - 1) * 32);
-      token(widen(dr[j]), widen(xr[j]), Bc);
-      copy_row(Bc, Bn);
-    }
+      Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
+      const float dt = widen(dd[j]);
+      const float dx = dt * widen(xx[j]);
+      dacc += (double)dt;
 #pragma unroll
-    for (int j = 0; j < kTok; ++j) { dr[j] = dn[j]; xr[j] = xn[j]; }
+      for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
+      Bc = Bn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Two register sets in turn: block i+1 is in flight while block i computes.
+  T dA[kTok], xA[kTok], dB[kTok], xB[kTok];
+  load_block(0, dA, xA);
+  Bc.load(brow);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int base = 0; base < nt; base += 2 * kTok) {
+    load_block(std::min(base + kTok, nt - kTok), dB, xB);
+    do_block(base, dA, xA);
+    if (base + kTok >= nt) break;
+    load_block(std::min(base + 2 * kTok, nt - kTok), dA, xA);
+    do_block(base + kTok, dB, xB);
   }
-  for (; base < nt; ++base) {          // fewer than kTok tokens left
-    const int64_t o = (int64_t)base * d_inner;
-    load_row(Bc, bcrow + (int64_t)base * 32);
-    token(widen(dp[o]), widen(xp[o]), Bc);
-  }
-  if (valid) {
-    const int64_t slot = b * (n_chunks - 1) + c;
+  if (lo == lane) {
+    const int64_t slot = b * n_segs + seg;
     float4* Sp = reinterpret_cast<float4*>(S + (slot * d_inner + d) * NSTATE);
 #pragma unroll
     for (int q = 0; q < 4; ++q) Sp[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
@@ -186,31 +236,48 @@ __global__ __launch_bounds__(256) void k_chunk_state(
 }
 
 // ------------------------------------------------------------ carry combine
-// One lane per (b, d, n).  Folds the chunks' (P_c, S_c) pairs in sequence
-// order, h <- P_c * h + S_c with P_c = exp2(A' * dsum_c), seeded with h0,
-// and records the state each chunk starts from.
+// One lane per (b, d, n).  Folds the segments' (P, S) pairs in sequence order,
+// h <- P * h + S with P = exp2(A' * dsum), seeded with h0, and records the
+// state each rescan chunk starts from (every seg_per_chunk segments).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, const float* __restrict__ S,
                                                  const float* __restrict__ dsum, const float* __restrict__ h0,
-                                                 float* __restrict__ hstart, int64_t d_inner, int n_chunks) {
+                                                 float* __restrict__ hstart, int64_t d_inner, int n_chunks,
+                                                 int seg_per_chunk) {
+  constexpr int G = 8;                 // segments whose loads are in flight together
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t b = blockIdx.y;
   const int64_t per_seq = d_inner * NSTATE;
   if (i >= per_seq) return;
   const int64_t d = i >> 4;
+  const int n_segs = (n_chunks - 1) * seg_per_chunk;
   const float a2 = A[i] * kLog2e;
+  const float* Sp = S + (b * n_segs) * per_seq + i;
+  const float* Dp = dsum + (b * n_segs) * d_inner + d;
+  float* Hp = hstart + (b * n_chunks) * per_seq + i;
   float h = h0 ? h0[b * per_seq + i] : 0.0f;
-  for (int c = 0; c < n_chunks; ++c) {
-    hstart[(b * n_chunks + c) * per_seq + i] = h;
-    if (c + 1 < n_chunks) {
-      const int64_t slot = b * (n_chunks - 1) + c;
-      h = fmaf(fast_exp2(a2 * dsum[slot * d_inner + d]), h, S[slot * per_seq + i]);
+  Hp[0] = h;
+  for (int s0 = 0; s0 < n_segs; s0 += G) {
+    float sv[G], dv[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int sg = std::min(s0 + k, n_segs - 1);
+      sv[k] = Sp[(int64_t)sg * per_seq];
+      dv[k] = Dp[(int64_t)sg * d_inner];
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int sg = s0 + k;
+      if (sg < n_segs) {
+        h = fmaf(fast_exp2(a2 * dv[k]), h, sv[k]);
+        if ((sg + 1) % seg_per_chunk == 0) Hp[(int64_t)((sg + 1) / seg_per_chunk) * per_seq] = h;
+      }
     }
   }
 }
 
 // ----------------------------------------------------------------- main scan
 struct ScanArgs {
-  const void* x; const void* delta; const float* A; const float* bc; const float* D;
+  const void* x; const void* delta; const float* A; const void* B; const void* C; const float* D;
   const void* z; const float* hinit;   // h0 (single chunk) or hstart (chunked), may be null
   void* y; float* hT;
   int64_t L, d_inner, chunk_len;
@@ -220,141 +287,145 @@ struct ScanArgs {
 // Grid: (ceil(d_inner / 64), chunks, batch); block: K waves.  Wave g of a
 // block owns states [g*16/K, (g+1)*16/K) of the block's 64 channels for the
 // block's chunk of tokens.
+//
+// Tokens go in blocks of kTok, the next block's loads issued before the
+// current block is computed.  A chunk's last block may be partial: its
+// missing tokens are loaded clamped onto the last token with delta = 0, so
+// they leave the state bit-for-bit unchanged (exp2(0) = 1, input term
+// 0 * x * B = 0 for finite x and B) and their output equals the last token's,
+// which they store again to the same address.  Every block therefore runs the
+// same branch-free code.
 template <class T, int K>
 __global__ __launch_bounds__(64 * K) void k_scan(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const float* __restrict__ bc, const float* __restrict__ Dw, const T* __restrict__ z,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dw, const T* __restrict__ z,
     const float* __restrict__ hinit, T* __restrict__ y, float* __restrict__ hT,
     int64_t L, int64_t d_inner, int64_t chunk_len, int n_chunks) {
   constexpr int S = NSTATE / K;
+  constexpr int F = kTok / K;          // tokens of a block finished by each wave
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t d = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t gbase = (int64_t)blockIdx.x * 64;
   const int c = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const bool valid = d < d_inner;
-  const int64_t dc = valid ? d : d_inner - 1;
+  const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
+  const int64_t d = gbase + lo;
   const int n0 = g * S;
 
   float a2[S], h[S];
 #pragma unroll
-  for (int s = 0; s < S; ++s) a2[s] = A[dc * NSTATE + n0 + s] * kLog2e;
+  for (int s = 0; s < S; ++s) a2[s] = A[d * NSTATE + n0 + s] * kLog2e;
   const float* hi = nullptr;
-  if (n_chunks > 1) hi = hinit + ((b * n_chunks + c) * d_inner + dc) * NSTATE + n0;
-  else if (hinit) hi = hinit + (b * d_inner + dc) * NSTATE + n0;
+  if (n_chunks > 1) hi = hinit + ((b * n_chunks + c) * d_inner + d) * NSTATE + n0;
+  else if (hinit) hi = hinit + (b * d_inner + d) * NSTATE + n0;
 #pragma unroll
   for (int s = 0; s < S; ++s) h[s] = hi ? hi[s] : 0.0f;
-  const float Dd = Dw[dc];
+  const float Dd = Dw[d];
 
   const int64_t t0 = (int64_t)c * chunk_len;
   const int nt = (int)std::min<int64_t>(chunk_len, L - t0);   // >= 1 for every chunk
-  const int64_t off0 = (b * L + t0) * d_inner + dc;
-  const T* xp = x + off0;
-  const T* dp = delta + off0;
-  const T* zp = z + off0;
-  T* yp = y + off0;
-  const float* bcrow = bc + (b * L + t0) * 32;
+  const int64_t row0 = (b * L + t0) * d_inner + gbase;
+  const T* xrow = x + row0;
+  const T* drow = delta + row0;
+  const T* zrow = z + row0;
+  T* yrow = y + row0;
+  const T* brow = Bm + (b * L + t0) * NSTATE + n0;
+  const T* crow = Cm + (b * L + t0) * NSTATE + n0;
 
-  __shared__ float red[K > 1 ? K : 1][kTok][64];
+  __shared__ float red[K > 1 ? 2 : 1][K > 1 ? K : 1][kTok][64];
 
-  // State update for one token; returns this wave's share of sum_n C*h.
-  auto token = [&](float dt, float xv, const float (&Bv)[S], const float (&Cv)[S]) {
-    const float dx = dt * xv;
-    float acc = 0.0f;
+  const uint32_t lb = (uint32_t)lo * sizeof(T);      // lane byte offset within a row
+  const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
+
+  // Loads of token block bb.  Rows past the chunk's end are clamped onto its
+  // last token, and their delta is read through an empty resource (0).
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&xff)[F], T (&zff)[F]) {
+    const int64_t o = (int64_t)bb * d_inner;
+    const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), r0 = rsrc(drow, 0);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bv[s]);
-      acc = fmaf(Cv[s], h[s], acc);
+    for (int j = 0; j < kTok; ++j) {
+      const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
+      buf_load(dd[j], bb + j < nt ? rd : r0, lb, so);
+      buf_load(xx[j], rx, lb, so);
+      if constexpr (K == 1) buf_load(zz[j], rz, lb, so);
     }
-    return acc;
-  };
-  // Lanes past d_inner run on the clamped channel d_inner - 1 with exactly the
-  // same inputs and arithmetic as that channel's own lane, so their store
-  // writes the identical value to the identical address; storing
-  // unconditionally keeps the token loop free of branches.
-  auto finish = [&](int64_t o, float acc, float xv, float zv) {
-    store_io(yp + o, fmaf(Dd, xv, acc) * silu(zv));
-  };
-  // K > 1: add the K partial sums of tokens [base, base+count) through LDS;
-  // wave g finishes the tokens j with j % K == g.
-  auto reduce_block = [&](int base, const float (&part)[kTok], int count) {
+    if constexpr (K > 1) {
 #pragma unroll
-    for (int j = 0; j < kTok; ++j) red[g][j][lane] = part[j];
-    __syncthreads();
+      for (int i = 0; i < F; ++i) {
+        const uint32_t so = (uint32_t)(std::min(bb + i * K + g, nt - 1) - bb) * rowb;
+        buf_load(xff[i], rx, lb, so); buf_load(zff[i], rz, lb, so);
+      }
+    }
+  };
+
+  // B of the next token is prefetched a token ahead; C is needed only after
+  // the token's state updates, so it is loaded at the token's start.
+  Row<T, S> Bc, Bn, Cv;
+  int buf = 0;
+  // y of token bb + j (padding tokens map onto the last token's address and
+  // store the identical value again).
+  auto finish = [&](__amdgpu_buffer_rsrc_t ry, int bb, int j, float acc, float xv, float zv) {
+    const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
+    buf_store(to_io(fmaf(Dd, xv, acc) * silu(zv), T()), ry, lb, so);
+  };
+  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
+                      const T (&xff)[F], const T (&zff)[F]) {
+    const auto ry = rsrc(yrow + (int64_t)bb * d_inner);
+    float part[kTok];
 #pragma unroll
-    for (int i = 0; i < kTok / K; ++i) {
-      const int j = i * K + g;
-      if (j < count) {
+    for (int j = 0; j < kTok; ++j) {
+      Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
+      Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
+      const float dt = widen(dd[j]);
+      const float xv = widen(xx[j]);
+      const float dx = dt * xv;
+#pragma unroll
+      for (int s = 0; s < S; ++s) h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bc[s]);
+      float acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) acc = fmaf(Cv[s], h[s], acc);
+      if constexpr (K == 1) finish(ry, bb, j, acc, xv, widen(zz[j]));
+      else part[j] = acc;
+      Bc = Bn;
+      // Keep each token's scalar B/C loads in its own token: hoisting them
+      // across tokens would hold several rows in SGPRs at once and spill.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (K > 1) {
+      // Partial sums through LDS, double-buffered so one barrier per block
+      // suffices: a wave overwrites buffer p only after the barrier of the
+      // following block, which every wave reaches after its reads of p.
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) red[buf][g][j][lane] = part[j];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
         float acc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < K; ++w) acc += red[w][j][lane];
-        const int64_t o = (int64_t)(base + j) * d_inner;
-        finish(o, acc, widen(xp[o]), widen(zp[o]));
+        for (int w = 0; w < K; ++w) acc += red[buf][w][i * K + g][lane];
+        finish(ry, bb, i * K + g, acc, widen(xff[i]), widen(zff[i]));
       }
+      buf ^= 1;
     }
-    __syncthreads();
   };
 
-  T dr[kTok], xr[kTok], zr[kTok];
-#pragma unroll
-  for (int j = 0; j < kTok; ++j) {
-    const int64_t o = (int64_t)std::min(j, nt - 1) * d_inner;
-    dr[j] = dp[o]; xr[j] = xp[o];
-    if constexpr (K == 1) zr[j] = zp[o];
-  }
-  float Bc[S], Cc[S], Bn[S], Cn[S];
-  load_row(Bc, bcrow + n0);
-  load_row(Cc, bcrow + NSTATE + n0);
+  // Two register sets in turn: block i+1 is in flight while block i computes.
+  T dA[kTok], xA[kTok], zA[kTok], fxA[F], fzA[F];
+  T dB[kTok], xB[kTok], zB[kTok], fxB[F], fzB[F];
+  load_block(0, dA, xA, zA, fxA, fzA);
+  Bc.load(brow);
   __builtin_amdgcn_s_waitcnt(0);
-
-  int base = 0;
-  for (; base + kTok <= nt; base += kTok) {
-    T dn[kTok], xn[kTok], zn[kTok];
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {   // next block, clamped inside the chunk
-      const int64_t o = (int64_t)std::min(base + kTok + j, nt - 1) * d_inner;
-      dn[j] = dp[o]; xn[j] = xp[o];
-      if constexpr (K == 1) zn[j] = zp[o];
-    }
-    float part[kTok];
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-      const float* nrow = bcrow + (int64_t)std::min(base + j + 1, nt - 1) * 32;
-      load_row(Bn, nrow + n0);
-      load_row(Cn, nrow + NSTATE + n0);
-      const float xv = widen(xr[j]);
-      const float acc = token(widen(dr[j]), xv, Bc, Cc);
-      if constexpr (K == 1) finish((int64_t)(base + j) * d_inner, acc, xv, widen(zr[j]));
-      else part[j] = acc;
-      copy_row(Bc, Bn);
-      copy_row(Cc, Cn);
-    }
-    if constexpr (K > 1) reduce_block(base, part, kTok);
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-      dr[j] = dn[j]; xr[j] = xn[j];
-      if constexpr (K == 1) zr[j] = zn[j];
-    }
+  // Prefetches past the chunk's end are clamped to its last block (valid rows,
+  // values unused), so every row offset below stays non-negative.
+  const int last = (nt - 1) / kTok * kTok;
+  for (int base = 0; base < nt; base += 2 * kTok) {
+    load_block(std::min(base + kTok, last), dB, xB, zB, fxB, fzB);
+    do_block(base, dA, xA, zA, fxA, fzA);
+    if (base + kTok >= nt) break;
+    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, fxA, fzA);
+    do_block(base + kTok, dB, xB, zB, fxB, fzB);
   }
-  if (base < nt) {                     // fewer than kTok tokens left
-    float part[kTok];
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-      part[j] = 0.0f;
-      if (base + j < nt) {
-        const int64_t o = (int64_t)(base + j) * d_inner;
-        const float* row = bcrow + (int64_t)(base + j) * 32;
-        load_row(Bc, row + n0);
-        load_row(Cc, row + NSTATE + n0);
-        const float xv = widen(xp[o]);
-        const float acc = token(widen(dp[o]), xv, Bc, Cc);
-        if constexpr (K == 1) finish(o, acc, xv, widen(zp[o]));
-        else part[j] = acc;
-      }
-    }
-    if constexpr (K > 1) reduce_block(base, part, nt - base);
-  }
-  if (hT && c == n_chunks - 1 && valid) {
+  if (hT && c == n_chunks - 1 && lo == lane) {
     float* ho = hT + (b * d_inner + d) * NSTATE + n0;
 #pragma unroll
     for (int s = 0; s < S; ++s) ho[s] = h[s];
@@ -445,66 +516,90 @@ bool overlap(const Range& a, const Range& b) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-struct Plan { int K; int chunks; int64_t chunk_len; };
+// Launch plan.  The main scan runs `chunks` chunks of chunk_len tokens per
+// sequence with K waves per 64 channels.  When chunks > 1, the tokens before
+// the last chunk are cut into segments of seg_len tokens (seg_per_chunk per
+// chunk) for the chunk-local pass, so that pass fills the GPU on its own.
+struct Plan {
+  int K;
+  int chunks;
+  int64_t chunk_len;
+  int seg_per_chunk;
+  int64_t seg_len;
+  int64_t segments() const { return chunks > 1 ? (int64_t)(chunks - 1) * seg_per_chunk : 0; }
+};
 
-// Pick the state split K and the chunk count for these sizes.  The model
-// counts VALU issue slots per channel-token: the rescan costs about 145 + 4K
-// (16 x (mul, exp at quarter rate, mul, fma, fma) plus the epilogue and the
-// K-fold replication of the per-token loads), the chunk-local pass about 115
-// on the (C-1)/C of the tokens that need a carry.  Candidates must give at
-// least two waves per SIMD and one workgroup per CU where the sizes allow.
-Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner) {
-  if (t_force_K > 0 && t_force_chunks > 0) {
-    const int64_t C = std::max<int64_t>(1, std::min<int64_t>(t_force_chunks, L));
-    const int64_t len = L > 0 ? (L + C - 1) / C : 1;
-    return Plan{t_force_K, L > 0 ? (int)((L + len - 1) / len) : 1, len};
-  }
-  if (L <= 0) return Plan{1, 1, 1};
+// Relative throughput of the scan loops with `waves` waves launched on the
+// 1024 SIMDs, measured on MI355X with the one-wave-per-64-channels kernels
+// (main scan at batch 1 and batch 8, d_inner 8192): one wave per SIMD issues
+// at most every other cycle, a few more hide the load and exp latencies, and
+// many more even out the tail across CUs.
+double wave_efficiency(double waves) {
+  static const double lw[] = {10, 11, 12, 13, 14, 15};
+  static const double ef[] = {0.37, 0.53, 0.68, 0.91, 0.96, 1.0};
+  const double l = std::log2(std::max(1.0, waves));
+  if (l <= lw[0]) return ef[0] * waves / 1024.0;
+  for (int i = 1; i < 6; ++i)
+    if (l <= lw[i]) return ef[i - 1] + (ef[i] - ef[i - 1]) * (l - lw[i - 1]);
+  return 1.0;
+}
+
+Plan make_plan(int64_t batch, int64_t L, int64_t d_inner, int K, int64_t C_target) {
+  Plan p{K, 1, std::max<int64_t>(L, 1), 1, std::max<int64_t>(L, 1)};
+  if (L <= 0 || C_target <= 1) return p;
   const int64_t groups = batch * ((d_inner + 63) / 64);
-  Plan best{1, 1, L};
+  // segments per chunk: enough chunk-local waves for 32 per SIMD, >= 64 tokens each
+  const int64_t want = (32 * 4 * kCUs + groups * (C_target - 1) - 1) / (groups * (C_target - 1));
+  int64_t F = std::max<int64_t>(1, std::min<int64_t>(want, (L / C_target) / kMinChunk));
+  int64_t seg = (L + C_target * F - 1) / (C_target * F);
+  seg = (seg + kTok - 1) / kTok * kTok;                    // whole token blocks
+  int64_t chunk_len = seg * F;
+  int64_t C = (L + chunk_len - 1) / chunk_len;
+  if (C <= 1) return p;
+  while ((C - 1) * F > 65535) { F = (F + 1) / 2; seg *= 2; chunk_len = seg * F; C = (L + chunk_len - 1) / chunk_len; }
+  if (C <= 1) return p;
+  return Plan{K, (int)C, chunk_len, (int)F, seg};
+}
+
+// Pick the plan.  Estimated time per channel-token: the rescan's VALU issue
+// slots (about 150: 16 x (mul, exp at quarter rate, mul, fma, fma) plus the
+// epilogue) over the efficiency its wave count reaches, plus the chunk-local
+// pass (about 115 slots) on the (C-1)/C of the tokens that need a carry, over
+// its own efficiency.  Measured on MI355X, splitting a channel's states over
+// K > 1 waves never beat one wave per 64 channels with more chunks (the
+// per-token work the K waves repeat and their barriers cost more than the
+// extra chunk-local work), so the automatic plan keeps K = 1.
+Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner) {
+  if (t_force_K > 0 && t_force_chunks > 0)
+    return make_plan(batch, L, d_inner, t_force_K, std::min<int64_t>(t_force_chunks, std::max<int64_t>(L, 1)));
+  if (L <= 0) return make_plan(batch, L, d_inner, 1, 1);
+  const int64_t groups = batch * ((d_inner + 63) / 64);
+  Plan best = make_plan(batch, L, d_inner, 1, 1);
   double best_cost = 1e300;
-  bool best_fills = false;
-  const int64_t max_chunks = std::max<int64_t>(1, L / kMinChunk);
-  for (int K : {1, 2, 4, 8}) {
-    for (int64_t C = 1; C <= 4096; C *= 2) {
-      if (C > max_chunks && C > 1) break;
-      const int64_t waves = groups * K * C;
-      const int64_t wgs = groups * C;
-      const bool fills = waves >= kWaveTarget && wgs >= kCUs;
-      const double cost = (145.0 + 4.0 * K) + 115.0 * (double)(C - 1) / (double)C;
-      // Prefer plans that fill the chip; among those the cheapest; if none
-      // fills it, the one with the most waves (then the cheapest).
-      bool better;
-      if (fills != best_fills) better = fills;
-      else if (fills) better = cost < best_cost;
-      else {
-        const int64_t bw = groups * best.K * best.chunks;
-        better = waves > bw || (waves == bw && cost < best_cost);
-      }
-      if (better) {
-        const int64_t len = (L + C - 1) / C;
-        best = Plan{K, (int)((L + len - 1) / len), len};
-        best_cost = cost;
-        best_fills = fills;
-      }
-    }
+  for (int64_t C = 1; C <= 4096; C *= 2) {
+    if (C > 1 && L / C < kMinChunk) break;
+    const Plan p = make_plan(batch, L, d_inner, 1, C);
+    double cost = 150.0 / wave_efficiency((double)groups * p.chunks);
+    if (p.chunks > 1)
+      cost += 115.0 * (double)(p.chunks - 1) / p.chunks / wave_efficiency((double)groups * p.segments());
+    if (cost < best_cost * 0.999) { best = p; best_cost = cost; }
   }
   return best;
 }
 
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-struct WsLayout { size_t bc, S, dsum, hstart, total; };
+struct WsLayout { size_t S, dsum, hstart, total; };
 
 WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   WsLayout w{};
-  w.bc = round_up((size_t)batch * (size_t)L * 32 * sizeof(float));
   if (p.chunks > 1) {
-    w.S = round_up((size_t)batch * (size_t)(p.chunks - 1) * (size_t)d_inner * NSTATE * sizeof(float));
-    w.dsum = round_up((size_t)batch * (size_t)(p.chunks - 1) * (size_t)d_inner * sizeof(float));
+    const size_t segs = (size_t)p.segments();
+    w.S = round_up((size_t)batch * segs * (size_t)d_inner * NSTATE * sizeof(float));
+    w.dsum = round_up((size_t)batch * segs * (size_t)d_inner * sizeof(float));
     w.hstart = round_up((size_t)batch * (size_t)p.chunks * (size_t)d_inner * NSTATE * sizeof(float));
   }
-  w.total = w.bc + w.S + w.dsum + w.hstart;
+  w.total = w.S + w.dsum + w.hstart;
   return w;
 }
 
@@ -521,7 +616,8 @@ template <class T, int K>
 hipError_t launch_scan(const ScanArgs& a, int64_t batch, hipStream_t st) {
   dim3 grid((unsigned)((a.d_inner + 63) / 64), (unsigned)a.n_chunks, (unsigned)batch);
   hipLaunchKernelGGL((k_scan<T, K>), grid, dim3(64 * K), 0, st, static_cast<const T*>(a.x),
-                     static_cast<const T*>(a.delta), a.A, a.bc, a.D, static_cast<const T*>(a.z), a.hinit,
+                     static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
+                     a.D, static_cast<const T*>(a.z), a.hinit,
                      static_cast<T*>(a.y), a.hT, a.L, a.d_inner, a.chunk_len, a.n_chunks);
   return hipGetLastError();
 }
@@ -542,27 +638,24 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
                          const float* h0, void* y, float* hT, char* ws, const Plan& p,
                          hipStream_t st) {
   const WsLayout w = ws_layout(batch, L, d_inner, p);
-  float* bc = reinterpret_cast<float*>(ws);
-  float* S = reinterpret_cast<float*>(ws + w.bc);
-  float* dsum = reinterpret_cast<float*>(ws + w.bc + w.S);
-  float* hstart = reinterpret_cast<float*>(ws + w.bc + w.S + w.dsum);
+  float* S = reinterpret_cast<float*>(ws);
+  float* dsum = reinterpret_cast<float*>(ws + w.S);
+  float* hstart = reinterpret_cast<float*>(ws + w.S + w.dsum);
   hipError_t e;
 
-  const int64_t rows = batch * L;
-  hipLaunchKernelGGL((k_widen_bc<T>), dim3((unsigned)((rows * 32 + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const T*>(B), static_cast<const T*>(C), bc, rows);
-  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "widen B/C launch");
-
   if (p.chunks > 1) {
-    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)(p.chunks - 1), (unsigned)batch);
+    const int segs = (int)p.segments();
+    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)segs, (unsigned)batch);
     hipLaunchKernelGGL((k_chunk_state<T>), g1, dim3(256), 0, st, static_cast<const T*>(x),
-                       static_cast<const T*>(delta), A, bc, S, dsum, L, d_inner, p.chunk_len, p.chunks);
+                       static_cast<const T*>(delta), A, static_cast<const T*>(B), S, dsum, L, d_inner, p.seg_len,
+                       segs);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
     dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
-    hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks);
+    hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks,
+                       p.seg_per_chunk);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
   }
-  ScanArgs a{x, delta, A, bc, D, z, p.chunks > 1 ? hstart : h0, y, hT, L, d_inner, p.chunk_len, p.chunks};
+  ScanArgs a{x, delta, A, B, C, D, z, p.chunks > 1 ? hstart : h0, y, hT, L, d_inner, p.chunk_len, p.chunks};
   hipEvent_t eb = t_ev_before, ea = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
   if (eb && ea && (e = hipEventRecord(eb, st)) != hipSuccess) return hip_fail(e, "event record");
@@ -706,7 +799,7 @@ jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
   }
   char* ws = static_cast<char*>(workspace);
   bool owned = false;
-  if (!ws) {
+  if (!ws && need > 0) {
     if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess)
       return hip_fail(e, "hipMallocAsync(workspace)");
     owned = true;
