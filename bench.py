@@ -68,6 +68,73 @@ def load_traffic(kernel_tag):
     return ent.get("hbm_bytes_per_launch")
 
 
+def _db_rows(db, sql):
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        return list(con.execute(sql))
+    finally:
+        con.close()
+
+
+def _short(name):
+    base = name.replace("(anonymous namespace)::", "")
+    if base.startswith("void "):
+        base = base[5:]
+    return base.split("(")[0].strip()
+
+
+def summarize_trace(db, out_md, command):
+    """Per-kernel duration table from a rocprofv3 --kernel-trace database."""
+    rows = _db_rows(db, "select name, duration from kernels order by start")
+    stats = {}
+    for name, dur in rows:
+        stats.setdefault(_short(name), []).append(dur / 1000.0)
+    lines = [f"# Kernel trace: {os.path.basename(os.path.dirname(out_md)) and os.path.basename(out_md)[:-3]}", "",
+             "Command (on the MI355X box, from the repository root):", "", "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | total (us) |",
+             "|---|---|---|---|---|---|"]
+    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | {sum(v):.1f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    return stats
+
+
+def summarize_traffic(pmc_dir, out_md, out_json, command):
+    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a plain 1 GiB -> 1 GiB copy."""
+    def per_kernel(sub, counter):
+        rows = _db_rows(os.path.join(pmc_dir, sub, "run_results.db"),
+                        f"select name, dispatch_id, counter_value from pmc_events where counter_name='{counter}'")
+        per = {}
+        for name, disp, val in rows:
+            per.setdefault(_short(name), {}).setdefault(disp, 0.0)
+            per[_short(name)][disp] += val
+        return {k: sorted(v.values())[len(v) // 2] * 1024.0 for k, v in per.items()}   # median, bytes
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    cf, cw = per_kernel("copy_fetch", "FETCH_SIZE"), per_kernel("copy_write", "WRITE_SIZE")
+    copy = "__amd_rocclr_copyBuffer"
+    f_scale, w_scale = (1 << 30) / cf[copy], (1 << 30) / cw[copy]
+    lines = ["# HBM traffic per dispatch (rocprofv3 counters, 64K-token prefill, batch 1, d_inner 8192)", "",
+             "Commands (on the MI355X box, from the repository root):", "", "```", command, "```", "",
+             f"Calibration: a 1 GiB -> 1 GiB device copy reads FETCH_SIZE = {cf[copy] / 1024:.0f} KiB and "
+             f"WRITE_SIZE = {cw[copy] / 1024:.0f} KiB, so FETCH_SIZE is scaled by {f_scale:.3f} and "
+             f"WRITE_SIZE by {w_scale:.3f}.", "",
+             "| kernel | read (MB) | written (MB) | total (MB) |", "|---|---|---|---|"]
+    res = {}
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        if k.startswith("__amd") or k.startswith("at::"):
+            continue
+        r, w = fetch[k] * f_scale, write.get(k, 0.0) * w_scale
+        res[k] = r + w
+        lines.append(f"| {k} | {r / 1e6:.1f} | {w / 1e6:.1f} | {(r + w) / 1e6:.1f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    data = {"k_scan_64k": {"source_sha": source_digest(), "hbm_bytes_per_launch": res.get("k_scan<unsigned short, 1>"),
+                           "fetch_scale": f_scale, "write_scale": w_scale}}
+    json.dump(data, open(out_json, "w"), indent=1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,7 +143,21 @@ def main():
     ap.add_argument("--L", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (read) to 1 GiB (write), --steps times, "
+                         "to calibrate HBM byte counters")
+    ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
+    ap.add_argument("--summarize-traffic", metavar="PMC_DIR", help="write the HBM traffic summary (no GPU work)")
+    ap.add_argument("--out", help="output file of a summary")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.out, os.path.join(ROOT, "profiles", "traffic.json"),
+                          args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -95,6 +176,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": src.numel() * 4,
+                                               "bytes_written_per_copy": dst.numel() * 4,
+                                               "copies": args.steps}}))
+        return
 
     batch, L, d_inner = 1, args.L, 8192
     t_gen = time.time()

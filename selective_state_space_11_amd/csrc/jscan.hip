@@ -157,8 +157,9 @@ __device__ __forceinline__ float to_io(float v, float) { return v; }
 
 // One lane per channel, all 16 states.  Segment s (of the tokens before the
 // last rescan chunk; every segment has seg_len tokens, a multiple of kTok) of
-// sequence b: S[b][s][d][n] = state after the segment when it starts from
+// sequence b: S[b][s][n][d] = state after the segment when it starts from
 // zero, dsum[b][s][d] = sum of delta over the segment (accumulated in fp64).
+// The workspace is state-major ([n][d]) so every access is a coalesced row.
 template <class T>
 __global__ __launch_bounds__(256) void k_chunk_state(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
@@ -228,33 +229,34 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   }
   if (lo == lane) {
     const int64_t slot = b * n_segs + seg;
-    float4* Sp = reinterpret_cast<float4*>(S + (slot * d_inner + d) * NSTATE);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) Sp[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+    for (int n = 0; n < NSTATE; ++n) S[(slot * NSTATE + n) * d_inner + d] = h[n];
     dsum[slot * d_inner + d] = (float)dacc;
   }
 }
 
 // ------------------------------------------------------------ carry combine
-// One lane per (b, d, n).  Folds the segments' (P, S) pairs in sequence order,
-// h <- P * h + S with P = exp2(A' * dsum), seeded with h0, and records the
-// state each rescan chunk starts from (every seg_per_chunk segments).
+// One lane per (b, n, d), d fastest.  Folds the segments' (P, S) pairs in
+// sequence order, h <- P * h + S with P = exp2(A' * dsum), seeded with h0,
+// and records the state each rescan chunk starts from (every seg_per_chunk
+// segments) in hstart[b][c][n][d].
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, const float* __restrict__ S,
                                                  const float* __restrict__ dsum, const float* __restrict__ h0,
                                                  float* __restrict__ hstart, int64_t d_inner, int n_chunks,
                                                  int seg_per_chunk) {
-  constexpr int G = 8;                 // segments whose loads are in flight together
+  constexpr int G = 16;                // segments whose loads are in flight together
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t b = blockIdx.y;
   const int64_t per_seq = d_inner * NSTATE;
   if (i >= per_seq) return;
-  const int64_t d = i >> 4;
+  const int64_t n = i / d_inner;
+  const int64_t d = i - n * d_inner;
   const int n_segs = (n_chunks - 1) * seg_per_chunk;
-  const float a2 = A[i] * kLog2e;
+  const float a2 = A[d * NSTATE + n] * kLog2e;
   const float* Sp = S + (b * n_segs) * per_seq + i;
   const float* Dp = dsum + (b * n_segs) * d_inner + d;
   float* Hp = hstart + (b * n_chunks) * per_seq + i;
-  float h = h0 ? h0[b * per_seq + i] : 0.0f;
+  float h = h0 ? h0[(b * d_inner + d) * NSTATE + n] : 0.0f;
   Hp[0] = h;
   for (int s0 = 0; s0 < n_segs; s0 += G) {
     float sv[G], dv[G];
@@ -315,11 +317,17 @@ __global__ __launch_bounds__(64 * K) void k_scan(
   float a2[S], h[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) a2[s] = A[d * NSTATE + n0 + s] * kLog2e;
-  const float* hi = nullptr;
-  if (n_chunks > 1) hi = hinit + ((b * n_chunks + c) * d_inner + d) * NSTATE + n0;
-  else if (hinit) hi = hinit + (b * d_inner + d) * NSTATE + n0;
+  // Start state: hstart[b][c][n][d] (state-major) for chunked plans, else
+  // h0[b][d][n] or zero.
+  if (n_chunks > 1) {
+    const float* hi = hinit + ((b * n_chunks + c) * NSTATE + n0) * d_inner + d;
 #pragma unroll
-  for (int s = 0; s < S; ++s) h[s] = hi ? hi[s] : 0.0f;
+    for (int s = 0; s < S; ++s) h[s] = hi[(int64_t)s * d_inner];
+  } else {
+    const float* hi = hinit ? hinit + (b * d_inner + d) * NSTATE + n0 : nullptr;
+#pragma unroll
+    for (int s = 0; s < S; ++s) h[s] = hi ? hi[s] : 0.0f;
+  }
   const float Dd = Dw[d];
 
   const int64_t t0 = (int64_t)c * chunk_len;
