@@ -135,6 +135,117 @@ def summarize_traffic(pmc_dir, out_md, out_json, command):
     return res
 
 
+def run_all_configs(log):
+    """Time every workload of the task once (GPU) beside the oracle on a sample.
+
+    Prints one JSON line per workload.  Inputs come from synth (numpy, seeded);
+    the seven hybrid-block layers use seeds 40..46.
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import selective_state_space_11_amd as js
+
+    dev = torch.device("cuda:0")
+
+    def dio(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+    def timed(fn, reps):
+        fn(); torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record(); torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def cpu_rate(inp, n_ch):
+        d_inner = inp["x"].shape[2]
+        chans = np.linspace(0, d_inner - 1, n_ch).astype(int)
+        sub = synth.channel_slice(inp, chans)
+        t0 = time.time()
+        oracle.prefill(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["h0"])
+        return inp["x"].shape[0] * inp["x"].shape[1] * n_ch / (time.time() - t0)
+
+    def emit(name, chtok, ms, abytes, cpu, extra=None):
+        rec = {"workload": name, "gpu_ms": round(ms, 4), "channel_tokens_per_s": chtok / (ms * 1e-3),
+               "alg_GBps": round(abytes / (ms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "cpu_oracle_channel_tokens_per_s": cpu, "cpu_threads": oracle.num_threads()}
+        rec.update(extra or {})
+        print(json.dumps(rec), flush=True)
+
+    prefill_cases = [("jamba prefill batch 2 x 4096", 2, 4096, 1), ("64K context batch 1", 1, 65536, 2),
+                     ("256K context batch 1 (single call)", 1, 262144, 2)]
+    for name, batch, L, seed in prefill_cases:
+        inp = synth.prefill_inputs(batch, L, 8192, seed=seed)
+        x, dl, z, B, C = (dio(inp[k]) for k in ("x", "delta", "z", "B", "C"))
+        A, D = dio(inp["A"]), dio(inp["D"])
+        y = torch.empty_like(x)
+        hT = torch.empty(batch, 8192, 16, device=dev)
+        ws = torch.empty(max(1, js.workspace_size(batch, L, 8192)), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: js.prefill(x, dl, A, B, C, D, z, None, y=y, hT=hT, workspace=ws), 10)
+        emit(name, batch * L * 8192, ms, alg_bytes_prefill(batch, L, 8192), cpu_rate(inp, 256),
+             {"plan": js.plan(batch, L, 8192)})
+        if L == 262144:
+            state = torch.zeros(1, 8192, 16, device=dev)
+            ws2 = torch.empty(max(1, js.workspace_size(1, 4096, 8192)), dtype=torch.uint8, device=dev)
+
+            def chained():
+                state.zero_()
+                for i in range(64):
+                    sl = slice(i * 4096, (i + 1) * 4096)
+                    js.prefill(x[:, sl], dl[:, sl], A, B[:, sl], C[:, sl], D, z[:, sl], state, y=y[:, sl],
+                               hT=state, workspace=ws2)
+            ms = timed(chained, 3)
+            emit("256K context as 64 chained calls of 4096 tokens", L * 8192, ms,
+                 alg_bytes_prefill(1, L, 8192) + 64 * 2 * 8192 * 64, None, {"plan": js.plan(1, 4096, 8192)})
+        del x, dl, z, y, inp
+        torch.cuda.empty_cache()
+
+    # decode: 256 sequences, 1024 steps with per-step seeded inputs
+    n_seq = 256
+    st = dio(synth.decode_state(n_seq, 8192, seed=3))
+    A, D, _ = synth.params(8192, seed=3)
+    A, D = dio(A), dio(D)
+    steps = []
+    for k in range(1024):
+        di = synth.decode_inputs(n_seq, 8192, seed=3, step=k)
+        steps.append(tuple(dio(di[n]) for n in ("x", "delta", "z", "B", "C")))
+    yd = torch.empty(n_seq, 8192, dtype=torch.bfloat16, device=dev)
+
+    def decode_run():
+        for (dx, dd, dz, dB, dC) in steps:
+            js.step_batch(st, dx, dd, A, dB, dC, D, dz, y=yd)
+    ms = timed(decode_run, 2)
+    emit("decode 256 sequences x 1024 steps", n_seq * 8192 * 1024, ms, 1024 * alg_bytes_step(n_seq, 8192), None,
+         {"us_per_step": round(ms * 1e3 / 1024, 2)})
+    del steps
+
+    # hybrid block: seven independent Mamba layers, batch 8 x 16384
+    layers = []
+    for l in range(7):
+        inp = synth.prefill_inputs(8, 16384, 8192, seed=40 + l)
+        layers.append(tuple(dio(inp[k]) for k in ("x", "delta", "z", "B", "C", "A", "D")))
+        if l == 0:
+            cpu = cpu_rate(inp, 64)
+        del inp
+    y = torch.empty_like(layers[0][0])
+    hT = torch.empty(8, 8192, 16, device=dev)
+    ws = torch.empty(max(1, js.workspace_size(8, 16384, 8192)), dtype=torch.uint8, device=dev)
+
+    def block():
+        for (x, dl, z, B, C, A, D) in layers:
+            js.prefill(x, dl, A, B, C, D, z, None, y=y, hT=hT, workspace=ws)
+    ms = timed(block, 3)
+    emit("hybrid block: 7 layers of batch 8 x 16384", 7 * 8 * 16384 * 8192, ms,
+         7 * alg_bytes_prefill(8, 16384, 8192), cpu, {"plan": js.plan(8, 16384, 8192)})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +257,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (read) to 1 GiB (write), --steps times, "
                          "to calibrate HBM byte counters")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time every workload (batch 2 x 4K, 64K, 256K single and chained, decode x1024, "
+                         "7-layer hybrid block) with the oracle on a sample; one JSON line each")
     ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR", help="write the HBM traffic summary (no GPU work)")
     ap.add_argument("--out", help="output file of a summary")
@@ -176,6 +290,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    if args.all_configs:
+        run_all_configs(log)
+        return
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB

@@ -556,8 +556,9 @@ Plan make_plan(int64_t batch, int64_t L, int64_t d_inner, int K, int64_t C_targe
   Plan p{K, 1, std::max<int64_t>(L, 1), 1, std::max<int64_t>(L, 1)};
   if (L <= 0 || C_target <= 1) return p;
   const int64_t groups = batch * ((d_inner + 63) / 64);
-  // segments per chunk: enough chunk-local waves for 32 per SIMD, >= 64 tokens each
-  const int64_t want = (32 * 4 * kCUs + groups * (C_target - 1) - 1) / (groups * (C_target - 1));
+  // segments per chunk: about 32 chunk-local waves per SIMD (rounded down: the
+  // combine's work grows with the segment count), >= 64 tokens each
+  const int64_t want = (32 * 4 * kCUs) / (groups * (C_target - 1));
   int64_t F = std::max<int64_t>(1, std::min<int64_t>(want, (L / C_target) / kMinChunk));
   int64_t seg = (L + C_target * F - 1) / (C_target * F);
   seg = (seg + kTok - 1) / kTok * kTok;                    // whole token blocks
