@@ -57,6 +57,8 @@ def _load():
             lib.oracle_prefill.restype = None
             lib.oracle_step.argtypes = [i64, i64, i64] + [dp] * 9
             lib.oracle_step.restype = None
+            lib.oracle_prologue.argtypes = [i64, i64, i64, i64] + [dp] * 6 + [dp, dp, ctypes.c_int, dp]
+            lib.oracle_prologue.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -133,3 +135,32 @@ def step(state, x, delta, A, B, C, D, z):
     _load().oracle_step(n_seq, d_inner, d_state, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
                         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y))
     return y, state
+
+
+def prologue(x, delta, conv_weight=None, conv_bias=None, conv_state=None, dt_bias=None, softplus=False):
+    """Input prologue of a Mamba layer (see jscan_oracle.c): causal depthwise
+    convolution of x + SiLU, and delta -> softplus(delta + dt_bias).
+
+    x, delta: [batch, L, d_inner]; conv_weight: [d_inner, width] or None (no
+    convolution); conv_bias, dt_bias: [d_inner] or None; conv_state:
+    [batch, width-1, d_inner] or None (zeros).
+    Returns (xc, delta_out, conv_state_out or None), float64.
+    """
+    x = np.asarray(x)
+    batch, L, d_inner = x.shape
+    x = _f64(x, (batch, L, d_inner), "x")
+    delta = _f64(delta, (batch, L, d_inner), "delta")
+    width = 1
+    w = bias = st = None
+    if conv_weight is not None:
+        width = np.asarray(conv_weight).shape[1]
+        w = _f64(conv_weight, (d_inner, width), "conv_weight")
+        bias = None if conv_bias is None else _f64(conv_bias, (d_inner,), "conv_bias")
+        st = None if conv_state is None else _f64(conv_state, (batch, width - 1, d_inner), "conv_state")
+    dtb = None if dt_bias is None else _f64(dt_bias, (d_inner,), "dt_bias")
+    xc = np.empty_like(x)
+    dout = np.empty_like(delta)
+    st_out = np.empty((batch, width - 1, d_inner)) if w is not None else None
+    _load().oracle_prologue(batch, L, d_inner, width, _ptr(x), _ptr(w), _ptr(bias), _ptr(st), _ptr(xc),
+                            _ptr(st_out), _ptr(delta), _ptr(dtb), 1 if softplus else 0, _ptr(dout))
+    return xc, dout, st_out

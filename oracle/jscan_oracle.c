@@ -131,3 +131,70 @@ void oracle_step(int64_t n_seq, int64_t d_inner, int64_t d_state, double* state,
     }
   }
 }
+
+/*
+ * Input prologue of a Mamba layer, applied before the scan (test
+ * infrastructure, same caveats as above).
+ *
+ * Causal depthwise convolution of x along the sequence, then SiLU: the outer
+ * convolution on x_t that Mamba-1/2 apply before the recurrence (contrasted
+ * with Mamba-3's in-recurrence form in the "Mamba-3" section of the
+ * "AI Engineering from Scratch" Jamba lesson).  The pages give no kernel
+ * width; width is a parameter (the library supports 1..4).  For each b, d:
+ *
+ *   hist(t) = x[b][t][d]                               for t >= 0
+ *           = conv_state[b][width-1+t][d]              for -(width-1) <= t < 0
+ *             (0 when conv_state is NULL)
+ *   xc[b][t][d] = SiLU(bias[d] + sum_{k=0}^{width-1} w[d][k] * hist(t - (width-1) + k))
+ *
+ * and the state left for the next call is the last width-1 values of hist:
+ *   conv_state_out[b][j][d] = hist(L - (width-1) + j),  j = 0 .. width-2.
+ *
+ * Time-step prologue: delta_out = softplus(delta + dt_bias[d]) =
+ * log(1 + exp(delta + dt_bias[d])) (computed as log1p(exp(.))) when
+ * softplus != 0 (dt_bias NULL: 0), else delta unchanged.
+ *
+ * Layouts: x, delta, xc, delta_out [batch][L][d_inner]; w [d_inner][width];
+ * bias, dt_bias [d_inner]; conv_state [batch][width-1][d_inner].
+ */
+void oracle_prologue(int64_t batch, int64_t L, int64_t d_inner, int64_t width,
+                     const double* x, const double* w, const double* bias,
+                     const double* conv_state, double* xc, double* conv_state_out,
+                     const double* delta, const double* dt_bias, int softplus,
+                     double* delta_out) {
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < d_inner; ++d) {
+      for (int64_t t = 0; t < L; ++t) {
+        int64_t i = (b * L + t) * d_inner + d;
+        if (w) {
+          double acc = bias ? bias[d] : 0.0;
+          for (int64_t k = 0; k < width; ++k) {
+            int64_t s = t - (width - 1) + k;      /* source token */
+            double v;
+            if (s >= 0) v = x[(b * L + s) * d_inner + d];
+            else v = conv_state ? conv_state[(b * (width - 1) + (width - 1 + s)) * d_inner + d] : 0.0;
+            acc += w[d * width + k] * v;
+          }
+          xc[i] = acc / (1.0 + exp(-acc));
+        } else {
+          xc[i] = x[i];
+        }
+        if (softplus) {
+          double v = delta[i] + (dt_bias ? dt_bias[d] : 0.0);
+          delta_out[i] = log1p(exp(v));
+        } else {
+          delta_out[i] = delta[i];
+        }
+      }
+      if (conv_state_out) {
+        for (int64_t j = 0; j < width - 1; ++j) {
+          int64_t s = L - (width - 1) + j;
+          double v;
+          if (s >= 0) v = x[(b * L + s) * d_inner + d];
+          else v = conv_state ? conv_state[(b * (width - 1) + (width - 1 + s)) * d_inner + d] : 0.0;
+          conv_state_out[(b * (width - 1) + j) * d_inner + d] = v;
+        }
+      }
+    }
+  }
+}

@@ -333,3 +333,66 @@ def test_thread_count_does_not_change_result():
         oracle.set_num_threads(n0)
     np.testing.assert_array_equal(y1, y2)
     np.testing.assert_array_equal(h1, h2)
+
+
+# ------------------------------------------------------------ input prologue
+def prologue_problem(rng, batch, L, d_inner, width):
+    x = rng.standard_normal((batch, L, d_inner))
+    delta = rng.standard_normal((batch, L, d_inner)) - 2.0
+    w = rng.standard_normal((d_inner, width)) / width
+    bias = rng.standard_normal(d_inner) / 4
+    state = rng.standard_normal((batch, width - 1, d_inner))
+    dt_bias = rng.standard_normal(d_inner) / 2
+    return x, delta, w, bias, state, dt_bias
+
+
+@pytest.mark.parametrize("width", [1, 2, 4])
+def test_prologue_conv_matches_scipy_fir(width):
+    """Causal depthwise convolution = an FIR filter per channel (scipy.signal.lfilter
+    with taps reversed), run over the history prepended to the sequence."""
+    rng = np.random.default_rng(30 + width)
+    x, delta, w, bias, state, _ = prologue_problem(rng, 2, 57, 5, width)
+    xc, _, st_out = oracle.prologue(x, delta, w, bias, state)
+    for b in range(2):
+        for d in range(5):
+            seq = np.concatenate([state[b, :, d], x[b, :, d]])
+            pre = scipy.signal.lfilter(w[d, ::-1], [1.0], seq)[width - 1:] + bias[d]
+            np.testing.assert_allclose(xc[b, :, d], silu_lib(pre), rtol=1e-13, atol=1e-15)
+            np.testing.assert_array_equal(st_out[b, :, d], seq[len(seq) - (width - 1):])
+
+
+def test_prologue_conv_zero_history_and_no_conv():
+    rng = np.random.default_rng(34)
+    x, delta, w, bias, _, _ = prologue_problem(rng, 1, 20, 3, 4)
+    xc, dout, st = oracle.prologue(x, delta, w, None, None)
+    for d in range(3):
+        pre = np.convolve(x[0, :, d], w[d, ::-1])[:20]          # zero history, no bias
+        np.testing.assert_allclose(xc[0, :, d], silu_lib(pre), rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(dout, delta)                   # softplus off: delta passes through
+    xc2, _, st2 = oracle.prologue(x, delta)                       # no convolution: x passes through
+    np.testing.assert_array_equal(xc2, x)
+    assert st2 is None
+
+
+def test_prologue_softplus_matches_library():
+    rng = np.random.default_rng(35)
+    x, delta, _, _, _, dt_bias = prologue_problem(rng, 2, 40, 6, 4)
+    delta[0, 0, 0], delta[0, 1, 0] = -40.0, 15.0               # far tails of softplus
+    _, dout, _ = oracle.prologue(x, delta, dt_bias=dt_bias, softplus=True)
+    v = torch.as_tensor(delta + dt_bias[None, None, :])
+    ref = torch.nn.functional.softplus(v, threshold=50.0).numpy()
+    np.testing.assert_allclose(dout, ref, rtol=1e-13, atol=0)
+    assert np.all(dout > 0)
+
+
+def test_prologue_state_carry_equals_one_call():
+    """Splitting the sequence and carrying the conv state gives the same bits."""
+    rng = np.random.default_rng(36)
+    x, delta, w, bias, state, dt_bias = prologue_problem(rng, 2, 61, 4, 4)
+    xc, dout, st = oracle.prologue(x, delta, w, bias, state, dt_bias, True)
+    xa, da, sa = oracle.prologue(x[:, :2], delta[:, :2], w, bias, state, dt_bias, True)   # shorter than the window
+    xb, db, sb = oracle.prologue(x[:, 2:30], delta[:, 2:30], w, bias, sa, dt_bias, True)
+    xz, dz, sz = oracle.prologue(x[:, 30:], delta[:, 30:], w, bias, sb, dt_bias, True)
+    np.testing.assert_array_equal(np.concatenate([xa, xb, xz], axis=1), xc)
+    np.testing.assert_array_equal(np.concatenate([da, db, dz], axis=1), dout)
+    np.testing.assert_array_equal(sz, st)
