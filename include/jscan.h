@@ -122,6 +122,59 @@ jscan_status jscan_step_batch(int64_t n_seq, int64_t d_inner, int64_t d_state, j
                               const void* B, const void* C, const float* D, const void* z,
                               void* y, void* stream);
 
+/*
+ * Optional input prologue of a Mamba layer, fused into the scan: the steps
+ * Mamba-1/2 apply to x and delta before the recurrence.  The "AI Engineering
+ * from Scratch" Jamba lesson (section "Mamba-3") contrasts Mamba-3's
+ * in-recurrence form with the "outer convolution on x_t" of the earlier
+ * models; the pages give no kernel width (1..4 here, Mamba's usual 4).
+ *
+ *  - Causal depthwise convolution of x over the sequence, then SiLU:
+ *      xc[t][d] = SiLU(conv_bias[d] + sum_k conv_weight[d][k] * x[t - (conv_width-1) + k][d])
+ *    where x before the first token comes from conv_state_in (the previous
+ *    call's last conv_width-1 raw x, [nseq][conv_width-1][d_inner] fp32;
+ *    NULL = zeros).  The scan then uses xc wherever it used x (input term
+ *    and D skip).  conv_state_out receives the last conv_width-1 raw x of
+ *    this call (NULL: not written; it may be the same buffer as
+ *    conv_state_in, for an in-place carry).  conv_weight NULL: no
+ *    convolution (conv_bias and the conv states must then be NULL).
+ *  - dt_softplus != 0: delta := softplus(delta + dt_bias[d]) =
+ *    log(1 + exp(delta + dt_bias[d])) (dt_bias NULL: no bias).
+ *
+ * All prologue arrays are fp32 device pointers, 16-byte aligned.  nseq is
+ * the batch (prefill) or n_seq (decode step).
+ */
+typedef struct {
+  const float* conv_weight;   /* [d_inner][conv_width] */
+  const float* conv_bias;     /* [d_inner] */
+  const float* conv_state_in; /* [nseq][conv_width-1][d_inner] */
+  float* conv_state_out;      /* [nseq][conv_width-1][d_inner] */
+  const float* dt_bias;       /* [d_inner] */
+  int32_t conv_width;         /* 1..4 */
+  int32_t dt_softplus;        /* nonzero: softplus(delta + dt_bias) */
+} jscan_prologue;
+
+/*
+ * jscan_prefill with the input prologue above applied to x and delta (NULL
+ * prologue = jscan_prefill).  Same arguments, layouts and errors otherwise;
+ * a bad conv_width returns JSCAN_ERR_UNSUPPORTED.  Runs the scan with one
+ * wave per 64 channels whatever the plan override says.
+ */
+jscan_status jscan_prefill_fused(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                 const void* x, const void* delta, const float* A, const void* B,
+                                 const void* C, const float* D, const void* z, const float* h0,
+                                 void* y, float* hT, const jscan_prologue* prologue, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * jscan_step_batch with the input prologue (conv state [n_seq][conv_width-1]
+ * [d_inner], normally updated in place: conv_state_out == conv_state_in).
+ */
+jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
+                                    float* state, const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    void* y, const jscan_prologue* prologue, void* stream);
+
 /* Static name of a status code. */
 const char* jscan_status_string(jscan_status status);
 

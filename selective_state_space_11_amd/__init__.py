@@ -11,6 +11,9 @@ Entry points mirror the C ABI in ``include/jscan.h``:
 * ``prefill(x, delta, A, B, C, D, z, h0=None)`` -> ``(y, hT)``
 * ``step(state, x, delta, A, B, C, D, z)`` -> ``y`` (state updated in place)
 * ``step_batch(state, x, delta, A, B, C, D, z)`` -> ``y`` (states updated in place)
+* ``prefill_fused`` / ``step_batch_fused``: the same with the layer's input
+  prologue (causal depthwise conv + SiLU on x, softplus(delta + dt_bias))
+  applied inside the scan kernels
 * ``workspace_size``, ``plan``, ``set_plan_override``, ``time_next_prefill``
 """
 from __future__ import annotations
@@ -30,7 +33,15 @@ IO_F32, IO_BF16 = 0, 1
 
 EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_step", "jscan_step_batch",
            "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
-           "jscan_set_plan_override", "jscan_time_next_prefill")
+           "jscan_set_plan_override", "jscan_time_next_prefill", "jscan_prefill_fused",
+           "jscan_step_batch_fused")
+
+
+class Prologue(ctypes.Structure):
+    """struct jscan_prologue (device pointers as integers)."""
+    _fields_ = [("conv_weight", ctypes.c_void_p), ("conv_bias", ctypes.c_void_p),
+                ("conv_state_in", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("dt_softplus", ctypes.c_int32)]
 
 
 class JscanUnavailable(RuntimeError):
@@ -80,6 +91,12 @@ def load_library(path: str = LIB_PATH):
         lib.jscan_set_plan_override.restype = st
         lib.jscan_time_next_prefill.argtypes = [vp, vp]
         lib.jscan_time_next_prefill.restype = None
+        pp = ctypes.POINTER(Prologue)
+        lib.jscan_prefill_fused.argtypes = [i64, i64, i64, i64, st, vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, pp, vp,
+                                            sz, vp]
+        lib.jscan_prefill_fused.restype = st
+        lib.jscan_step_batch_fused.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, pp, vp]
+        lib.jscan_step_batch_fused.restype = st
         _lib = lib
         return lib
 
@@ -229,4 +246,89 @@ def step(state, x, delta, A, B, C, D, z, *, y=None, stream=None):
     _dev(y, "y", x.dtype, x.shape)
     _check(lib.jscan_step(d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
                           _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(stream)))
+    return y
+
+
+def _prologue(nseq, d_inner, conv_weight, conv_bias, conv_state_in, conv_state_out, dt_bias, softplus):
+    torch = _torch()
+    width = 1
+    if conv_weight is not None:
+        _dev(conv_weight, "conv_weight", torch.float32)
+        if conv_weight.dim() != 2 or conv_weight.shape[0] != d_inner:
+            raise ValueError(f"conv_weight must be [{d_inner}, width], got {tuple(conv_weight.shape)}")
+        width = conv_weight.shape[1]
+        _dev(conv_bias, "conv_bias", torch.float32, (d_inner,))
+        _dev(conv_state_in, "conv_state_in", torch.float32, (nseq, width - 1, d_inner))
+        _dev(conv_state_out, "conv_state_out", torch.float32, (nseq, width - 1, d_inner))
+    _dev(dt_bias, "dt_bias", torch.float32, (d_inner,))
+    p = Prologue()
+    p.conv_weight = None if conv_weight is None else conv_weight.data_ptr()
+    p.conv_bias = None if conv_bias is None else conv_bias.data_ptr()
+    p.conv_state_in = None if conv_state_in is None else conv_state_in.data_ptr()
+    p.conv_state_out = None if conv_state_out is None else conv_state_out.data_ptr()
+    p.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
+    p.conv_width = width
+    p.dt_softplus = 1 if softplus else 0
+    return p
+
+
+def prefill_fused(x, delta, A, B, C, D, z, h0=None, *, conv_weight=None, conv_bias=None, conv_state_in=None,
+                  conv_state_out=None, dt_bias=None, softplus=False, y=None, hT=None, want_state=True,
+                  workspace=None, stream=None):
+    """prefill with the input prologue: x -> SiLU(causal depthwise conv(x) + conv_bias)
+    (conv_weight [d_inner, width], width 1..4; conv_state_in/out [batch, width-1, d_inner],
+    may be one tensor) and, with softplus, delta -> softplus(delta + dt_bias).  Returns (y, hT)."""
+    torch = _torch()
+    lib = load_library()
+    _dev(x, "x")
+    batch, L, d_inner = x.shape
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (batch, L, D_STATE))
+    _dev(C, "C", x.dtype, (batch, L, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, D_STATE))
+    pro = _prologue(batch, d_inner, conv_weight, conv_bias, conv_state_in, conv_state_out, dt_bias, softplus)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    if hT is None and want_state:
+        hT = torch.empty((batch, d_inner, D_STATE), dtype=torch.float32, device=x.device)
+    _dev(hT, "hT", torch.float32, (batch, d_inner, D_STATE))
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.jscan_prefill_fused(batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), ctypes.byref(pro),
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
+    return y, hT
+
+
+def step_batch_fused(state, x, delta, A, B, C, D, z, *, conv_weight=None, conv_bias=None, conv_state=None,
+                     dt_bias=None, softplus=False, y=None, stream=None):
+    """step_batch with the input prologue; conv_state [n_seq, width-1, d_inner] holds the last
+    width-1 raw x of each sequence and is updated in place, like state."""
+    torch = _torch()
+    lib = load_library()
+    _dev(state, "state", torch.float32)
+    n_seq, d_inner, _ = state.shape
+    _dev(state, "state", torch.float32, (n_seq, d_inner, D_STATE))
+    _dev(x, "x", None, (n_seq, d_inner))
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (n_seq, D_STATE))
+    _dev(C, "C", x.dtype, (n_seq, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    pro = _prologue(n_seq, d_inner, conv_weight, conv_bias, conv_state, conv_state, dt_bias, softplus)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    _check(lib.jscan_step_batch_fused(n_seq, d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                                      _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), ctypes.byref(pro),
+                                      _stream(stream)))
     return y

@@ -70,6 +70,80 @@ __device__ __forceinline__ float silu(float zv) {
   return zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
 }
 
+// softplus(v) = log(1 + exp(v)), through v_exp_f32 / v_log_f32 (base 2).  For
+// v > 15 it equals v to fp32 precision; for tiny exp(v) log(1 + e) ~ e - e^2/2.
+__device__ __forceinline__ float softplus(float v) {
+  const float e = fast_exp2(v * kLog2e);
+  const float r = e < 1.0e-3f ? e - 0.5f * e * e : __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
+  return v > 15.0f ? v : r;
+}
+
+// Optional input prologue of a Mamba layer, applied per token as x and delta
+// are loaded:
+//   x  -> SiLU(conv_b + sum_k w[k] * x[t - (width - 1) + k])   (causal depthwise conv)
+//   dt -> softplus(dt + dt_bias)
+// The convolution keeps the last three raw x of its channel in registers;
+// taps are right-aligned in a 4-tap window with the missing ones zero, which
+// adds exact zeros.
+struct ProArgs {
+  const float* conv_w;      // [d_inner][width], or null: no convolution
+  const float* conv_b;      // [d_inner], or null
+  const float* hist;        // [batch][width-1][d_inner] history before the sequence, or null (zeros)
+  float* hist_out;          // [batch][width-1][d_inner] history after it, or null
+  const float* dt_bias;     // [d_inner], or null
+  int width;
+};
+
+template <bool CONV, bool SP>
+struct Prologue {
+  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, cb = 0.f, dtb = 0.f;
+  float h1 = 0.f, h2 = 0.f, h3 = 0.f;       // raw x of tokens t-1, t-2, t-3
+  __device__ __forceinline__ void init(const ProArgs& p, int64_t d) {
+    if constexpr (CONV) {
+      // tap k of the caller's width-W filter goes to slot 4 - W + k
+      const float* wr = p.conv_w + d * p.width;
+      const int off = 4 - p.width;
+      w3 = wr[p.width - 1];
+      w2 = off <= 2 ? wr[2 - off] : 0.f;
+      w1 = off <= 1 ? wr[1 - off] : 0.f;
+      w0 = off <= 0 ? wr[0] : 0.f;
+      cb = p.conv_b ? p.conv_b[d] : 0.f;
+    }
+    if constexpr (SP) dtb = p.dt_bias ? p.dt_bias[d] : 0.f;
+  }
+  // Raw x before token t0 of sequence b: from x itself, or from the history
+  // given for the sequence start (hist, or zeros).
+  template <class T>
+  __device__ __forceinline__ float before(const ProArgs& p, const float* hist, const T* x, int64_t b, int64_t L,
+                                          int64_t d_inner, int64_t pos, int64_t d) const {
+    if (pos >= 0) return widen(x[(b * L + pos) * d_inner + d]);
+    const int64_t j = (p.width - 1) + pos;
+    return (hist && j >= 0) ? hist[(b * (p.width - 1) + j) * d_inner + d] : 0.f;
+  }
+  template <class T>
+  __device__ __forceinline__ void start(const ProArgs& p, const float* hist, const T* x, int64_t b, int64_t L,
+                                        int64_t d_inner, int64_t t0, int64_t d) {
+    if constexpr (CONV) {
+      h1 = before(p, hist, x, b, L, d_inner, t0 - 1, d);
+      h2 = before(p, hist, x, b, L, d_inner, t0 - 2, d);
+      h3 = before(p, hist, x, b, L, d_inner, t0 - 3, d);
+    }
+  }
+  __device__ __forceinline__ float xin(float xv) {
+    if constexpr (CONV) {
+      const float acc = fmaf(w3, xv, fmaf(w2, h1, fmaf(w1, h2, fmaf(w0, h3, cb))));
+      h3 = h2; h2 = h1; h1 = xv;
+      return silu(acc);
+    } else {
+      return xv;
+    }
+  }
+  __device__ __forceinline__ float dt(float dv) const {
+    if constexpr (SP) return softplus(dv + dtb);
+    else return dv;
+  }
+};
+
 // ------------------------------------------------- chunk-local end states
 // Load S consecutive floats from a wave-uniform address (scalar loads).
 template <int S>
@@ -160,11 +234,11 @@ __device__ __forceinline__ float to_io(float v, float) { return v; }
 // sequence b: S[b][s][n][d] = state after the segment when it starts from
 // zero, dsum[b][s][d] = sum of delta over the segment (accumulated in fp64).
 // The workspace is state-major ([n][d]) so every access is a coalesced row.
-template <class T>
+template <class T, bool CONV = false, bool SP = false>
 __global__ __launch_bounds__(256) void k_chunk_state(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, float* __restrict__ S, float* __restrict__ dsum,
-    int64_t L, int64_t d_inner, int64_t seg_len, int n_segs) {
+    int64_t L, int64_t d_inner, int64_t seg_len, int n_segs, ProArgs pa) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t gbase = ((int64_t)blockIdx.x * 4 + wave) * 64;
@@ -193,6 +267,9 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   const T* brow = Bm + (b * L + t0) * NSTATE;
   const uint32_t lb = (uint32_t)lo * sizeof(T);      // lane byte offset within a row
   const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
+  Prologue<CONV, SP> pro;
+  pro.init(pa, d);
+  pro.start(pa, pa.hist, x, b, L, d_inner, t0, d);
 
   // Loads of token block bb (always kTok whole tokens: segments are multiples).
   auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok]) {
@@ -206,8 +283,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
-      const float dt = widen(dd[j]);
-      const float dx = dt * widen(xx[j]);
+      const float dt = pro.dt(widen(dd[j]));
+      const float dx = dt * pro.xin(widen(xx[j]));
       dacc += (double)dt;
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
@@ -240,10 +317,16 @@ __global__ __launch_bounds__(256) void k_chunk_state(
 // sequence order, h <- P * h + S with P = exp2(A' * dsum), seeded with h0,
 // and records the state each rescan chunk starts from (every seg_per_chunk
 // segments) in hstart[b][c][n][d].
+//
+// With a convolution prologue it also copies the conv history before the
+// sequence into the workspace (hist_copy), so the rescan's first chunk never
+// reads the caller's history buffer, which the last chunk may overwrite in
+// place.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, const float* __restrict__ S,
                                                  const float* __restrict__ dsum, const float* __restrict__ h0,
                                                  float* __restrict__ hstart, int64_t d_inner, int n_chunks,
-                                                 int seg_per_chunk) {
+                                                 int seg_per_chunk, const float* __restrict__ hist,
+                                                 float* __restrict__ hist_copy, int hist_rows) {
   constexpr int G = 16;                // segments whose loads are in flight together
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t b = blockIdx.y;
@@ -252,6 +335,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, co
   const int64_t n = i / d_inner;
   const int64_t d = i - n * d_inner;
   const int n_segs = (n_chunks - 1) * seg_per_chunk;
+  if (hist_copy && n < hist_rows) {
+    const int64_t o = (b * hist_rows + n) * d_inner + d;
+    hist_copy[o] = hist ? hist[o] : 0.0f;
+  }
   const float a2 = A[d * NSTATE + n] * kLog2e;
   const float* Sp = S + (b * n_segs) * per_seq + i;
   const float* Dp = dsum + (b * n_segs) * d_inner + d;
@@ -284,6 +371,7 @@ struct ScanArgs {
   void* y; float* hT;
   int64_t L, d_inner, chunk_len;
   int n_chunks;
+  ProArgs pa;
 };
 
 // Grid: (ceil(d_inner / 64), chunks, batch); block: K waves.  Wave g of a
@@ -297,12 +385,13 @@ struct ScanArgs {
 // 0 * x * B = 0 for finite x and B) and their output equals the last token's,
 // which they store again to the same address.  Every block therefore runs the
 // same branch-free code.
-template <class T, int K>
+template <class T, int K, bool CONV = false, bool SP = false>
 __global__ __launch_bounds__(64 * K) void k_scan(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dw, const T* __restrict__ z,
     const float* __restrict__ hinit, T* __restrict__ y, float* __restrict__ hT,
-    int64_t L, int64_t d_inner, int64_t chunk_len, int n_chunks) {
+    int64_t L, int64_t d_inner, int64_t chunk_len, int n_chunks, ProArgs pa) {
+  static_assert(K == 1 || !(CONV || SP), "the input prologue runs with one wave per 64 channels");
   constexpr int S = NSTATE / K;
   constexpr int F = kTok / K;          // tokens of a block finished by each wave
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -344,6 +433,9 @@ __global__ __launch_bounds__(64 * K) void k_scan(
 
   const uint32_t lb = (uint32_t)lo * sizeof(T);      // lane byte offset within a row
   const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
+  Prologue<CONV, SP> pro;
+  pro.init(pa, d);
+  pro.start(pa, pa.hist, x, b, L, d_inner, t0, d);
 
   // Loads of token block bb.  Rows past the chunk's end are clamped onto its
   // last token, and their delta is read through an empty resource (0).
@@ -372,9 +464,11 @@ __global__ __launch_bounds__(64 * K) void k_scan(
   int buf = 0;
   // y of token bb + j (padding tokens map onto the last token's address and
   // store the identical value again).
+  // With a convolution, a padding token's input differs (its history has
+  // shifted), so only real tokens store.
   auto finish = [&](__amdgpu_buffer_rsrc_t ry, int bb, int j, float acc, float xv, float zv) {
     const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
-    buf_store(to_io(fmaf(Dd, xv, acc) * silu(zv), T()), ry, lb, so);
+    if (!CONV || bb + j < nt) buf_store(to_io(fmaf(Dd, xv, acc) * silu(zv), T()), ry, lb, so);
   };
   auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
                       const T (&xff)[F], const T (&zff)[F]) {
@@ -384,8 +478,10 @@ __global__ __launch_bounds__(64 * K) void k_scan(
     for (int j = 0; j < kTok; ++j) {
       Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
-      const float dt = widen(dd[j]);
-      const float xv = widen(xx[j]);
+      // A padding token's delta reads 0; softplus would turn that into a
+      // positive step, so it is forced back to 0 (a wave-uniform select).
+      const float dt = SP ? (bb + j < nt ? pro.dt(widen(dd[j])) : 0.0f) : widen(dd[j]);
+      const float xv = pro.xin(widen(xx[j]));
       const float dx = dt * xv;
 #pragma unroll
       for (int s = 0; s < S; ++s) h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bc[s]);
@@ -438,6 +534,17 @@ __global__ __launch_bounds__(64 * K) void k_scan(
 #pragma unroll
     for (int s = 0; s < S; ++s) ho[s] = h[s];
   }
+  // Conv history after the sequence: its last width-1 raw x (read back from
+  // x, or from the history before it when the sequence is shorter).  With
+  // chunks > 1 every read here comes from x, so an in-place history is safe.
+  if constexpr (CONV) {
+    if (pa.hist_out && c == n_chunks - 1 && lo == lane) {
+      for (int j = 0; j < pa.width - 1; ++j) {
+        const float v = pro.before(pa, pa.hist, x, b, L, d_inner, L - (pa.width - 1) + j, d);
+        pa.hist_out[(b * (pa.width - 1) + j) * d_inner + d] = v;
+      }
+    }
+  }
 }
 
 // Copy (or zero) the state for an empty sequence: hT = h0, or 0 when h0 is null.
@@ -452,12 +559,16 @@ __global__ __launch_bounds__(256) void k_copy_state(const float* __restrict__ sr
 // channel (64 bytes) is read and written as four float4s by adjacent lanes,
 // so a wave moves 1 KiB of contiguous state per access.  The partial sums
 // C.h of the four lanes are added with two xor shuffles inside the quad.
-template <class T>
+// With a convolution prologue the conv history of the channel
+// (pa.hist[s][j][d], width-1 raw x) is read first and the shifted history,
+// ending with this token's x, written by the quad's first lane (in place
+// allowed).
+template <class T, bool CONV = false, bool SP = false>
 __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T* __restrict__ x,
                                               const T* __restrict__ delta, const float* __restrict__ A,
                                               const T* __restrict__ B, const T* __restrict__ C,
                                               const float* __restrict__ D, const T* __restrict__ z,
-                                              T* __restrict__ y, int64_t n_seq, int64_t d_inner) {
+                                              T* __restrict__ y, int64_t n_seq, int64_t d_inner, ProArgs pa) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = n_seq * d_inner * 4;
   const bool active = gid < total;
@@ -469,8 +580,22 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
 
   float4 hv = reinterpret_cast<const float4*>(state)[g];
   const float4 av = reinterpret_cast<const float4*>(A)[d * 4 + q];
-  const float dt = widen(delta[sd]);
-  const float xv = widen(x[sd]);
+  Prologue<CONV, SP> pro;
+  pro.init(pa, d);
+  const float xraw = widen(x[sd]);
+  float hist[3] = {0.f, 0.f, 0.f};              // oldest first: x[t-(width-1)] .. x[t-1]
+  const int hw = pa.width - 1;                  // history length (0..3)
+  if constexpr (CONV) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < hw && pa.hist) hist[j] = pa.hist[(s * hw + j) * d_inner + d];
+    // x[t-1], x[t-2], x[t-3] out of the history, oldest first
+    pro.h1 = hw == 3 ? hist[2] : hw == 2 ? hist[1] : hw == 1 ? hist[0] : 0.f;
+    pro.h2 = hw == 3 ? hist[1] : hw == 2 ? hist[0] : 0.f;
+    pro.h3 = hw == 3 ? hist[0] : 0.f;
+  }
+  const float xv = pro.xin(xraw);
+  const float dt = pro.dt(widen(delta[sd]));
   const T* Bs = B + s * NSTATE + 4 * q;
   const T* Cs = C + s * NSTATE + 4 * q;
   const float dx = dt * xv;
@@ -486,7 +611,16 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
   part += __shfl_xor(part, 2, 4);
   if (active) {
     reinterpret_cast<float4*>(state)[g] = hv;
-    if (q == 0) store_io(y + sd, fmaf(D[d], xv, part) * silu(widen(z[sd])));
+    if (q == 0) {
+      store_io(y + sd, fmaf(D[d], xv, part) * silu(widen(z[sd])));
+      if constexpr (CONV) {
+        if (pa.hist_out) {
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            if (j < hw) pa.hist_out[(s * hw + j) * d_inner + d] = j + 1 < hw ? hist[j + 1] : xraw;
+        }
+      }
+    }
   }
 }
 
@@ -598,7 +732,7 @@ Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner) {
 
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-struct WsLayout { size_t S, dsum, hstart, total; };
+struct WsLayout { size_t S, dsum, hstart, hist, total; };
 
 WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   WsLayout w{};
@@ -607,8 +741,9 @@ WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
     w.S = round_up((size_t)batch * segs * (size_t)d_inner * NSTATE * sizeof(float));
     w.dsum = round_up((size_t)batch * segs * (size_t)d_inner * sizeof(float));
     w.hstart = round_up((size_t)batch * (size_t)p.chunks * (size_t)d_inner * NSTATE * sizeof(float));
+    w.hist = round_up((size_t)batch * 3 * (size_t)d_inner * sizeof(float));   // conv history copy
   }
-  w.total = w.S + w.dsum + w.hstart;
+  w.total = w.S + w.dsum + w.hstart + w.hist;
   return w;
 }
 
@@ -621,56 +756,74 @@ bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner) {
   return L <= INT32_MAX && batch <= 65535;
 }
 
-template <class T, int K>
+template <class T, int K, bool CONV, bool SP>
 hipError_t launch_scan(const ScanArgs& a, int64_t batch, hipStream_t st) {
   dim3 grid((unsigned)((a.d_inner + 63) / 64), (unsigned)a.n_chunks, (unsigned)batch);
-  hipLaunchKernelGGL((k_scan<T, K>), grid, dim3(64 * K), 0, st, static_cast<const T*>(a.x),
+  hipLaunchKernelGGL((k_scan<T, K, CONV, SP>), grid, dim3(64 * K), 0, st, static_cast<const T*>(a.x),
                      static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
                      a.D, static_cast<const T*>(a.z), a.hinit,
-                     static_cast<T*>(a.y), a.hT, a.L, a.d_inner, a.chunk_len, a.n_chunks);
+                     static_cast<T*>(a.y), a.hT, a.L, a.d_inner, a.chunk_len, a.n_chunks, a.pa);
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool CONV, bool SP>
 hipError_t launch_scan_k(int K, const ScanArgs& a, int64_t batch, hipStream_t st) {
-  switch (K) {
-    case 1: return launch_scan<T, 1>(a, batch, st);
-    case 2: return launch_scan<T, 2>(a, batch, st);
-    case 4: return launch_scan<T, 4>(a, batch, st);
-    default: return launch_scan<T, 8>(a, batch, st);
+  if constexpr (CONV || SP) {
+    return launch_scan<T, 1, CONV, SP>(a, batch, st);     // the prologue runs with K = 1
+  } else {
+    switch (K) {
+      case 1: return launch_scan<T, 1, false, false>(a, batch, st);
+      case 2: return launch_scan<T, 2, false, false>(a, batch, st);
+      case 4: return launch_scan<T, 4, false, false>(a, batch, st);
+      default: return launch_scan<T, 8, false, false>(a, batch, st);
+    }
   }
 }
 
-template <class T>
+template <class T, bool CONV, bool SP>
 jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* x, const void* delta,
                          const float* A, const void* B, const void* C, const float* D, const void* z,
-                         const float* h0, void* y, float* hT, char* ws, const Plan& p,
+                         const float* h0, void* y, float* hT, char* ws, const Plan& p, const ProArgs& pa,
                          hipStream_t st) {
   const WsLayout w = ws_layout(batch, L, d_inner, p);
   float* S = reinterpret_cast<float*>(ws);
   float* dsum = reinterpret_cast<float*>(ws + w.S);
   float* hstart = reinterpret_cast<float*>(ws + w.S + w.dsum);
+  float* hist_copy = reinterpret_cast<float*>(ws + w.S + w.dsum + w.hstart);
   hipError_t e;
 
+  ProArgs scan_pa = pa;
   if (p.chunks > 1) {
     const int segs = (int)p.segments();
     dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)segs, (unsigned)batch);
-    hipLaunchKernelGGL((k_chunk_state<T>), g1, dim3(256), 0, st, static_cast<const T*>(x),
+    hipLaunchKernelGGL((k_chunk_state<T, CONV, SP>), g1, dim3(256), 0, st, static_cast<const T*>(x),
                        static_cast<const T*>(delta), A, static_cast<const T*>(B), S, dsum, L, d_inner, p.seg_len,
-                       segs);
+                       segs, pa);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
+    const int hist_rows = CONV ? pa.width - 1 : 0;
     dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
     hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks,
-                       p.seg_per_chunk);
+                       p.seg_per_chunk, pa.hist, hist_rows > 0 ? hist_copy : nullptr, hist_rows);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
+    if (hist_rows > 0) scan_pa.hist = hist_copy;
   }
-  ScanArgs a{x, delta, A, B, C, D, z, p.chunks > 1 ? hstart : h0, y, hT, L, d_inner, p.chunk_len, p.chunks};
+  ScanArgs a{x, delta, A, B, C, D, z, p.chunks > 1 ? hstart : h0, y, hT, L, d_inner, p.chunk_len, p.chunks,
+             scan_pa};
   hipEvent_t eb = t_ev_before, ea = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
   if (eb && ea && (e = hipEventRecord(eb, st)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = launch_scan_k<T>(p.K, a, batch, st)) != hipSuccess) return hip_fail(e, "scan launch");
+  if ((e = launch_scan_k<T, CONV, SP>(p.K, a, batch, st)) != hipSuccess) return hip_fail(e, "scan launch");
   if (eb && ea && (e = hipEventRecord(ea, st)) != hipSuccess) return hip_fail(e, "event record");
   return JSCAN_OK;
+}
+
+// Calls f(integral_constant<bool, CONV>, integral_constant<bool, SP>).
+template <class F>
+auto with_prologue(bool conv, bool sp, F&& f) {
+  if (conv && sp) return f(std::true_type{}, std::true_type{});
+  if (conv) return f(std::true_type{}, std::false_type{});
+  if (sp) return f(std::false_type{}, std::true_type{});
+  return f(std::false_type{}, std::false_type{});
 }
 
 jscan_status check_common(int64_t d_state, jscan_io io) {
@@ -695,18 +848,181 @@ jscan_status check_ranges(const Range* in, int n_in, const Range* out, int n_out
   return JSCAN_OK;
 }
 
-template <class T>
+template <class T, bool CONV, bool SP>
 jscan_status run_step(int64_t n_seq, int64_t d_inner, float* state, const void* x, const void* delta,
                       const float* A, const void* B, const void* C, const float* D, const void* z,
-                      void* y, hipStream_t st) {
+                      void* y, const ProArgs& pa, hipStream_t st) {
   const int64_t total = n_seq * d_inner * 4;
-  hipLaunchKernelGGL((k_step<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, state,
+  hipLaunchKernelGGL((k_step<T, CONV, SP>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, state,
                      static_cast<const T*>(x), static_cast<const T*>(delta), A, static_cast<const T*>(B),
                      static_cast<const T*>(C), D, static_cast<const T*>(z), static_cast<T*>(y), n_seq,
-                     d_inner);
+                     d_inner, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "step launch");
   return JSCAN_OK;
+}
+
+// Validates the optional prologue and fills `pa`; appends its arrays to the
+// input and output range lists for the alias check.  nseq = batch (prefill)
+// or n_seq (step).
+jscan_status check_prologue(const jscan_prologue* pro, int64_t nseq, int64_t d_inner, ProArgs* pa,
+                            Range* in, int* n_in, Range* out, int* n_out) {
+  *pa = ProArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 1};
+  if (!pro) return JSCAN_OK;
+  if (pro->conv_weight) {
+    if (pro->conv_width < 1 || pro->conv_width > 4)
+      return fail(JSCAN_ERR_UNSUPPORTED, "conv_width must be 1..4");
+    pa->conv_w = pro->conv_weight;
+    pa->conv_b = pro->conv_bias;
+    pa->hist = pro->conv_state_in;
+    pa->hist_out = pro->conv_state_out;
+    pa->width = pro->conv_width;
+  } else if (pro->conv_bias || pro->conv_state_in || pro->conv_state_out) {
+    return fail(JSCAN_ERR_NULL, "conv_bias / conv_state given without conv_weight");
+  }
+  if (pro->dt_softplus) pa->dt_bias = pro->dt_bias;
+  const void* ptrs[] = {pro->conv_weight, pro->conv_bias, pro->conv_state_in, pro->conv_state_out,
+                        pro->dt_bias};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  const size_t hb = (size_t)nseq * (size_t)(pa->width - 1) * (size_t)d_inner * 4;
+  in[(*n_in)++] = Range{pa->conv_w, (size_t)d_inner * pa->width * 4, "conv_weight"};
+  in[(*n_in)++] = Range{pa->conv_b, (size_t)d_inner * 4, "conv_bias"};
+  in[(*n_in)++] = Range{pa->hist, hb, "conv_state_in"};
+  in[(*n_in)++] = Range{pro->dt_softplus ? pro->dt_bias : nullptr, (size_t)d_inner * 4, "dt_bias"};
+  out[(*n_out)++] = Range{pa->hist_out, hb, "conv_state_out"};
+  return JSCAN_OK;
+}
+
+jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                          const void* x, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* h0, void* y, float* hT,
+                          const jscan_prologue* pro, void* workspace, size_t workspace_bytes, void* stream) {
+  t_last_error.clear();
+  jscan_status s = check_common(d_state, io);
+  if (s != JSCAN_OK) return s;
+  if (!sizes_ok(batch, L, d_inner)) return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
+  const bool work = batch > 0 && L > 0 && d_inner > 0;
+  if (work && (!x || !delta || !A || !B || !C || !D || !z || !y))
+    return fail(JSCAN_ERR_NULL, "x, delta, A, B, C, D, z and y are required");
+  const void* ptrs[] = {x, delta, A, B, C, D, z, h0, y, hT, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
+  const size_t tok = (size_t)batch * (size_t)L * (size_t)d_inner * es;
+  const size_t rowb = (size_t)batch * (size_t)L * NSTATE * es;
+  const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
+  Plan plan = choose_plan(batch, L, d_inner);
+  const size_t need = ws_layout(batch, L, d_inner, plan).total;
+  Range in[12] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
+                  {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"}};
+  Range out[4] = {{y, tok, "y"}, {hT, stb, "hT"}, {workspace, workspace ? need : 0, "workspace"}};
+  int n_in = 8, n_out = 3;
+  ProArgs pa;
+  if ((s = check_prologue(pro, batch, d_inner, &pa, in, &n_in, out, &n_out)) != JSCAN_OK) return s;
+  // An output may be the very same buffer as one input: hT == h0, or an
+  // in-place conv history.
+  for (int i = 0; i < n_out; ++i)
+    for (int j = 0; j < n_in; ++j) {
+      const bool same = out[i].p && out[i].p == in[j].p && out[i].bytes == in[j].bytes &&
+                        ((out[i].p == (const void*)hT && in[j].p == (const void*)h0) ||
+                         (out[i].p == (const void*)pa.hist_out && in[j].p == (const void*)pa.hist));
+      if (!same && overlap(out[i], in[j]))
+        return fail(JSCAN_ERR_ALIAS, std::string(out[i].name) + " overlaps " + in[j].name);
+    }
+  for (int i = 0; i < n_out; ++i)
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(out[i], out[j]))
+        return fail(JSCAN_ERR_ALIAS, std::string(out[i].name) + " overlaps " + out[j].name);
+  if (workspace && workspace_bytes < need)
+    return fail(JSCAN_ERR_WORKSPACE, "workspace smaller than jscan_prefill_workspace_size()");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!work) {
+    // Nothing to scan.  With L == 0 the final state and conv history are the initial ones.
+    if (L == 0 && batch > 0 && d_inner > 0) {
+      if (hT && hT != h0) {
+        const int64_t n = batch * d_inner * NSTATE;
+        hipLaunchKernelGGL(k_copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, h0, hT, n);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "state copy launch");
+      }
+      if (pa.hist_out && pa.hist_out != pa.hist && pa.width > 1) {
+        const int64_t n = batch * (pa.width - 1) * d_inner;
+        hipLaunchKernelGGL(k_copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pa.hist,
+                           pa.hist_out, n);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "history copy launch");
+      }
+    }
+    t_ev_before = t_ev_after = nullptr;
+    return JSCAN_OK;
+  }
+  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus;
+  if (conv || sp) plan.K = 1;                              // the prologue runs with one wave per group
+  char* ws = static_cast<char*>(workspace);
+  bool owned = false;
+  if (!ws && need > 0) {
+    if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess)
+      return hip_fail(e, "hipMallocAsync(workspace)");
+    owned = true;
+  }
+  s = with_prologue(conv, sp, [&](auto cv, auto spv) {
+    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value;
+    return io == JSCAN_IO_BF16
+               ? run_prefill<uint16_t, CV, SPV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws, plan,
+                                                pa, st)
+               : run_prefill<float, CV, SPV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws, plan, pa,
+                                             st);
+  });
+  if (owned) {
+    e = hipFreeAsync(ws, st);
+    if (s == JSCAN_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
+  }
+  return s;
+}
+
+jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io, float* state,
+                       const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, void* y, const jscan_prologue* pro, void* stream) {
+  t_last_error.clear();
+  jscan_status s = check_common(d_state, io);
+  if (s != JSCAN_OK) return s;
+  int64_t t;
+  if (n_seq < 0 || d_inner < 0 || !mul_ok(n_seq, d_inner, &t) || !mul_ok(t, NSTATE * 16, &t) ||
+      t / (NSTATE * 16) > ((int64_t)1 << 37))
+    return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
+  if (n_seq == 0 || d_inner == 0) {                       // nothing to do; the prologue is still checked
+    Range in[5], out[1];
+    int n_in = 0, n_out = 0;
+    ProArgs pa;
+    return check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out);
+  }
+  if (!state || !x || !delta || !A || !B || !C || !D || !z || !y)
+    return fail(JSCAN_ERR_NULL, "every pointer is required");
+  const void* ptrs[] = {state, x, delta, A, B, C, D, z, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
+  const size_t tok = (size_t)n_seq * (size_t)d_inner * es;
+  const size_t rowb = (size_t)n_seq * NSTATE * es;
+  const size_t stb = (size_t)n_seq * (size_t)d_inner * NSTATE * 4;
+  Range in[11] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
+                  {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}};
+  Range out[3] = {{y, tok, "y"}, {state, stb, "state"}};
+  int n_in = 7, n_out = 2;
+  ProArgs pa;
+  if ((s = check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out)) != JSCAN_OK) return s;
+  if ((s = check_ranges(in, n_in, out, n_out, pa.hist_out && pa.hist_out == pa.hist ? pa.hist : nullptr)) !=
+      JSCAN_OK)
+    return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus;
+  return with_prologue(conv, sp, [&](auto cv, auto spv) {
+    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value;
+    return io == JSCAN_IO_BF16
+               ? run_step<uint16_t, CV, SPV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st)
+               : run_step<float, CV, SPV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st);
+  });
 }
 
 }  // namespace
@@ -770,93 +1086,37 @@ jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
                            const void* C, const float* D, const void* z, const float* h0,
                            void* y, float* hT, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  t_last_error.clear();
-  jscan_status s = check_common(d_state, io);
-  if (s != JSCAN_OK) return s;
-  if (!sizes_ok(batch, L, d_inner)) return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
-  const bool work = batch > 0 && L > 0 && d_inner > 0;
-  if (work && (!x || !delta || !A || !B || !C || !D || !z || !y))
-    return fail(JSCAN_ERR_NULL, "x, delta, A, B, C, D, z and y are required");
-  const void* ptrs[] = {x, delta, A, B, C, D, z, h0, y, hT, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
-  const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
-  const size_t tok = (size_t)batch * (size_t)L * (size_t)d_inner * es;
-  const size_t rowb = (size_t)batch * (size_t)L * NSTATE * es;
-  const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
-  const Plan plan = choose_plan(batch, L, d_inner);
-  const size_t need = ws_layout(batch, L, d_inner, plan).total;
-  const Range in[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
-                      {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"},
-                      {h0, stb, "h0"}};
-  const Range out[] = {{y, tok, "y"}, {hT, stb, "hT"}, {workspace, workspace ? need : 0, "workspace"}};
-  if ((s = check_ranges(in, 8, out, 3, hT == h0 ? h0 : nullptr)) != JSCAN_OK) return s;
-  if (workspace && workspace_bytes < need)
-    return fail(JSCAN_ERR_WORKSPACE, "workspace smaller than jscan_prefill_workspace_size()");
+  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, nullptr, workspace,
+                      workspace_bytes, stream);
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (!work) {
-    // Nothing to scan.  With L == 0 the final state is the initial state.
-    if (hT && hT != h0 && L == 0 && batch > 0 && d_inner > 0) {
-      const int64_t n = batch * d_inner * NSTATE;
-      hipLaunchKernelGGL(k_copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, h0, hT, n);
-      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "state copy launch");
-    }
-    t_ev_before = t_ev_after = nullptr;
-    return JSCAN_OK;
-  }
-  char* ws = static_cast<char*>(workspace);
-  bool owned = false;
-  if (!ws && need > 0) {
-    if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess)
-      return hip_fail(e, "hipMallocAsync(workspace)");
-    owned = true;
-  }
-  s = io == JSCAN_IO_BF16
-          ? run_prefill<uint16_t>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws, plan, st)
-          : run_prefill<float>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws, plan, st);
-  if (owned) {
-    e = hipFreeAsync(ws, st);
-    if (s == JSCAN_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
-  }
-  return s;
+jscan_status jscan_prefill_fused(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                 const void* x, const void* delta, const float* A, const void* B,
+                                 const void* C, const float* D, const void* z, const float* h0,
+                                 void* y, float* hT, const jscan_prologue* prologue, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, prologue, workspace,
+                      workspace_bytes, stream);
 }
 
 jscan_status jscan_step_batch(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
                               float* state, const void* x, const void* delta, const float* A,
                               const void* B, const void* C, const float* D, const void* z,
                               void* y, void* stream) {
-  t_last_error.clear();
-  jscan_status s = check_common(d_state, io);
-  if (s != JSCAN_OK) return s;
-  int64_t t;
-  if (n_seq < 0 || d_inner < 0 || !mul_ok(n_seq, d_inner, &t) || !mul_ok(t, NSTATE * 16, &t) ||
-      t / (NSTATE * 16) > ((int64_t)1 << 37))
-    return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
-  if (n_seq == 0 || d_inner == 0) return JSCAN_OK;
-  if (!state || !x || !delta || !A || !B || !C || !D || !z || !y)
-    return fail(JSCAN_ERR_NULL, "every pointer is required");
-  const void* ptrs[] = {state, x, delta, A, B, C, D, z, y};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
-  const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
-  const size_t tok = (size_t)n_seq * (size_t)d_inner * es;
-  const size_t rowb = (size_t)n_seq * NSTATE * es;
-  const size_t stb = (size_t)n_seq * (size_t)d_inner * NSTATE * 4;
-  const Range in[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
-                      {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}};
-  const Range out[] = {{y, tok, "y"}, {state, stb, "state"}};
-  if ((s = check_ranges(in, 7, out, 2)) != JSCAN_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return io == JSCAN_IO_BF16 ? run_step<uint16_t>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, st)
-                             : run_step<float>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, st);
+  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, nullptr, stream);
+}
+
+jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
+                                    float* state, const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    void* y, const jscan_prologue* prologue, void* stream) {
+  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, prologue, stream);
 }
 
 jscan_status jscan_step(int64_t d_inner, int64_t d_state, jscan_io io, float* state, const void* x,
                         const void* delta, const float* A, const void* B, const void* C, const float* D,
                         const void* z, void* y, void* stream) {
-  return jscan_step_batch(1, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, stream);
+  return step_impl(1, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, nullptr, stream);
 }
 
 }  // extern "C"

@@ -19,6 +19,14 @@ Recipe (Jamba-shaped inputs: hidden 4096, d_inner 8192, d_state 16):
   - A[d, n] = -exp(U(log 1, log 16)), fp32
   - D[d] ~ N(0, 1), fp32
   - h0 ~ N(0, 1) fp32 when requested, else absent (zero state)
+* Input-prologue parameters (causal depthwise conv of width W, time-step
+  bias) come from ``PCG64([seed, PROLOGUE_STREAM])`` in the order
+  conv_weight [d_inner, W] ~ N(0, 1) / sqrt(W), conv_bias [d_inner] ~
+  N(0, 1) / 4, conv_state [batch, W-1, d_inner] ~ N(0, 1), dt_bias
+  [d_inner] = log(expm1(dt0)) with log dt0 ~ U(log 1e-3, log 1e-1), all fp32.
+  Raw (pre-softplus) time steps for tokens [0, L) come from
+  ``PCG64([seed, PROLOGUE_STREAM, 1])`` as N(0, 1) [batch, L, d_inner] in the
+  I/O dtype.
 * Decode inputs for step k of a run seeded ``seed`` come from
   ``PCG64([seed, DECODE_STREAM, k])`` in the order x, delta, z ([n_seq,
   d_inner]), B, C ([n_seq, d_state]); the initial decode state (~N(0, 1)) from
@@ -40,6 +48,7 @@ CHUNK = 4096
 PARAM_STREAM = 1_000_003
 DECODE_STREAM = 2_000_003
 STATE_STREAM = 3_000_017
+PROLOGUE_STREAM = 4_000_037
 
 IO_BF16 = "bf16"
 IO_F32 = "f32"
@@ -157,6 +166,24 @@ def prefill_inputs(batch, L, d_inner, d_state=16, seed=0, io=IO_BF16, h0=False,
     A, D, h = params(d_inner, d_state, seed, h0=h0, batch=batch)
     out["A"], out["D"], out["h0"] = A, D, h
     return out
+
+
+def prologue_params(d_inner, width, seed=0, batch=1):
+    """conv_weight [d_inner, width], conv_bias [d_inner], conv_state
+    [batch, width-1, d_inner] and dt_bias [d_inner], all fp32."""
+    g = np.random.Generator(np.random.PCG64([seed, PROLOGUE_STREAM]))
+    w = (g.standard_normal(size=(d_inner, width)) / np.sqrt(width)).astype(np.float32)
+    b = (g.standard_normal(size=(d_inner,)) / 4.0).astype(np.float32)
+    st = g.standard_normal(size=(batch, width - 1, d_inner)).astype(np.float32)
+    dt0 = np.exp(g.uniform(np.log(1e-3), np.log(1e-1), size=(d_inner,)))
+    dtb = np.log(np.expm1(dt0)).astype(np.float32)
+    return {"conv_weight": w, "conv_bias": b, "conv_state": st, "dt_bias": dtb}
+
+
+def raw_time_steps(batch, L, d_inner, seed=0, io=IO_BF16):
+    """Pre-softplus time steps ~ N(0, 1), [batch, L, d_inner] in the I/O dtype."""
+    g = np.random.Generator(np.random.PCG64([seed, PROLOGUE_STREAM, 1]))
+    return _round(g.standard_normal(size=(batch, L, d_inner)), io)
 
 
 def decode_state(n_seq, d_inner, d_state=16, seed=3):

@@ -203,3 +203,72 @@ def test_binding_fails_loudly_without_library(tmp_path):
             js.load_library(str(tmp_path / "missing.so"))
     finally:
         js._lib = saved
+
+
+# ------------------------------------------------------------ fused prologue
+def prologue(**over):
+    p = dict(conv_weight=fake(11), conv_bias=fake(12), conv_state_in=fake(13), conv_state_out=fake(14),
+             dt_bias=fake(15), conv_width=4, dt_softplus=1)
+    p.update(over)
+    s = js.Prologue()
+    for k, v in p.items():
+        setattr(s, k, v.value if isinstance(v, ctypes.c_void_p) else v)
+    return s
+
+
+def call_prefill_fused(lib, a, pro):
+    return lib.jscan_prefill_fused(a["batch"], a["L"], a["d_inner"], a["d_state"], a["io"], a["x"], a["delta"],
+                                   a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["y"], a["hT"],
+                                   ctypes.byref(pro) if pro is not None else None, a["workspace"], a["ws_bytes"],
+                                   a["stream"])
+
+
+def test_prefill_fused_validation(lib):
+    a = prefill_args()
+    for w in (0, 5, -1):
+        assert call_prefill_fused(lib, a, prologue(conv_width=w)) == UNSUP
+    # conv bias or history without weights
+    assert call_prefill_fused(lib, a, prologue(conv_weight=None)) == NULL
+    # misaligned prologue arrays
+    for name in ("conv_weight", "conv_bias", "conv_state_in", "conv_state_out", "dt_bias"):
+        bad = ctypes.c_void_p(getattr(prologue(), name) + 4)
+        assert call_prefill_fused(lib, a, prologue(**{name: bad})) == ALIGN
+    # conv_state_out on top of an input, or of y
+    assert call_prefill_fused(lib, a, prologue(conv_state_out=fake(0))) == ALIAS
+    assert call_prefill_fused(lib, a, prologue(conv_state_out=fake(8, 256))) == ALIAS
+    # conv_state_out partly over conv_state_in (history is 1 x 3 x 128 fp32 = 1536 B)
+    assert call_prefill_fused(lib, a, prologue(conv_state_out=fake(13, 512))) == ALIAS
+    # y over the conv weights
+    assert call_prefill_fused(lib, prefill_args(y=fake(11)), prologue()) == ALIAS
+    # the nothing-to-do case still validates the prologue
+    assert call_prefill_fused(lib, prefill_args(batch=0), prologue(conv_width=9)) == UNSUP
+
+
+def test_prefill_fused_in_place_history_is_allowed(lib):
+    # conv_state_out == conv_state_in passes the alias check; the call then
+    # stops at the (deliberately short) workspace, before any launch.
+    L, d = 65536, 8192
+    ws = js.workspace_size(1, L, d)
+    a = prefill_args(L=L, d_inner=d, workspace=fake(10), ws_bytes=ws - 1)
+    assert call_prefill_fused(lib, a, prologue(conv_state_out=fake(13))) == WS
+    assert call_prefill_fused(lib, a, prologue()) == WS
+    assert call_prefill_fused(lib, a, None) == WS
+
+
+def test_step_fused_validation(lib):
+    a = step_args()
+
+    def call(pro):
+        return lib.jscan_step_batch_fused(a["n_seq"], a["d_inner"], a["d_state"], a["io"], a["state"], a["x"],
+                                          a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["y"],
+                                          ctypes.byref(pro), a["stream"])
+    assert call(prologue(conv_width=7)) == UNSUP
+    assert call(prologue(conv_weight=None)) == NULL
+    assert call(prologue(dt_bias=ctypes.c_void_p(fake(15).value + 8))) == ALIGN
+    # history over the state (2 x 64 x 16 fp32 = 8 KiB)
+    assert call(prologue(conv_state_out=fake(0, 1024), conv_state_in=fake(13))) == ALIAS
+    # y over the conv weights
+    assert lib.jscan_step_batch_fused(2, 64, 16, BF16, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+                                      fake(6), fake(7), fake(11), ctypes.byref(prologue()), None) == ALIAS
+    assert lib.jscan_step_batch_fused(0, 64, 16, BF16, None, None, None, None, None, None, None, None, None,
+                                      ctypes.byref(prologue(conv_width=9)), None) == UNSUP

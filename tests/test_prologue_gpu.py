@@ -1,0 +1,277 @@
+"""GPU parity of the fused input prologue (causal depthwise conv + SiLU on x,
+softplus(delta + dt_bias)) against the fp64 oracle: ``oracle.prologue``
+followed by ``oracle.prefill`` / ``oracle.step``.
+
+Inputs are seeded synthetic data from ``synth`` (token tensors of the scan's
+recipe, prologue parameters from ``synth.prologue_params``, raw time steps
+from ``synth.raw_time_steps``).  The conv history the library writes back is
+a copy of raw x values, so it is compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import selective_state_space_11_amd as js
+from gpu_util import assert_state, assert_y, dev_f32, dev_io, host64, oracle_inputs, to_device
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only machines, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def print_case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def problem(batch, L, d_inner, width, seed, io, h0=True, raw_dt=True):
+    inp = synth.prefill_inputs(batch, L, d_inner, seed=seed, io=io, h0=h0)
+    if raw_dt:
+        inp["delta"] = synth.raw_time_steps(batch, L, d_inner, seed=seed, io=io)
+    pro = synth.prologue_params(d_inner, max(width, 1), seed=seed, batch=batch)
+    return inp, pro
+
+
+def oracle_fused(inp, pro, width, softplus, conv_state=True, use_h0=True):
+    """Reference: prologue, then the scan, all in fp64."""
+    o = oracle_inputs(inp)
+    w = pro["conv_weight"] if width > 0 else None
+    xc, dt, st = oracle.prologue(o["x"], o["delta"], w, pro["conv_bias"] if width > 0 else None,
+                                 pro["conv_state"] if (width > 0 and conv_state) else None,
+                                 pro["dt_bias"] if softplus else None, softplus)
+    y, hT = oracle.prefill(xc, dt, o["A"], o["B"], o["C"], o["D"], o["z"], o["h0"] if use_h0 else None)
+    return y, hT, st
+
+
+def gpu_fused(t, pro, width, softplus, conv_state=True, use_h0=True, in_place=False, **kw):
+    """Runs prefill_fused; returns (y, hT, conv_state_out)."""
+    batch, L, d_inner = t["x"].shape
+    cw = dev_f32(pro["conv_weight"]) if width > 0 else None
+    cb = dev_f32(pro["conv_bias"]) if width > 0 else None
+    cs_in = dev_f32(pro["conv_state"]) if (width > 0 and conv_state) else None
+    if width > 0:
+        cs_out = cs_in if (in_place and cs_in is not None) else torch.full(
+            (batch, width - 1, d_inner), float("nan"), device="cuda")
+    else:
+        cs_out = None
+    y, hT = js.prefill_fused(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                             t["h0"] if use_h0 else None, conv_weight=cw, conv_bias=cb, conv_state_in=cs_in,
+                             conv_state_out=cs_out, dt_bias=dev_f32(pro["dt_bias"]) if softplus else None,
+                             softplus=softplus, **kw)
+    torch.cuda.synchronize()
+    return y, hT, cs_out
+
+
+def with_plan(K, chunks, fn):
+    try:
+        js.set_plan_override(K, chunks)
+        return fn()
+    finally:
+        js.set_plan_override(0, 0)
+
+
+# ------------------------------------------------------------ small, every output
+@pytest.mark.parametrize("width", [4, 3, 2, 1])
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("chunks", [1, 5])
+def test_prefill_fused_ragged_bf16(width, softplus, chunks):
+    """Two sequences, L 777 (partial last token block), d_inner 200 (partial
+    channel group), h0 and a conv history given; single-pass and chunked plans."""
+    print_case(f"fused ragged bf16 width={width} softplus={softplus} chunks={chunks}")
+    # without softplus the time steps must already be positive: the scan's own recipe
+    inp, pro = problem(2, 777, 200, width, seed=11, io=synth.IO_BF16, raw_dt=softplus)
+    t = to_device(inp)
+    yr, hr, sr = oracle_fused(inp, pro, width, softplus)
+    y, hT, so = with_plan(1, chunks, lambda: gpu_fused(t, pro, width, softplus))
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+    assert np.array_equal(host64(so), sr), "conv_state_out"
+
+
+@pytest.mark.parametrize("chunks", [1, 3])
+def test_prefill_fused_f32_no_history(chunks):
+    """fp32 I/O, no conv history (zeros) and no h0."""
+    print_case(f"fused f32 no history chunks={chunks}")
+    inp, pro = problem(1, 333, 64, 4, seed=12, io=synth.IO_F32, h0=False)
+    t = to_device(inp)
+    yr, hr, sr = oracle_fused(inp, pro, 4, True, conv_state=False, use_h0=False)
+    y, hT, so = with_plan(1, chunks, lambda: gpu_fused(t, pro, 4, True, conv_state=False, use_h0=False))
+    assert_y(y, yr, bf16=False)
+    assert_state(hT, hr, "hT")
+    assert np.array_equal(host64(so), sr)
+
+
+@pytest.mark.parametrize("chunks", [1, 4])
+def test_prefill_fused_in_place_conv_state(chunks):
+    """conv_state_out is the conv_state_in buffer (the usual carry)."""
+    print_case(f"fused in-place conv state chunks={chunks}")
+    inp, pro = problem(2, 400, 128, 4, seed=13, io=synth.IO_BF16)
+    t = to_device(inp)
+    yr, hr, sr = oracle_fused(inp, pro, 4, True)
+    y, hT, so = with_plan(1, chunks, lambda: gpu_fused(t, pro, 4, True, in_place=True))
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+    assert np.array_equal(host64(so), sr)
+
+
+def test_prefill_fused_override_of_waves_is_ignored():
+    """A plan override with several waves per group still runs the fused path
+    with one (and gives the same result as the automatic plan's K)."""
+    print_case("fused with K=4 override")
+    inp, pro = problem(1, 300, 96, 4, seed=14, io=synth.IO_BF16)
+    t = to_device(inp)
+    yr, hr, sr = oracle_fused(inp, pro, 4, True)
+    y, hT, so = with_plan(4, 3, lambda: gpu_fused(t, pro, 4, True))
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+    assert np.array_equal(host64(so), sr)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 9])
+def test_prefill_fused_short_sequences(L):
+    """Sequences shorter than the conv window: the history written back mixes
+    the given history and the new tokens."""
+    print_case(f"fused short L={L}")
+    inp, pro = problem(2, L, 80, 4, seed=15, io=synth.IO_BF16)
+    t = to_device(inp)
+    yr, hr, sr = oracle_fused(inp, pro, 4, True)
+    y, hT, so = gpu_fused(t, pro, 4, True)
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+    assert np.array_equal(host64(so), sr)
+    # in place as well
+    y2, hT2, so2 = gpu_fused(t, pro, 4, True, in_place=True)
+    assert torch.equal(y2, y) and torch.equal(hT2, hT) and torch.equal(so2, so)
+
+
+def test_prefill_fused_empty_sequence_copies_history():
+    """L = 0: hT = h0 and the conv history passes through unchanged."""
+    print_case("fused L=0")
+    inp, pro = problem(2, 0, 64, 4, seed=16, io=synth.IO_BF16)
+    t = to_device(inp)
+    y, hT, so = gpu_fused(t, pro, 4, True)
+    assert y.numel() == 0
+    assert np.array_equal(host64(hT), inp["h0"].astype(np.float64))
+    assert np.array_equal(host64(so), pro["conv_state"].astype(np.float64))
+
+
+def test_prefill_fused_without_prologue_is_plain_prefill():
+    """An empty prologue (no conv, no softplus) is the plain scan, bit for bit."""
+    print_case("fused with empty prologue")
+    inp = synth.prefill_inputs(1, 500, 128, seed=17, io=synth.IO_BF16, h0=True)
+    t = to_device(inp)
+    y0, h0 = js.prefill(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"])
+    y1, h1 = js.prefill_fused(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(h0, h1)
+
+
+@pytest.mark.parametrize("split", [256, 501])
+def test_prefill_fused_chained_calls_carry_both_states(split):
+    """A sequence cut in two calls, each carrying hT and the conv history into
+    the next, gives the single call's result."""
+    print_case(f"fused chained split={split}")
+    L = 777
+    inp, pro = problem(1, L, 136, 4, seed=18, io=synth.IO_BF16)
+    yr, hr, sr = oracle_fused(inp, pro, 4, True)
+    t = to_device(inp)
+    parts = []
+    h = t["h0"].clone()
+    cs = dev_f32(pro["conv_state"])
+    for lo, hi in ((0, split), (split, L)):
+        sub = {k: (v[:, lo:hi].contiguous() if k in ("x", "delta", "z", "B", "C") else v) for k, v in t.items()}
+        y, _ = js.prefill_fused(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], h,
+                                hT=h, conv_weight=dev_f32(pro["conv_weight"]), conv_bias=dev_f32(pro["conv_bias"]),
+                                conv_state_in=cs, conv_state_out=cs, dt_bias=dev_f32(pro["dt_bias"]),
+                                softplus=True)
+        parts.append(y)
+    torch.cuda.synchronize()
+    assert_y(torch.cat(parts, dim=1), yr, bf16=True)
+    assert_state(h, hr, "hT")
+    assert np.array_equal(host64(cs), sr)
+
+
+# ------------------------------------------------------------------ decode step
+def test_step_fused_matches_oracle_steps():
+    """Eight chained fused decode steps for three sequences against the oracle's
+    prologue + step, conv history and state carried in place."""
+    print_case("fused decode steps")
+    n_seq, d, width = 3, 200, 4
+    pro = synth.prologue_params(d, width, seed=19, batch=n_seq)
+    A, D, _ = synth.params(d, seed=19)
+    st64 = synth.decode_state(n_seq, d, seed=19).astype(np.float64)
+    cs64 = pro["conv_state"].astype(np.float64)
+    state = dev_f32(synth.decode_state(n_seq, d, seed=19))
+    cs = dev_f32(pro["conv_state"])
+    tA, tD = dev_f32(A), dev_f32(D)
+    for k in range(8):
+        s = synth.decode_inputs(n_seq, d, seed=19, step=k)
+        s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=100 + k)[:, 0, :]
+        xc, dt, cs64 = oracle.prologue(synth.widen(s["x"])[:, None, :], synth.widen(s["delta"])[:, None, :],
+                                       pro["conv_weight"], pro["conv_bias"], cs64, pro["dt_bias"], True)
+        yr, st64 = oracle.step(st64, xc[:, 0, :], dt[:, 0, :], A.astype(np.float64), synth.widen(s["B"]),
+                               synth.widen(s["C"]), D.astype(np.float64), synth.widen(s["z"]))
+        y = js.step_batch_fused(state, dev_io(s["x"]), dev_io(s["delta"]), tA, dev_io(s["B"]), dev_io(s["C"]), tD,
+                                dev_io(s["z"]), conv_weight=dev_f32(pro["conv_weight"]),
+                                conv_bias=dev_f32(pro["conv_bias"]), conv_state=cs,
+                                dt_bias=dev_f32(pro["dt_bias"]), softplus=True)
+        torch.cuda.synchronize()
+        assert_y(y, yr, bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+        assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
+
+
+@pytest.mark.parametrize("width", [4, 2, 1])
+def test_fused_steps_continue_a_fused_prefill(width):
+    """Prefill of 300 tokens then 5 fused steps equals one fused prefill of 305
+    tokens (decode continues where the prompt's two states left off)."""
+    print_case(f"fused prefill + steps width={width}")
+    L0, T, d = 300, 5, 128
+    inp, pro = problem(1, L0 + T, d, width, seed=20, io=synth.IO_BF16)
+    t = to_device(inp)
+    y_all, h_all, cs_all = gpu_fused(t, pro, width, True)
+    head = {k: (v[:, :L0].contiguous() if k in ("x", "delta", "z", "B", "C") else v) for k, v in t.items()}
+    y_head, state, cs = gpu_fused(head, pro, width, True)
+    cw, cb, dtb = dev_f32(pro["conv_weight"]), dev_f32(pro["conv_bias"]), dev_f32(pro["dt_bias"])
+    ys = []
+    for k in range(L0, L0 + T):
+        ys.append(js.step_batch_fused(state, t["x"][:, k].contiguous(), t["delta"][:, k].contiguous(), t["A"],
+                                      t["B"][:, k].contiguous(), t["C"][:, k].contiguous(), t["D"],
+                                      t["z"][:, k].contiguous(), conv_weight=cw, conv_bias=cb,
+                                      conv_state=cs, dt_bias=dtb, softplus=True))
+    torch.cuda.synchronize()
+    y_steps = torch.stack(ys, dim=1)
+    yr, hr, sr = oracle_fused(inp, pro, width, True)
+    assert_y(y_steps, yr[:, L0:], bf16=True, what="decoded y")
+    assert_y(y_head, yr[:, :L0], bf16=True, what="prompt y")
+    assert_state(state, hr, "state after decode")
+    assert_state(h_all, hr, "hT of the full prefill")
+    if width > 1:
+        assert torch.equal(cs, cs_all)
+        assert np.array_equal(host64(cs), sr)
+
+
+# ------------------------------------------------------------ full size, sampled
+def test_fused_prefill_64k_sampled():
+    """The 64K-token prefill (batch 1, d_inner 8192, bf16) with the full
+    prologue, in the automatic plan; 24 channels (three whole channel groups'
+    edges and a random spread) compared against the oracle over all 65536
+    tokens; every output finite."""
+    L, d, width = 65536, 8192, 4
+    print_case(f"fused 64K sampled L={L} d={d}")
+    inp = synth.prefill_inputs(1, L, d, seed=21, io=synth.IO_BF16, h0=True)
+    pro = synth.prologue_params(d, width, seed=21)
+    t = to_device(inp)
+    y, hT, so = gpu_fused(t, pro, width, True)
+    assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+    rng = np.random.default_rng(21)
+    ch = np.unique(np.concatenate([[0, 63, 64, 4095, 4096, 8191], rng.choice(d, 18, replace=False)]))
+    sub = synth.channel_slice(inp, ch)
+    xc, dt, st = oracle.prologue(sub["x"], sub["delta"], pro["conv_weight"][ch], pro["conv_bias"][ch],
+                                 pro["conv_state"][:, :, ch], pro["dt_bias"][ch], True)
+    yr, hr = oracle.prefill(xc, dt, sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["h0"])
+    assert_y(y[:, :, ch], yr, bf16=True)
+    assert_state(hT[:, ch], hr, "hT")
+    assert np.array_equal(host64(so)[:, :, ch], st)
