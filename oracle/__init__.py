@@ -9,6 +9,8 @@ Two implementations of the same definition live here:
 * ``jscan_oracle.c`` (loaded through ctypes): the sequential fp64 loop, threaded
   over independent (batch, channel) pairs.  ``prefill`` and ``step`` are written
   separately in C.
+* ``backward`` (C, ``oracle_backward``): the gradient of the prefill by the
+  adjoint recurrence, every forward state kept, for training.
 * ``twin.py``: the same loop in numpy, vectorised over channels only, for
   small shapes and as a cross-check of the C code.
 
@@ -59,6 +61,8 @@ def _load():
             lib.oracle_step.restype = None
             lib.oracle_prologue.argtypes = [i64, i64, i64, i64] + [dp] * 6 + [dp, dp, ctypes.c_int, dp]
             lib.oracle_prologue.restype = None
+            lib.oracle_backward.argtypes = [i64, i64, i64, i64] + [dp] * 18
+            lib.oracle_backward.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -164,3 +168,39 @@ def prologue(x, delta, conv_weight=None, conv_bias=None, conv_state=None, dt_bia
     _load().oracle_prologue(batch, L, d_inner, width, _ptr(x), _ptr(w), _ptr(bias), _ptr(st), _ptr(xc),
                             _ptr(st_out), _ptr(delta), _ptr(dtb), 1 if softplus else 0, _ptr(dout))
     return xc, dout, st_out
+
+
+def backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None):
+    """Gradients of the prefill for output gradients dy [batch, L, d_inner] and
+    dhT [batch, d_inner, d_state] (None: zero), by the adjoint recurrence (see
+    jscan_oracle.c).  Returns a dict of float64 arrays dx, ddelta, dz
+    [batch, L, d_inner], dA [d_inner, d_state], dB, dC [batch, L, d_state],
+    dD [d_inner] and dh0 [batch, d_inner, d_state]."""
+    x = np.asarray(x)
+    batch, L, d_inner = x.shape
+    d_state = np.asarray(A).shape[1]
+    if d_state > 256:
+        raise ValueError("oracle supports d_state <= 256")
+    x = _f64(x, (batch, L, d_inner), "x")
+    delta = _f64(delta, (batch, L, d_inner), "delta")
+    z = _f64(z, (batch, L, d_inner), "z")
+    dy = _f64(dy, (batch, L, d_inner), "dy")
+    A = _f64(A, (d_inner, d_state), "A")
+    B = _f64(B, (batch, L, d_state), "B")
+    C = _f64(C, (batch, L, d_state), "C")
+    D = _f64(D, (d_inner,), "D")
+    h0 = None if h0 is None else _f64(h0, (batch, d_inner, d_state), "h0")
+    dhT = None if dhT is None else _f64(dhT, (batch, d_inner, d_state), "dhT")
+    out = {k: np.empty((batch, L, d_inner)) for k in ("dx", "ddelta", "dz")}
+    out["dA"] = np.empty((d_inner, d_state))
+    out["dB"] = np.empty((batch, L, d_state))
+    out["dC"] = np.empty((batch, L, d_state))
+    out["dD"] = np.empty((d_inner,))
+    out["dh0"] = np.empty((batch, d_inner, d_state))
+    rc = _load().oracle_backward(batch, L, d_inner, d_state, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dhT), _ptr(out["dx"]),
+                                 _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                                 _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]))
+    if rc:
+        raise MemoryError("oracle_backward: out of memory")
+    return out

@@ -198,3 +198,137 @@ void oracle_prologue(int64_t batch, int64_t L, int64_t d_inner, int64_t width,
     }
   }
 }
+
+/*
+ * Backward (gradient) of the prefill, for training (test infrastructure, same
+ * caveats as above).  The pages name training with sequence and tensor
+ * parallelism ("AI Engineering from Scratch" Jamba paper notes, section 3.3 on
+ * the training framework) but give no backward; this is the reverse-mode
+ * derivative of the recurrence defined at the top of this file, taken by hand
+ * (adjoint method), for a scalar loss whose gradients with respect to the
+ * outputs are dy [batch][L][d_inner] and dhT [batch][d_inner][d_state]
+ * (dhT NULL: zero).
+ *
+ * Per (b, d), with the forward states h_t (h_{-1} = h0), decays
+ * a_tn = exp(dt_t A_n), pre-gate output p_t = sum_n C_tn h_tn + D xv_t and
+ * gate g_t = SiLU(z_t):
+ *   lambda_t = dL/dh_t  (total, through all later tokens):
+ *     lambda_{L-1} = dp_{L-1} C_{L-1} + dhT,
+ *     lambda_t     = dp_t C_t + a_{t+1} * lambda_{t+1}   (per n)
+ *   where dp_t = dy_t g_t.  Then
+ *     dz_t     = dy_t p_t SiLU'(z_t),  SiLU'(z) = s (1 + z (1 - s)), s = 1/(1+exp(-z))
+ *     dx_t     = D dp_t + dt_t sum_n lambda_tn B_tn
+ *     ddelta_t = sum_n lambda_tn (A_n a_tn h_{t-1,n} + B_tn xv_t)
+ *     dA_n    += sum_t lambda_tn dt_t a_tn h_{t-1,n}        (over b and t)
+ *     dD      += sum_t dp_t xv_t                             (over b and t)
+ *     dB_tn   += lambda_tn dt_t xv_t                         (over d)
+ *     dC_tn   += dp_t h_tn                                   (over d)
+ *     dh0_n    = a_0n lambda_0n
+ * Every output is overwritten (dA, dD, dB, dC are sums built from zero).
+ * dh0 may be NULL.  Layouts as for oracle_prefill; dA [d_inner][d_state],
+ * dD [d_inner], dB, dC [batch][L][d_state].
+ *
+ * Channels run in parallel; each thread sums its channels' dB, dC, dA and dD
+ * contributions privately and the partial sums are added in thread order.
+ */
+#include <stdlib.h>
+#include <string.h>
+
+int oracle_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                    const double* x, const double* delta, const double* A,
+                    const double* B, const double* C, const double* Dv,
+                    const double* z, const double* h0, const double* dy,
+                    const double* dhT, double* dx, double* ddelta, double* dz,
+                    double* dA, double* dB, double* dC, double* dD, double* dh0) {
+  const int64_t N = d_state;
+  const int64_t rows = batch * L * N;
+  int nthreads = oracle_num_threads();
+  double* accBC = (double*)calloc((size_t)nthreads * (size_t)rows * 2, sizeof(double));
+  double* accAD = (double*)calloc((size_t)nthreads * (size_t)d_inner * (size_t)(N + 1), sizeof(double));
+  if (!accBC || !accAD) { free(accBC); free(accAD); return 1; }
+  int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+  {
+#ifdef _OPENMP
+    const int tid = omp_get_thread_num();
+#else
+    const int tid = 0;
+#endif
+    double* myB = accBC + (size_t)tid * (size_t)rows * 2;
+    double* myC = myB + rows;
+    double* myAD = accAD + (size_t)tid * (size_t)d_inner * (size_t)(N + 1);
+    double* hs = (double*)malloc((size_t)(L + 1) * (size_t)N * sizeof(double));
+    if (!hs) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t bd = 0; bd < batch * d_inner; ++bd) {
+      if (!hs) continue;
+      const int64_t b = bd / d_inner, d = bd % d_inner;
+      /* forward, keeping every state: hs[(t+1)*N + n] = h_t[n] */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * d_inner + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = (b * L + t) * d_inner + d;
+        const double* Bt = B + (b * L + t) * N;
+        for (int64_t n = 0; n < N; ++n)
+          hs[(t + 1) * N + n] = exp(delta[i] * A[d * N + n]) * hs[t * N + n] + delta[i] * Bt[n] * x[i];
+      }
+      /* reverse sweep; mu[n] is the adjoint arriving at h_t from later tokens */
+      double mu[256];
+      for (int64_t n = 0; n < N; ++n) mu[n] = dhT ? dhT[(b * d_inner + d) * N + n] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t i = (b * L + t) * d_inner + d;
+        const double* Bt = B + (b * L + t) * N;
+        const double* Ct = C + (b * L + t) * N;
+        const double* ht = hs + (t + 1) * N;
+        const double* hp = hs + t * N;
+        const double dt = delta[i], xv = x[i], zv = z[i];
+        const double s = 1.0 / (1.0 + exp(-zv));
+        double p = Dv[d] * xv;
+        for (int64_t n = 0; n < N; ++n) p += Ct[n] * ht[n];
+        dz[i] = dy[i] * p * s * (1.0 + zv * (1.0 - s));
+        const double dp = dy[i] * zv * s;
+        double sx = 0.0, sd = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double lam = dp * Ct[n] + mu[n];
+          const double a = exp(dt * A[d * N + n]);
+          myC[(b * L + t) * N + n] += dp * ht[n];
+          myB[(b * L + t) * N + n] += lam * dt * xv;
+          sx += lam * Bt[n];
+          sd += lam * (A[d * N + n] * a * hp[n] + Bt[n] * xv);
+          myAD[d * (N + 1) + n] += lam * dt * a * hp[n];
+          mu[n] = a * lam;
+        }
+        myAD[d * (N + 1) + N] += dp * xv;
+        dx[i] = Dv[d] * dp + dt * sx;
+        ddelta[i] = sd;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * d_inner + d) * N + n] = mu[n];
+    }
+    free(hs);
+  }
+  if (!failed) {
+    for (int64_t r = 0; r < rows; ++r) {
+      double sb = 0.0, sc = 0.0;
+      for (int k = 0; k < nthreads; ++k) {
+        sb += accBC[(size_t)k * (size_t)rows * 2 + (size_t)r];
+        sc += accBC[(size_t)k * (size_t)rows * 2 + (size_t)rows + (size_t)r];
+      }
+      dB[r] = sb;
+      dC[r] = sc;
+    }
+    for (int64_t d = 0; d < d_inner; ++d) {
+      for (int64_t n = 0; n <= N; ++n) {
+        double s = 0.0;
+        for (int k = 0; k < nthreads; ++k) s += accAD[((size_t)k * (size_t)d_inner + (size_t)d) * (size_t)(N + 1) + (size_t)n];
+        if (n < N) dA[d * N + n] = s;
+        else dD[d] = s;
+      }
+    }
+  }
+  free(accBC);
+  free(accAD);
+  return failed;
+}
