@@ -175,6 +175,47 @@ jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_st
                                     const void* B, const void* C, const float* D, const void* z,
                                     void* y, const jscan_prologue* prologue, void* stream);
 
+/*
+ * Backward (gradient) of jscan_prefill, for training.  The pages describe
+ * training Jamba (paper notes, section 3.3 on the training framework) but
+ * give no backward; this is the reverse-mode derivative of the recurrence
+ * above.  Given the forward's inputs and the gradients of a scalar loss with
+ * respect to its outputs,
+ *   dy  [batch][L][d_inner]           (I/O dtype)
+ *   dhT [batch][d_inner][d_state] fp32 (NULL: zero; hT was not used),
+ * it writes the gradients with respect to every input:
+ *   dx, ddelta, dz [batch][L][d_inner] (I/O dtype)
+ *   dA [d_inner][d_state] fp32, dD [d_inner] fp32 (summed over batch, tokens)
+ *   dB, dC [batch][L][d_state] fp32 (summed over channels)
+ *   dh0 [batch][d_inner][d_state] fp32 (NULL: not written; h0 NULL is a zero
+ *        initial state and dh0 is still its gradient)
+ * Every output is overwritten, never accumulated.  The forward states are
+ * recomputed from the inputs (nothing is saved by jscan_prefill).
+ *
+ * Gradients (per sequence b, channel d, state n, with a_t = exp(delta_t A),
+ * the forward states h_t, p_t = C_t . h_t + D x_t and dp_t = dy_t SiLU(z_t)):
+ * the adjoint lambda_t = dp_t C_t + a_{t+1} lambda_{t+1} (lambda_{L-1} gets
+ * + dhT) gives dx_t = D dp_t + delta_t (lambda_t . B_t), ddelta_t =
+ * sum_n lambda_tn (A_n a_tn h_{t-1,n} + B_tn x_t), dz_t = dy_t p_t SiLU'(z_t),
+ * dA_n = sum lambda_tn delta_t a_tn h_{t-1,n}, dD = sum dp_t x_t,
+ * dB_tn = sum_d lambda_tn delta_t x_t, dC_tn = sum_d dp_t h_tn,
+ * dh0 = a_0 lambda_0.
+ *
+ * workspace: NULL (allocated and freed stream-ordered) or at least
+ * jscan_backward_workspace_size() bytes; it holds recomputed states (about 8
+ * bytes per channel-token) and partial sums.  Errors as for jscan_prefill;
+ * no output may overlap an input or another output.  Results do not depend
+ * on scheduling (every sum is taken in a fixed order).
+ */
+size_t jscan_backward_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                                     jscan_io io);
+
+jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                            const void* x, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const float* h0, const void* dy, const float* dhT,
+                            void* dx, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
+                            float* dh0, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static name of a status code. */
 const char* jscan_status_string(jscan_status status);
 

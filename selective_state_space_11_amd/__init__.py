@@ -14,6 +14,8 @@ Entry points mirror the C ABI in ``include/jscan.h``:
 * ``prefill_fused`` / ``step_batch_fused``: the same with the layer's input
   prologue (causal depthwise conv + SiLU on x, softplus(delta + dt_bias))
   applied inside the scan kernels
+* ``backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None)`` -> dict of the
+  gradients dx, ddelta, dz, dA, dB, dC, dD, dh0
 * ``workspace_size``, ``plan``, ``set_plan_override``, ``time_next_prefill``
 """
 from __future__ import annotations
@@ -34,7 +36,7 @@ IO_F32, IO_BF16 = 0, 1
 EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_step", "jscan_step_batch",
            "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
            "jscan_set_plan_override", "jscan_time_next_prefill", "jscan_prefill_fused",
-           "jscan_step_batch_fused")
+           "jscan_step_batch_fused", "jscan_backward_workspace_size", "jscan_backward")
 
 
 class Prologue(ctypes.Structure):
@@ -97,6 +99,10 @@ def load_library(path: str = LIB_PATH):
         lib.jscan_prefill_fused.restype = st
         lib.jscan_step_batch_fused.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, pp, vp]
         lib.jscan_step_batch_fused.restype = st
+        lib.jscan_backward_workspace_size.argtypes = [i64, i64, i64, i64, st]
+        lib.jscan_backward_workspace_size.restype = sz
+        lib.jscan_backward.argtypes = [i64, i64, i64, i64, st] + [vp] * 18 + [vp, sz, vp]
+        lib.jscan_backward.restype = st
         _lib = lib
         return lib
 
@@ -332,3 +338,50 @@ def step_batch_fused(state, x, delta, A, B, C, D, z, *, conv_weight=None, conv_b
                                       _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), ctypes.byref(pro),
                                       _stream(stream)))
     return y
+
+
+def backward_workspace_size(batch, L, d_inner, d_state=D_STATE, io=IO_BF16) -> int:
+    return int(load_library().jscan_backward_workspace_size(batch, L, d_inner, d_state, io))
+
+
+def backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None, *, want_dh0=True, out=None, workspace=None,
+             stream=None):
+    """Gradients of prefill for output gradients dy (like y) and dhT ([batch, d_inner, 16]
+    fp32 or None).  Returns a dict: dx, ddelta, dz (like x), dA [d_inner, 16], dB, dC
+    [batch, L, 16], dD [d_inner] (fp32) and dh0 ([batch, d_inner, 16] fp32, or None when
+    want_dh0 is False).  ``out`` may supply any of these tensors."""
+    torch = _torch()
+    lib = load_library()
+    _dev(x, "x")
+    batch, L, d_inner = x.shape
+    io = _io_of(x)
+    for name, t in (("delta", delta), ("z", z), ("dy", dy)):
+        _dev(t, name, x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (batch, L, D_STATE))
+    _dev(C, "C", x.dtype, (batch, L, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, D_STATE))
+    _dev(dhT, "dhT", torch.float32, (batch, d_inner, D_STATE))
+    out = dict(out or {})
+    shapes = {"dx": (x.shape, x.dtype), "ddelta": (x.shape, x.dtype), "dz": (x.shape, x.dtype),
+              "dA": ((d_inner, D_STATE), torch.float32), "dB": ((batch, L, D_STATE), torch.float32),
+              "dC": ((batch, L, D_STATE), torch.float32), "dD": ((d_inner,), torch.float32),
+              "dh0": ((batch, d_inner, D_STATE), torch.float32)}
+    for name, (shape, dtype) in shapes.items():
+        if name == "dh0" and not want_dh0 and out.get(name) is None:
+            out[name] = None
+            continue
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=dtype, device=x.device)
+        _dev(out[name], name, dtype, shape)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.jscan_backward(batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                              _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dhT), _ptr(out["dx"]),
+                              _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                              _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(workspace), ws_bytes,
+                              _stream(stream)))
+    return out

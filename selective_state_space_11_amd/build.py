@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "jscan.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("jscan.hip", "jscan_bwd.hip")]
 LIB = os.path.join(PKG, "libjscan.so")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -27,7 +27,7 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l and "not a recognized feature" not in l)

@@ -1,0 +1,192 @@
+// Device helpers shared by the forward and backward scan kernels of libjscan
+// (gfx950): I/O widening and rounding, the fast transcendental forms, the
+// optional input prologue, scalar-loaded B/C rows and raw buffer accesses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace jscan_detail {
+
+constexpr int NSTATE = 16;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kTok = 8;         // tokens per software-pipelined block
+constexpr int kCUs = 256;       // MI355X compute units
+constexpr int64_t kMinChunk = 64;           // shortest chunk worth a carry
+
+// ---------------------------------------------------------------- I/O types
+__device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ void store_io(uint16_t* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, (__bf16)v);   // v_cvt_pk_bf16_f32: round to nearest even
+}
+__device__ __forceinline__ void store_io(float* p, float v) { *p = v; }
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// SiLU(z) = z / (1 + exp(-z)); v_exp_f32 and v_rcp_f32.  For z -> -inf the
+// denominator is +inf and the result is -0, as in the definition.
+__device__ __forceinline__ float silu(float zv) {
+  return zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
+}
+
+// softplus(v) = log(1 + exp(v)), through v_exp_f32 / v_log_f32 (base 2).  For
+// v > 15 it equals v to fp32 precision; for tiny exp(v) log(1 + e) ~ e - e^2/2.
+__device__ __forceinline__ float softplus(float v) {
+  const float e = fast_exp2(v * kLog2e);
+  const float r = e < 1.0e-3f ? e - 0.5f * e * e : __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
+  return v > 15.0f ? v : r;
+}
+
+// Optional input prologue of a Mamba layer, applied per token as x and delta
+// are loaded:
+//   x  -> SiLU(conv_b + sum_k w[k] * x[t - (width - 1) + k])   (causal depthwise conv)
+//   dt -> softplus(dt + dt_bias)
+// The convolution keeps the last three raw x of its channel in registers;
+// taps are right-aligned in a 4-tap window with the missing ones zero, which
+// adds exact zeros.
+struct ProArgs {
+  const float* conv_w;      // [d_inner][width], or null: no convolution
+  const float* conv_b;      // [d_inner], or null
+  const float* hist;        // [batch][width-1][d_inner] history before the sequence, or null (zeros)
+  float* hist_out;          // [batch][width-1][d_inner] history after it, or null
+  const float* dt_bias;     // [d_inner], or null
+  int width;
+};
+
+template <bool CONV, bool SP>
+struct Prologue {
+  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, cb = 0.f, dtb = 0.f;
+  float h1 = 0.f, h2 = 0.f, h3 = 0.f;       // raw x of tokens t-1, t-2, t-3
+  __device__ __forceinline__ void init(const ProArgs& p, int64_t d) {
+    if constexpr (CONV) {
+      // tap k of the caller's width-W filter goes to slot 4 - W + k
+      const float* wr = p.conv_w + d * p.width;
+      const int off = 4 - p.width;
+      w3 = wr[p.width - 1];
+      w2 = off <= 2 ? wr[2 - off] : 0.f;
+      w1 = off <= 1 ? wr[1 - off] : 0.f;
+      w0 = off <= 0 ? wr[0] : 0.f;
+      cb = p.conv_b ? p.conv_b[d] : 0.f;
+    }
+    if constexpr (SP) dtb = p.dt_bias ? p.dt_bias[d] : 0.f;
+  }
+  // Raw x before token t0 of sequence b: from x itself, or from the history
+  // given for the sequence start (hist, or zeros).
+  template <class T>
+  __device__ __forceinline__ float before(const ProArgs& p, const float* hist, const T* x, int64_t b, int64_t L,
+                                          int64_t d_inner, int64_t pos, int64_t d) const {
+    if (pos >= 0) return widen(x[(b * L + pos) * d_inner + d]);
+    const int64_t j = (p.width - 1) + pos;
+    return (hist && j >= 0) ? hist[(b * (p.width - 1) + j) * d_inner + d] : 0.f;
+  }
+  template <class T>
+  __device__ __forceinline__ void start(const ProArgs& p, const float* hist, const T* x, int64_t b, int64_t L,
+                                        int64_t d_inner, int64_t t0, int64_t d) {
+    if constexpr (CONV) {
+      h1 = before(p, hist, x, b, L, d_inner, t0 - 1, d);
+      h2 = before(p, hist, x, b, L, d_inner, t0 - 2, d);
+      h3 = before(p, hist, x, b, L, d_inner, t0 - 3, d);
+    }
+  }
+  __device__ __forceinline__ float xin(float xv) {
+    if constexpr (CONV) {
+      const float acc = fmaf(w3, xv, fmaf(w2, h1, fmaf(w1, h2, fmaf(w0, h3, cb))));
+      h3 = h2; h2 = h1; h1 = xv;
+      return silu(acc);
+    } else {
+      return xv;
+    }
+  }
+  __device__ __forceinline__ float dt(float dv) const {
+    if constexpr (SP) return softplus(dv + dtb);
+    else return dv;
+  }
+};
+
+// Load S consecutive floats from a wave-uniform address (scalar loads).
+template <int S>
+__device__ __forceinline__ void load_row(float (&v)[S], const float* __restrict__ p) {
+  if constexpr (S % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < S / 4; ++q) {
+      const float4 w = reinterpret_cast<const float4*>(p)[q];
+      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < S / 2; ++q) {
+      const float2 w = reinterpret_cast<const float2*>(p)[q];
+      v[2 * q] = w.x; v[2 * q + 1] = w.y;
+    }
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void copy_row(float (&dst)[S], const float (&src)[S]) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) dst[s] = src[s];
+}
+
+// S consecutive values of a B or C row, read with scalar loads from a
+// wave-uniform address and kept in SGPRs in the I/O format.  bf16 pairs stay
+// packed (S/2 dwords) and are widened when used (a scalar shift or mask).
+template <class T, int S> struct Row;
+template <int S> struct Row<uint16_t, S> {
+  static_assert(S % 2 == 0, "bf16 rows are read in pairs");
+  uint32_t w[S / 2];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ p) {
+    if constexpr (S % 8 == 0) {
+#pragma unroll
+      for (int q = 0; q < S / 8; ++q) {
+        const uint4 v = reinterpret_cast<const uint4*>(p)[q];
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < S / 2; ++q) w[q] = reinterpret_cast<const uint32_t*>(p)[q];
+    }
+  }
+  __device__ __forceinline__ float operator[](int s) const {
+    return (s & 1) ? __uint_as_float(w[s >> 1] & 0xffff0000u) : __uint_as_float(w[s >> 1] << 16);
+  }
+};
+template <int S> struct Row<float, S> {
+  float w[S];
+  __device__ __forceinline__ void load(const float* __restrict__ p) { load_row(w, p); }
+  __device__ __forceinline__ float operator[](int s) const { return w[s]; }
+};
+
+// Addressing: a wave covers 64 consecutive channels [gbase, gbase + 64).  Row
+// pointers (token t, channel gbase) are wave-uniform and live in SGPRs; a lane
+// adds its own 32-bit offset `lo`.  Lanes past d_inner are clamped onto
+// channel d_inner - 1 (they read valid memory and their results are dropped or
+// duplicate that channel's).
+
+// Streaming loads and stores are buffer instructions: a wave-uniform resource
+// (SGPRs, based at the first row of the current token block), the lane's
+// constant byte offset (VGPR) and the token's row offset (SGPR), so they cost
+// no VALU address arithmetic.  A resource with num_records = 0 makes every
+// load return 0 (out-of-range rule); it stands in for padding tokens' delta.
+constexpr int kBufDword3 = 0x00020000;      // gfx9 raw buffer: 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int records = -1) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, records, kBufDword3);
+}
+__device__ __forceinline__ void buf_load(uint16_t& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  v = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_load(float& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t to_io(float v, uint16_t) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ float to_io(float v, float) { return v; }
+
+}  // namespace jscan_detail

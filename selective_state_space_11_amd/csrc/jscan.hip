@@ -46,189 +46,12 @@
 
 #include "jscan.h"
 
-namespace {
+#include "common.h"
+#include "host.h"
 
-constexpr int NSTATE = 16;
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kTok = 8;         // tokens per software-pipelined block
-constexpr int kCUs = 256;       // MI355X compute units
-constexpr int64_t kMinChunk = 64;           // shortest chunk worth a carry
-
-// ---------------------------------------------------------------- I/O types
-__device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-__device__ __forceinline__ float widen(float v) { return v; }
-__device__ __forceinline__ void store_io(uint16_t* p, float v) {
-  *p = __builtin_bit_cast(uint16_t, (__bf16)v);   // v_cvt_pk_bf16_f32: round to nearest even
-}
-__device__ __forceinline__ void store_io(float* p, float v) { *p = v; }
-
-__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
-
-// SiLU(z) = z / (1 + exp(-z)); v_exp_f32 and v_rcp_f32.  For z -> -inf the
-// denominator is +inf and the result is -0, as in the definition.
-__device__ __forceinline__ float silu(float zv) {
-  return zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
-}
-
-// softplus(v) = log(1 + exp(v)), through v_exp_f32 / v_log_f32 (base 2).  For
-// v > 15 it equals v to fp32 precision; for tiny exp(v) log(1 + e) ~ e - e^2/2.
-__device__ __forceinline__ float softplus(float v) {
-  const float e = fast_exp2(v * kLog2e);
-  const float r = e < 1.0e-3f ? e - 0.5f * e * e : __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
-  return v > 15.0f ? v : r;
-}
-
-// Optional input prologue of a Mamba layer, applied per token as x and delta
-// are loaded:
-//   x  -> SiLU(conv_b + sum_k w[k] * x[t - (width - 1) + k])   (causal depthwise conv)
-//   dt -> softplus(dt + dt_bias)
-// The convolution keeps the last three raw x of its channel in registers;
-// taps are right-aligned in a 4-tap window with the missing ones zero, which
-// adds exact zeros.
-struct ProArgs {
-  const float* conv_w;      // [d_inner][width], or null: no convolution
-  const float* conv_b;      // [d_inner], or null
-  const float* hist;        // [batch][width-1][d_inner] history before the sequence, or null (zeros)
-  float* hist_out;          // [batch][width-1][d_inner] history after it, or null
-  const float* dt_bias;     // [d_inner], or null
-  int width;
-};
-
-template <bool CONV, bool SP>
-struct Prologue {
-  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, cb = 0.f, dtb = 0.f;
-  float h1 = 0.f, h2 = 0.f, h3 = 0.f;       // raw x of tokens t-1, t-2, t-3
-  __device__ __forceinline__ void init(const ProArgs& p, int64_t d) {
-    if constexpr (CONV) {
-      // tap k of the caller's width-W filter goes to slot 4 - W + k
-      const float* wr = p.conv_w + d * p.width;
-      const int off = 4 - p.width;
-      w3 = wr[p.width - 1];
-      w2 = off <= 2 ? wr[2 - off] : 0.f;
-      w1 = off <= 1 ? wr[1 - off] : 0.f;
-      w0 = off <= 0 ? wr[0] : 0.f;
-      cb = p.conv_b ? p.conv_b[d] : 0.f;
-    }
-    if constexpr (SP) dtb = p.dt_bias ? p.dt_bias[d] : 0.f;
-  }
-  // Raw x before token t0 of sequence b: from x itself, or from the history
-  // given for the sequence start (hist, or zeros).
-  template <class T>
-  __device__ __forceinline__ float before(const ProArgs& p, const float* hist, const T* x, int64_t b, int64_t L,
-                                          int64_t d_inner, int64_t pos, int64_t d) const {
-    if (pos >= 0) return widen(x[(b * L + pos) * d_inner + d]);
-    const int64_t j = (p.width - 1) + pos;
-    return (hist && j >= 0) ? hist[(b * (p.width - 1) + j) * d_inner + d] : 0.f;
-  }
-  template <class T>
-  __device__ __forceinline__ void start(const ProArgs& p, const float* hist, const T* x, int64_t b, int64_t L,
-                                        int64_t d_inner, int64_t t0, int64_t d) {
-    if constexpr (CONV) {
-      h1 = before(p, hist, x, b, L, d_inner, t0 - 1, d);
-      h2 = before(p, hist, x, b, L, d_inner, t0 - 2, d);
-      h3 = before(p, hist, x, b, L, d_inner, t0 - 3, d);
-    }
-  }
-  __device__ __forceinline__ float xin(float xv) {
-    if constexpr (CONV) {
-      const float acc = fmaf(w3, xv, fmaf(w2, h1, fmaf(w1, h2, fmaf(w0, h3, cb))));
-      h3 = h2; h2 = h1; h1 = xv;
-      return silu(acc);
-    } else {
-      return xv;
-    }
-  }
-  __device__ __forceinline__ float dt(float dv) const {
-    if constexpr (SP) return softplus(dv + dtb);
-    else return dv;
-  }
-};
+namespace jscan_detail {
 
 // ------------------------------------------------- chunk-local end states
-// Load S consecutive floats from a wave-uniform address (scalar loads).
-template <int S>
-__device__ __forceinline__ void load_row(float (&v)[S], const float* __restrict__ p) {
-  if constexpr (S % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < S / 4; ++q) {
-      const float4 w = reinterpret_cast<const float4*>(p)[q];
-      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < S / 2; ++q) {
-      const float2 w = reinterpret_cast<const float2*>(p)[q];
-      v[2 * q] = w.x; v[2 * q + 1] = w.y;
-    }
-  }
-}
-
-template <int S>
-__device__ __forceinline__ void copy_row(float (&dst)[S], const float (&src)[S]) {
-#pragma unroll
-  for (int s = 0; s < S; ++s) dst[s] = src[s];
-}
-
-// S consecutive values of a B or C row, read with scalar loads from a
-// wave-uniform address and kept in SGPRs in the I/O format.  bf16 pairs stay
-// packed (S/2 dwords) and are widened when used (a scalar shift or mask).
-template <class T, int S> struct Row;
-template <int S> struct Row<uint16_t, S> {
-  static_assert(S % 2 == 0, "bf16 rows are read in pairs");
-  uint32_t w[S / 2];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ p) {
-    if constexpr (S % 8 == 0) {
-#pragma unroll
-      for (int q = 0; q < S / 8; ++q) {
-        const uint4 v = reinterpret_cast<const uint4*>(p)[q];
-        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < S / 2; ++q) w[q] = reinterpret_cast<const uint32_t*>(p)[q];
-    }
-  }
-  __device__ __forceinline__ float operator[](int s) const {
-    return (s & 1) ? __uint_as_float(w[s >> 1] & 0xffff0000u) : __uint_as_float(w[s >> 1] << 16);
-  }
-};
-template <int S> struct Row<float, S> {
-  float w[S];
-  __device__ __forceinline__ void load(const float* __restrict__ p) { load_row(w, p); }
-  __device__ __forceinline__ float operator[](int s) const { return w[s]; }
-};
-
-// Addressing: a wave covers 64 consecutive channels [gbase, gbase + 64).  Row
-// pointers (token t, channel gbase) are wave-uniform and live in SGPRs; a lane
-// adds its own 32-bit offset `lo`.  Lanes past d_inner are clamped onto
-// channel d_inner - 1 (they read valid memory and their results are dropped or
-// duplicate that channel's).
-
-// Streaming loads and stores are buffer instructions: a wave-uniform resource
-// (SGPRs, based at the first row of the current token block), the lane's
-// constant byte offset (VGPR) and the token's row offset (SGPR), so they cost
-// no VALU address arithmetic.  A resource with num_records = 0 makes every
-// load return 0 (out-of-range rule); it stands in for padding tokens' delta.
-constexpr int kBufDword3 = 0x00020000;      // gfx9 raw buffer: 32-bit data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int records = -1) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, records, kBufDword3);
-}
-__device__ __forceinline__ void buf_load(uint16_t& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  v = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-__device__ __forceinline__ void buf_load(float& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-__device__ __forceinline__ void buf_store(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
-}
-__device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
-}
-__device__ __forceinline__ uint16_t to_io(float v, uint16_t) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
-__device__ __forceinline__ float to_io(float v, float) { return v; }
-
 // One lane per channel, all 16 states.  Segment s (of the tokens before the
 // last rescan chunk; every segment has seg_len tokens, a multiple of kTok) of
 // sequence b: S[b][s][n][d] = state after the segment when it starts from
@@ -648,7 +471,6 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
-struct Range { const void* p; size_t bytes; const char* name; };
 
 bool overlap(const Range& a, const Range& b) {
   if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
@@ -658,18 +480,6 @@ bool overlap(const Range& a, const Range& b) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Launch plan.  The main scan runs `chunks` chunks of chunk_len tokens per
-// sequence with K waves per 64 channels.  When chunks > 1, the tokens before
-// the last chunk are cut into segments of seg_len tokens (seg_per_chunk per
-// chunk) for the chunk-local pass, so that pass fills the GPU on its own.
-struct Plan {
-  int K;
-  int chunks;
-  int64_t chunk_len;
-  int seg_per_chunk;
-  int64_t seg_len;
-  int64_t segments() const { return chunks > 1 ? (int64_t)(chunks - 1) * seg_per_chunk : 0; }
-};
 
 // Relative throughput of the scan loops with `waves` waves launched on the
 // 1024 SIMDs, measured on MI355X with the one-wave-per-64-channels kernels
@@ -688,8 +498,8 @@ double wave_efficiency(double waves) {
 
 Plan make_plan(int64_t batch, int64_t L, int64_t d_inner, int K, int64_t C_target) {
   Plan p{K, 1, std::max<int64_t>(L, 1), 1, std::max<int64_t>(L, 1)};
-  if (L <= 0 || C_target <= 1) return p;
   const int64_t groups = batch * ((d_inner + 63) / 64);
+  if (L <= 0 || C_target <= 1 || groups <= 0) return p;
   // segments per chunk: about 32 chunk-local waves per SIMD (rounded down: the
   // combine's work grows with the segment count), >= 64 tokens each
   const int64_t want = (32 * 4 * kCUs) / (groups * (C_target - 1));
@@ -715,8 +525,8 @@ Plan make_plan(int64_t batch, int64_t L, int64_t d_inner, int K, int64_t C_targe
 Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner) {
   if (t_force_K > 0 && t_force_chunks > 0)
     return make_plan(batch, L, d_inner, t_force_K, std::min<int64_t>(t_force_chunks, std::max<int64_t>(L, 1)));
-  if (L <= 0) return make_plan(batch, L, d_inner, 1, 1);
   const int64_t groups = batch * ((d_inner + 63) / 64);
+  if (L <= 0 || groups <= 0) return make_plan(batch, L, d_inner, 1, 1);
   Plan best = make_plan(batch, L, d_inner, 1, 1);
   double best_cost = 1e300;
   for (int64_t C = 1; C <= 4096; C *= 2) {
@@ -732,7 +542,6 @@ Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner) {
 
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-struct WsLayout { size_t S, dsum, hstart, hist, total; };
 
 WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   WsLayout w{};
@@ -817,6 +626,36 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
   return JSCAN_OK;
 }
 
+// Chunk starting states of a chunked plan (the chunk-local pass and the
+// combine, without a prologue), for callers other than the prefill.
+jscan_status forward_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
+                                  const void* delta, const float* A, const void* B, const float* h0, char* ws,
+                                  const Plan& p, hipStream_t st) {
+  if (p.chunks <= 1) return JSCAN_OK;
+  const WsLayout w = ws_layout(batch, L, d_inner, p);
+  float* S = reinterpret_cast<float*>(ws);
+  float* dsum = reinterpret_cast<float*>(ws + w.S);
+  float* hstart = reinterpret_cast<float*>(ws + w.S + w.dsum);
+  const ProArgs none{nullptr, nullptr, nullptr, nullptr, nullptr, 1};
+  const int segs = (int)p.segments();
+  dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)segs, (unsigned)batch);
+  if (io == JSCAN_IO_BF16)
+    hipLaunchKernelGGL((k_chunk_state<uint16_t>), g1, dim3(256), 0, st, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(delta), A, static_cast<const uint16_t*>(B), S, dsum, L,
+                       d_inner, p.seg_len, segs, none);
+  else
+    hipLaunchKernelGGL((k_chunk_state<float>), g1, dim3(256), 0, st, static_cast<const float*>(x),
+                       static_cast<const float*>(delta), A, static_cast<const float*>(B), S, dsum, L, d_inner,
+                       p.seg_len, segs, none);
+  hipError_t e;
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
+  dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
+  hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks, p.seg_per_chunk,
+                     nullptr, nullptr, 0);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
+  return JSCAN_OK;
+}
+
 // Calls f(integral_constant<bool, CONV>, integral_constant<bool, SP>).
 template <class F>
 auto with_prologue(bool conv, bool sp, F&& f) {
@@ -834,8 +673,7 @@ jscan_status check_common(int64_t d_state, jscan_io io) {
 
 // Every output against every input and every other output.  An output may be
 // the very same buffer as one input (`same_ok`, e.g. an in-place state carry).
-jscan_status check_ranges(const Range* in, int n_in, const Range* out, int n_out,
-                          const void* same_ok = nullptr) {
+jscan_status check_ranges(const Range* in, int n_in, const Range* out, int n_out, const void* same_ok) {
   for (int i = 0; i < n_out; ++i) {
     for (int j = 0; j < n_in; ++j)
       if (!(same_ok && out[i].p == same_ok && in[j].p == same_ok && out[i].bytes == in[j].bytes) &&
@@ -1025,7 +863,9 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
   });
 }
 
-}  // namespace
+}  // namespace jscan_detail
+
+using namespace jscan_detail;
 
 // ================================================================ C ABI
 extern "C" {

@@ -1,0 +1,626 @@
+// libjscan backward: gradients of the selective scan (jscan_prefill) for
+// training, on gfx950.
+//
+// The forward recurrence (per sequence b, channel d, state n) is
+//   h_t = a_t h_{t-1} + dt_t B_t x_t,  a_t = exp(dt_t A),
+//   y_t = (C_t . h_t + D x_t) SiLU(z_t)
+// ("AI Engineering from Scratch" Jamba lesson, section on the SSM; A real and
+// diagonal as in Mamba-1).  Its adjoint, for output gradients dy and dhT,
+// runs backwards in time with the same decays:
+//   lambda_t = dp_t C_t + mu_{t+1},  mu_t = a_t lambda_t,  mu_L = dhT,
+// with dp_t = dy_t SiLU(z_t), and every input gradient is a local product of
+// lambda_t, mu_t and the forward state at token t:
+//   dx_t     = D dp_t + dt_t (lambda_t . B_t)
+//   ddelta_t = x_t (lambda_t . B_t) + sum_n A_n mu_tn h_{t-1,n}
+//   dz_t     = dy_t p_t SiLU'(z_t)             (p_t: the pre-gate output)
+//   dA_n     = sum_{b,t} dt_t mu_tn h_{t-1,n},   dD = sum_{b,t} dp_t x_t
+//   dB_tn    = sum_d lambda_tn dt_t x_t,         dC_tn = sum_d dp_t h_tn
+//   dh0      = mu_0.
+//
+// Work decomposition (one lane per channel, 64 channels per wave, as in the
+// forward):
+// 1. Forward chunk starting states: the forward's chunk-local pass and
+//    combine (chunked plans only).
+// 2. Chunk-local adjoint (k_adj_local): every chunk but the first runs the
+//    adjoint backwards from mu = 0 over its tokens; its result M_c and the
+//    chunk's delta sum give the (decay, offset) pair of the chunk.
+// 3. k_adj_combine folds the pairs from the last chunk down, seeded with
+//    dhT, giving the adjoint that enters each chunk from the later ones.
+// 4. k_bwd, per (chunk, 64 channels): a forward sweep from the chunk's
+//    starting state writes dz, the dC partial sums and a state checkpoint
+//    every kTok tokens; a reverse sweep then takes the chunk's pieces of kTok
+//    tokens from the last: it recomputes the piece's states from its
+//    checkpoint (kept in registers) and steps the adjoint back through the
+//    piece, writing dx, ddelta and the dB partial sums and accumulating
+//    dA and dD.
+// 5. Reductions: dB and dC over the 64-channel groups, dA and dD over chunks
+//    and sequences (fixed order, so results are deterministic).
+// dB_t and dC_t are sums over channels: inside a wave a transposing
+// butterfly (permlane swaps and DPP) reduces the 16 values of the 64 lanes
+// in 35 instructions, leaving one partial per (group, token, state).
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <string>
+
+#include "jscan.h"
+
+#include "common.h"
+#include "host.h"
+
+namespace {
+
+using namespace jscan_detail;
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum of v[n] over the 64 lanes of the wave for each n; lane i returns the sum
+// for n = i >> 2.  Each step pairs every lane with a partner, keeps half of
+// its values and adds the partner's copy of them:
+//   permlane32 swap: lanes 0-31 keep n < 8, lanes 32-63 keep n >= 8;
+//   permlane16 swap: odd 16-lane rows take n + 4;
+//   DPP row_ror:8 (lane i ^ 8 within a row) and row_half_mirror (i ^ 7
+//   within 8 lanes) split the last four values over lane bits 3 and 2;
+//   two quad_perm adds finish the sum over lane bits 1 and 0.
+__device__ __forceinline__ float wave_sum16(const float (&v)[NSTATE], int lane) {
+  float r[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 8]), false, false);
+    r[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  float q[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(r[k]), __float_as_uint(r[k + 4]), false, false);
+    q[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+  float s[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) s[k] = (b3 ? q[k + 2] : q[k]) + dpp_mov<0x128>(b3 ? q[k] : q[k + 2]);
+  float u = (b2 ? s[1] : s[0]) + dpp_mov<0x141>(b2 ? s[0] : s[1]);
+  u += dpp_mov<0xB1>(u);     // quad_perm [1,0,3,2]
+  u += dpp_mov<0x4E>(u);     // quad_perm [2,3,0,1]
+  return u;
+}
+
+// ------------------------------------------------------ chunk-local adjoint
+// One lane per channel.  Chunk c >= 1 of sequence b, from its last token
+// back to its first with mu = 0 entering: M[b][c][n][d] = mu at the chunk's
+// first token, dsum[b][c][d] = sum of delta over the chunk (fp64 sum).  A
+// partial last chunk is padded at its end with delta = 0 and dy = 0, which
+// keep mu at zero.
+template <class T>
+__global__ __launch_bounds__(256) void k_adj_local(const T* __restrict__ delta, const float* __restrict__ A,
+                                                   const T* __restrict__ Cm, const T* __restrict__ z,
+                                                   const T* __restrict__ dy, float* __restrict__ M,
+                                                   float* __restrict__ dsum, int64_t L, int64_t d_inner,
+                                                   int64_t chunk_len, int n_chunks) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t gbase = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (gbase >= d_inner) return;
+  const int c = blockIdx.y + 1;
+  const int64_t b = blockIdx.z;
+  const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
+  const int64_t d = gbase + lo;
+
+  float a2[NSTATE], mu[NSTATE];
+  const float4* Ap = reinterpret_cast<const float4*>(A + d * NSTATE);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = Ap[q];
+    a2[4 * q + 0] = v.x * kLog2e; a2[4 * q + 1] = v.y * kLog2e;
+    a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
+  }
+#pragma unroll
+  for (int n = 0; n < NSTATE; ++n) mu[n] = 0.0f;
+  double dacc = 0.0;
+
+  const int64_t t0 = (int64_t)c * chunk_len;
+  const int nt = (int)std::min<int64_t>(chunk_len, L - t0);
+  const int64_t row0 = (b * L + t0) * d_inner + gbase;
+  const T* drow = delta + row0;
+  const T* zrow = z + row0;
+  const T* grow = dy + row0;
+  const T* crow = Cm + (b * L + t0) * NSTATE;
+  const uint32_t lb = (uint32_t)lo * sizeof(T);
+  const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
+
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&zz)[kTok], T (&gg)[kTok]) {
+    const int64_t o = (int64_t)bb * d_inner;
+    const auto rd = rsrc(drow + o), rz = rsrc(zrow + o), rg = rsrc(grow + o), r0 = rsrc(drow, 0);
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+      const bool real = bb + j < nt;
+      const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
+      buf_load(dd[j], real ? rd : r0, lb, so);
+      buf_load(zz[j], rz, lb, so);
+      buf_load(gg[j], real ? rg : r0, lb, so);
+    }
+  };
+  Row<T, NSTATE> Cr;
+  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&zz)[kTok], const T (&gg)[kTok]) {
+#pragma unroll
+    for (int j = kTok - 1; j >= 0; --j) {
+      Cr.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
+      const float dt = widen(dd[j]);
+      const float dp = widen(gg[j]) * silu(widen(zz[j]));
+      dacc += (double)dt;
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) mu[n] = fast_exp2(dt * a2[n]) * fmaf(dp, Cr[n], mu[n]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int last = (nt - 1) / kTok * kTok;
+  T dA_[kTok], zA[kTok], gA[kTok], dB_[kTok], zB[kTok], gB[kTok];
+  load_block(last, dA_, zA, gA);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int base = last; base >= 0; base -= 2 * kTok) {
+    load_block(std::max(base - kTok, 0), dB_, zB, gB);
+    do_block(base, dA_, zA, gA);
+    if (base - kTok < 0) break;
+    load_block(std::max(base - 2 * kTok, 0), dA_, zA, gA);
+    do_block(base - kTok, dB_, zB, gB);
+  }
+  if (lo == lane) {
+    const int64_t slot = b * n_chunks + c;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) M[(slot * NSTATE + n) * d_inner + d] = mu[n];
+    dsum[slot * d_inner + d] = (float)dacc;
+  }
+}
+
+// ------------------------------------------------------- adjoint carries
+// One lane per (b, n, d).  Folds the chunks' pairs from the last chunk down:
+// mu <- exp2(A' dsum_c) mu + M_c, seeded with dhT (or 0).  Afterwards slot c
+// (c >= 1) of M holds the adjoint entering chunk c - 1 from later tokens.
+__global__ __launch_bounds__(256) void k_adj_combine(const float* __restrict__ A, const float* __restrict__ dsum,
+                                                     const float* __restrict__ dhT, float* __restrict__ M,
+                                                     int64_t d_inner, int n_chunks) {
+  constexpr int G = 16;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  const int64_t per_seq = d_inner * NSTATE;
+  if (i >= per_seq) return;
+  const int64_t n = i / d_inner;
+  const int64_t d = i - n * d_inner;
+  const float a2 = A[d * NSTATE + n] * kLog2e;
+  float mu = dhT ? dhT[(b * d_inner + d) * NSTATE + n] : 0.0f;
+  float* Mp = M + (b * n_chunks) * per_seq + i;
+  const float* Dp = dsum + (b * n_chunks) * d_inner + d;
+  for (int c0 = n_chunks - 1; c0 >= 1; c0 -= G) {
+    float mv[G], dv[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int c = std::max(c0 - k, 1);
+      mv[k] = Mp[(int64_t)c * per_seq];
+      dv[k] = Dp[(int64_t)c * d_inner];
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int c = c0 - k;
+      if (c >= 1) {
+        mu = fmaf(fast_exp2(a2 * dv[k]), mu, mv[k]);
+        Mp[(int64_t)c * per_seq] = mu;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ main backward
+// Grid: (d_inner / 64 groups, chunks, batch); one wave per block.  See the
+// file header for the two sweeps.  Padding tokens of a partial last block
+// read delta = 0 and dy = 0 (empty buffer resource): they change neither the
+// state nor the adjoint, and their outputs are not stored.  Lanes clamped
+// onto the last channel contribute zero to the channel sums.
+template <class T>
+__global__ __launch_bounds__(64) void k_bwd(
+    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dw, const T* __restrict__ z,
+    const T* __restrict__ dy, const float* __restrict__ hinit, const float* __restrict__ Min,
+    const float* __restrict__ dhT, T* __restrict__ dx, T* __restrict__ ddelta, T* __restrict__ dz,
+    float* __restrict__ dBp, float* __restrict__ dCp, float* __restrict__ dAp, float* __restrict__ dDp,
+    float* __restrict__ dh0, float* __restrict__ ck, int64_t L, int64_t d_inner, int64_t chunk_len,
+    int n_chunks) {
+  const int lane = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int64_t G = gridDim.x;
+  const int64_t gbase = g * 64;
+  const int c = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
+  const int64_t d = gbase + lo;
+  const float lf = lo == lane ? 1.0f : 0.0f;
+
+  float a2[NSTATE], h[NSTATE];
+  const float4* Ap = reinterpret_cast<const float4*>(A + d * NSTATE);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = Ap[q];
+    a2[4 * q + 0] = v.x * kLog2e; a2[4 * q + 1] = v.y * kLog2e;
+    a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
+  }
+  if (n_chunks > 1) {
+    const float* hi = hinit + ((b * n_chunks + c) * NSTATE) * d_inner + d;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) h[n] = hi[(int64_t)n * d_inner];
+  } else {
+    const float* hi = hinit ? hinit + (b * d_inner + d) * NSTATE : nullptr;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) h[n] = hi ? hi[n] : 0.0f;
+  }
+  const float Dd = Dw[d];
+
+  const int64_t t0 = (int64_t)c * chunk_len;
+  const int nt = (int)std::min<int64_t>(chunk_len, L - t0);
+  const int64_t row0 = (b * L + t0) * d_inner + gbase;
+  const T* xrow = x + row0;
+  const T* drow = delta + row0;
+  const T* zrow = z + row0;
+  const T* grow = dy + row0;
+  T* dxrow = dx + row0;
+  T* ddrow = ddelta + row0;
+  T* dzrow = dz + row0;
+  const T* brow = Bm + (b * L + t0) * NSTATE;
+  const T* crow = Cm + (b * L + t0) * NSTATE;
+  const int64_t pieces = (chunk_len + kTok - 1) / kTok;
+  float* ckp = ck + ((b * n_chunks + c) * pieces * NSTATE) * d_inner + d;
+  float* dbp = dBp + ((b * G + g) * L + t0) * NSTATE + (lane >> 2);
+  float* dcp = dCp + ((b * G + g) * L + t0) * NSTATE + (lane >> 2);
+  const uint32_t lb = (uint32_t)lo * sizeof(T);
+  const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
+  const int last = (nt - 1) / kTok * kTok;
+
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&gg)[kTok]) {
+    const int64_t o = (int64_t)bb * d_inner;
+    const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), rg = rsrc(grow + o);
+    const auto r0 = rsrc(drow, 0);
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+      const bool real = bb + j < nt;
+      const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
+      buf_load(dd[j], real ? rd : r0, lb, so);
+      buf_load(xx[j], rx, lb, so);
+      buf_load(zz[j], rz, lb, so);
+      buf_load(gg[j], real ? rg : r0, lb, so);
+    }
+  };
+
+  // ---- forward sweep: dz, dC partials, checkpoints, dD
+  float dD = 0.0f;
+  Row<T, NSTATE> Bc, Bn, Cv;
+  auto fwd_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
+                       const T (&gg)[kTok]) {
+    float* cp = ckp + (int64_t)(bb / kTok) * NSTATE * d_inner;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) cp[(int64_t)n * d_inner] = h[n];     // state before token bb
+    const auto rz = rsrc(dzrow + (int64_t)bb * d_inner);
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+      Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
+      Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
+      const float dt = widen(dd[j]), xv = widen(xx[j]);
+      const float dxv = dt * xv;
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Bc[n]);
+      float acc = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) acc = fmaf(Cv[n], h[n], acc);
+      const float zv = widen(zz[j]), gv = widen(gg[j]);
+      const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
+      const float sl = zv * sg;
+      const float dp = gv * sl;
+      const float p = fmaf(Dd, xv, acc);
+      dD = fmaf(dp, xv, dD);
+      float v[NSTATE];
+      const float dpl = dp * lf;
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) v[n] = dpl * h[n];
+      const float sum = wave_sum16(v, lane);
+      if (bb + j < nt) {
+        buf_store(to_io(gv * p * sg * (1.0f + zv - sl), T()), rz, lb, (uint32_t)j * rowb);
+        if ((lane & 3) == 0) dcp[(int64_t)(bb + j) * NSTATE] = sum;
+      }
+      Bc = Bn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  {
+    T dA_[kTok], xA[kTok], zA[kTok], gA[kTok], dB_[kTok], xB[kTok], zB[kTok], gB[kTok];
+    load_block(0, dA_, xA, zA, gA);
+    Bc.load(brow);
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int base = 0; base < nt; base += 2 * kTok) {
+      load_block(std::min(base + kTok, last), dB_, xB, zB, gB);
+      fwd_block(base, dA_, xA, zA, gA);
+      if (base + kTok >= nt) break;
+      load_block(std::min(base + 2 * kTok, last), dA_, xA, zA, gA);
+      fwd_block(base + kTok, dB_, xB, zB, gB);
+    }
+  }
+
+  // ---- reverse sweep: dx, ddelta, dB partials, dA
+  float mu[NSTATE], dA[NSTATE];
+  if (c == n_chunks - 1) {
+    const float* mi = dhT ? dhT + (b * d_inner + d) * NSTATE : nullptr;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) mu[n] = mi ? mi[n] : 0.0f;
+  } else {
+    const float* mi = Min + ((b * n_chunks + c + 1) * NSTATE) * d_inner + d;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) mu[n] = mi[(int64_t)n * d_inner];
+  }
+#pragma unroll
+  for (int n = 0; n < NSTATE; ++n) dA[n] = 0.0f;
+  Row<T, NSTATE> Br;
+  for (int pb = last; pb >= 0; pb -= kTok) {
+    T dd[kTok], xx[kTok], zz[kTok], gg[kTok];
+    load_block(pb, dd, xx, zz, gg);
+    const float* cp = ckp + (int64_t)(pb / kTok) * NSTATE * d_inner;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) h[n] = cp[(int64_t)n * d_inner];
+    // states before each token of the piece
+    float hp[kTok][NSTATE];
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+      Br.load(brow + (int64_t)std::min(pb + j, nt - 1) * NSTATE);
+      const float dt = widen(dd[j]);
+      const float dxv = dt * widen(xx[j]);
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) {
+        hp[j][n] = h[n];
+        h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Br[n]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const auto rx = rsrc(dxrow + (int64_t)pb * d_inner), rd = rsrc(ddrow + (int64_t)pb * d_inner);
+#pragma unroll
+    for (int j = kTok - 1; j >= 0; --j) {
+      Br.load(brow + (int64_t)std::min(pb + j, nt - 1) * NSTATE);
+      Cv.load(crow + (int64_t)std::min(pb + j, nt - 1) * NSTATE);
+      const float dt = widen(dd[j]), xv = widen(xx[j]), zv = widen(zz[j]), gv = widen(gg[j]);
+      const float dp = gv * silu(zv);
+      const float dxl = dt * xv * lf;
+      float sLB = 0.0f, sAW = 0.0f, u[NSTATE];
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) {
+        const float lam = fmaf(dp, Cv[n], mu[n]);
+        sLB = fmaf(lam, Br[n], sLB);
+        const float m = fast_exp2(dt * a2[n]) * lam;
+        mu[n] = m;
+        const float w = m * hp[j][n];
+        sAW = fmaf(a2[n], w, sAW);
+        dA[n] = fmaf(dt, w, dA[n]);
+        u[n] = lam * dxl;
+      }
+      const float sum = wave_sum16(u, lane);
+      if (pb + j < nt) {
+        const uint32_t so = (uint32_t)j * rowb;
+        buf_store(to_io(fmaf(Dd, dp, dt * sLB), T()), rx, lb, so);
+        buf_store(to_io(fmaf(xv, sLB, kLn2 * sAW), T()), rd, lb, so);
+        if ((lane & 3) == 0) dbp[(int64_t)(pb + j) * NSTATE] = sum;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (lo == lane) {
+    if (c == 0 && dh0) {
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) dh0[(b * d_inner + d) * NSTATE + n] = mu[n];
+    }
+    const int64_t slot = b * n_chunks + c;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) dAp[(slot * NSTATE + n) * d_inner + d] = dA[n];
+    dDp[slot * d_inner + d] = dD;
+  }
+}
+
+// dB[b][t][n] and dC[b][t][n]: sums of the G group partials (fixed order).
+__global__ __launch_bounds__(256) void k_reduce_bc(const float* __restrict__ dBp, const float* __restrict__ dCp,
+                                                   float* __restrict__ dB, float* __restrict__ dC, int64_t L,
+                                                   int G) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  const int64_t per = L * NSTATE;
+  if (i >= per) return;
+  const float* pb = dBp + (b * G) * per + i;
+  const float* pc = dCp + (b * G) * per + i;
+  float sb = 0.0f, sc = 0.0f;
+  for (int g = 0; g < G; ++g) {
+    sb += pb[(int64_t)g * per];
+    sc += pc[(int64_t)g * per];
+  }
+  dB[b * per + i] = sb;
+  dC[b * per + i] = sc;
+}
+
+// dA[d][n] and dD[d]: sums of the per-(sequence, chunk) partials (fixed order).
+__global__ __launch_bounds__(256) void k_reduce_ad(const float* __restrict__ dAp, const float* __restrict__ dDp,
+                                                   float* __restrict__ dA, float* __restrict__ dD,
+                                                   int64_t d_inner, int64_t slots) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = d_inner * NSTATE;
+  if (i >= per) return;
+  const int64_t n = i / d_inner;
+  const int64_t d = i - n * d_inner;
+  float sa = 0.0f, sd = 0.0f;
+  for (int64_t k = 0; k < slots; ++k) {
+    sa += dAp[k * per + i];
+    if (n == 0) sd += dDp[k * d_inner + d];
+  }
+  dA[d * NSTATE + n] = sa;
+  if (n == 0) dD[d] = sd;
+}
+
+__global__ __launch_bounds__(256) void k_copy_or_zero(const float* __restrict__ src, float* __restrict__ dst,
+                                                      int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+// ------------------------------------------------------------------ host
+struct BwdLayout {
+  size_t fwd, M, dsum, ck, dBp, dCp, dAp, dDp, total;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
+  BwdLayout w{};
+  if (batch <= 0 || L <= 0 || d_inner <= 0) return w;
+  const size_t B = (size_t)batch, C = (size_t)p.chunks, Dn = (size_t)d_inner;
+  const size_t G = (size_t)((d_inner + 63) / 64);
+  const size_t pieces = (size_t)((p.chunk_len + kTok - 1) / kTok);
+  w.fwd = ws_layout(batch, L, d_inner, p).total;
+  if (p.chunks > 1) {
+    w.M = round_up(B * C * NSTATE * Dn * 4);
+    w.dsum = round_up(B * C * Dn * 4);
+  }
+  w.ck = round_up(B * C * pieces * NSTATE * Dn * 4);
+  w.dBp = round_up(B * G * (size_t)L * NSTATE * 4);
+  w.dCp = w.dBp;
+  w.dAp = round_up(B * C * NSTATE * Dn * 4);
+  w.dDp = round_up(B * C * Dn * 4);
+  w.total = w.fwd + w.M + w.dsum + w.ck + w.dBp + w.dCp + w.dAp + w.dDp;
+  return w;
+}
+
+template <class T>
+jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io, const void* x, const void* delta,
+                          const float* A, const void* B, const void* C, const float* D, const void* z,
+                          const float* h0, const void* dy, const float* dhT, void* dx, void* ddelta, void* dz,
+                          float* dA, float* dB, float* dC, float* dD, float* dh0, char* ws, const Plan& p,
+                          hipStream_t st) {
+  const BwdLayout w = bwd_layout(batch, L, d_inner, p);
+  const WsLayout fw = ws_layout(batch, L, d_inner, p);
+  float* hstart = reinterpret_cast<float*>(ws + fw.S + fw.dsum);
+  char* q = ws + w.fwd;
+  float* M = reinterpret_cast<float*>(q); q += w.M;
+  float* dsum = reinterpret_cast<float*>(q); q += w.dsum;
+  float* ck = reinterpret_cast<float*>(q); q += w.ck;
+  float* dBp = reinterpret_cast<float*>(q); q += w.dBp;
+  float* dCp = reinterpret_cast<float*>(q); q += w.dCp;
+  float* dAp = reinterpret_cast<float*>(q); q += w.dAp;
+  float* dDp = reinterpret_cast<float*>(q);
+  const int G = (int)((d_inner + 63) / 64);
+  hipError_t e;
+  jscan_status s;
+
+  if (p.chunks > 1) {
+    if ((s = forward_chunk_starts(io, batch, L, d_inner, x, delta, A, B, h0, ws, p, st)) != JSCAN_OK) return s;
+    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)(p.chunks - 1), (unsigned)batch);
+    hipLaunchKernelGGL((k_adj_local<T>), g1, dim3(256), 0, st, static_cast<const T*>(delta), A,
+                       static_cast<const T*>(C), static_cast<const T*>(z), static_cast<const T*>(dy), M, dsum, L,
+                       d_inner, p.chunk_len, p.chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "adjoint chunk launch");
+    dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
+    hipLaunchKernelGGL(k_adj_combine, g2, dim3(256), 0, st, A, dsum, dhT, M, d_inner, p.chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "adjoint combine launch");
+  }
+  dim3 g3((unsigned)G, (unsigned)p.chunks, (unsigned)batch);
+  hipLaunchKernelGGL((k_bwd<T>), g3, dim3(64), 0, st, static_cast<const T*>(x), static_cast<const T*>(delta), A,
+                     static_cast<const T*>(B), static_cast<const T*>(C), D, static_cast<const T*>(z),
+                     static_cast<const T*>(dy), p.chunks > 1 ? hstart : h0, M, dhT, static_cast<T*>(dx),
+                     static_cast<T*>(ddelta), static_cast<T*>(dz), dBp, dCp, dAp, dDp, dh0, ck, L, d_inner,
+                     p.chunk_len, p.chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "backward launch");
+  dim3 g4((unsigned)((L * NSTATE + 255) / 256), (unsigned)batch);
+  hipLaunchKernelGGL(k_reduce_bc, g4, dim3(256), 0, st, dBp, dCp, dB, dC, L, G);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dB/dC reduce launch");
+  hipLaunchKernelGGL(k_reduce_ad, dim3((unsigned)((d_inner * NSTATE + 255) / 256)), dim3(256), 0, st, dAp, dDp, dA,
+                     dD, d_inner, batch * (int64_t)p.chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dA/dD reduce launch");
+  return JSCAN_OK;
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" {
+
+size_t jscan_backward_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io) {
+  (void)io;
+  if (d_state != NSTATE || !sizes_ok(batch, L, d_inner)) return 0;
+  return bwd_layout(batch, L, d_inner, choose_plan(batch, L, d_inner)).total;
+}
+
+jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                            const void* x, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const float* h0, const void* dy, const float* dhT,
+                            void* dx, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
+                            float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  t_last_error.clear();
+  jscan_status s = check_common(d_state, io);
+  if (s != JSCAN_OK) return s;
+  if (!sizes_ok(batch, L, d_inner)) return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
+  const bool work = batch > 0 && L > 0 && d_inner > 0;
+  if (work && (!x || !delta || !B || !C || !z || !dy || !dx || !ddelta || !dz || !dB || !dC))
+    return fail(JSCAN_ERR_NULL, "x, delta, B, C, z, dy, dx, ddelta, dz, dB and dC are required");
+  if (d_inner > 0 && (!A || !D || !dA || !dD)) return fail(JSCAN_ERR_NULL, "A, D, dA and dD are required");
+  const void* ptrs[] = {x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz, dA, dB, dC, dD, dh0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
+  const size_t tok = (size_t)batch * (size_t)L * (size_t)d_inner * es;
+  const size_t rowb = (size_t)batch * (size_t)L * NSTATE * es;
+  const size_t row4 = (size_t)batch * (size_t)L * NSTATE * 4;
+  const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
+  const size_t pd = (size_t)d_inner * NSTATE * 4;
+  const Plan plan = choose_plan(batch, L, d_inner);
+  const size_t need = bwd_layout(batch, L, d_inner, plan).total;
+  const Range in[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {dy, tok, "dy"}, {B, rowb, "B"},
+                      {C, rowb, "C"}, {A, pd, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"},
+                      {dhT, stb, "dhT"}};
+  const Range out[] = {{dx, tok, "dx"}, {ddelta, tok, "ddelta"}, {dz, tok, "dz"}, {dA, pd, "dA"},
+                       {dB, row4, "dB"}, {dC, row4, "dC"}, {dD, (size_t)d_inner * 4, "dD"}, {dh0, stb, "dh0"},
+                       {workspace, workspace ? need : 0, "workspace"}};
+  if ((s = check_ranges(in, (int)(sizeof(in) / sizeof(in[0])), out, (int)(sizeof(out) / sizeof(out[0])))) !=
+      JSCAN_OK)
+    return s;
+  if (workspace && workspace_bytes < need)
+    return fail(JSCAN_ERR_WORKSPACE, "workspace smaller than jscan_backward_workspace_size()");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!work) {
+    // Nothing to scan: parameter gradients are zero and dh0 = dhT (or 0).
+    if (d_inner > 0) {
+      hipLaunchKernelGGL(k_reduce_ad, dim3((unsigned)((d_inner * NSTATE + 255) / 256)), dim3(256), 0, st,
+                         nullptr, nullptr, dA, dD, d_inner, (int64_t)0);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "zero-fill launch");
+    }
+    if (dh0 && batch > 0 && d_inner > 0) {
+      const int64_t n = batch * d_inner * NSTATE;
+      hipLaunchKernelGGL(k_copy_or_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dhT, dh0, n);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dh0 copy launch");
+    }
+    return JSCAN_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  bool owned = false;
+  if (!ws) {
+    if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess)
+      return hip_fail(e, "hipMallocAsync(workspace)");
+    owned = true;
+  }
+  s = io == JSCAN_IO_BF16
+          ? run_backward<uint16_t>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz,
+                                   dA, dB, dC, dD, dh0, ws, plan, st)
+          : run_backward<float>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz, dA,
+                                dB, dC, dD, dh0, ws, plan, st);
+  if (owned) {
+    e = hipFreeAsync(ws, st);
+    if (s == JSCAN_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
+  }
+  return s;
+}
+
+}  // extern "C"

@@ -27,6 +27,10 @@ Recipe (Jamba-shaped inputs: hidden 4096, d_inner 8192, d_state 16):
   Raw (pre-softplus) time steps for tokens [0, L) come from
   ``PCG64([seed, PROLOGUE_STREAM, 1])`` as N(0, 1) [batch, L, d_inner] in the
   I/O dtype.
+* Output gradients for the backward scan come from ``PCG64([seed,
+  GRAD_STREAM, block])`` per block of ``CHUNK`` tokens as dy ~ N(0, 1)
+  [batch, block, d_inner] in the I/O dtype, and dhT ~ N(0, 1) [batch, d_inner,
+  d_state] fp32 from ``PCG64([seed, GRAD_STREAM])``.
 * Decode inputs for step k of a run seeded ``seed`` come from
   ``PCG64([seed, DECODE_STREAM, k])`` in the order x, delta, z ([n_seq,
   d_inner]), B, C ([n_seq, d_state]); the initial decode state (~N(0, 1)) from
@@ -49,6 +53,7 @@ PARAM_STREAM = 1_000_003
 DECODE_STREAM = 2_000_003
 STATE_STREAM = 3_000_017
 PROLOGUE_STREAM = 4_000_037
+GRAD_STREAM = 5_000_011
 
 IO_BF16 = "bf16"
 IO_F32 = "f32"
@@ -184,6 +189,25 @@ def raw_time_steps(batch, L, d_inner, seed=0, io=IO_BF16):
     """Pre-softplus time steps ~ N(0, 1), [batch, L, d_inner] in the I/O dtype."""
     g = np.random.Generator(np.random.PCG64([seed, PROLOGUE_STREAM, 1]))
     return _round(g.standard_normal(size=(batch, L, d_inner)), io)
+
+
+def output_grads(batch, L, d_inner, d_state=16, seed=0, io=IO_BF16, t_begin=0, t_end=None):
+    """dy [batch, T, d_inner] (I/O dtype) for tokens [t_begin, t_end) and dhT
+    [batch, d_inner, d_state] fp32.  t_begin, t_end: multiples of CHUNK unless 0, L."""
+    t_end = L if t_end is None else t_end
+    dy = np.empty((batch, t_end - t_begin, d_inner), _io_dtype(io))
+    t = t_begin
+    while t < t_end:
+        blk = t // CHUNK
+        hi = min(t_end, (blk + 1) * CHUNK, L)
+        g = np.random.Generator(np.random.PCG64([seed, GRAD_STREAM, blk]))
+        full = min(CHUNK, L - blk * CHUNK)
+        v = g.standard_normal(size=(batch, full, d_inner))
+        dy[:, t - t_begin:hi - t_begin, :] = _round(v[:, t - blk * CHUNK:hi - blk * CHUNK, :], io)
+        t = hi
+    g = np.random.Generator(np.random.PCG64([seed, GRAD_STREAM]))
+    dhT = g.standard_normal(size=(batch, d_inner, d_state)).astype(np.float32)
+    return dy, dhT
 
 
 def decode_state(n_seq, d_inner, d_state=16, seed=3):

@@ -137,6 +137,9 @@ def test_workspace_size_formula(lib):
     assert js.workspace_size(1, 64, 128, 15) == 0
     assert js.workspace_size(-1, 64, 128) == 0
     assert js.workspace_size(0, 0, 0) == 0
+    # no channel groups (batch 0 or d_inner 0) with tokens: a single-pass plan
+    assert js.workspace_size(0, 65536, 8192) == 0
+    assert js.plan(0, 65536, 8192) == (1, 1) and js.plan(1, 65536, 0) == (1, 1)
 
 
 def test_automatic_plan_fills_mi355x():
@@ -272,3 +275,54 @@ def test_step_fused_validation(lib):
                                       fake(6), fake(7), fake(11), ctypes.byref(prologue()), None) == ALIAS
     assert lib.jscan_step_batch_fused(0, 64, 16, BF16, None, None, None, None, None, None, None, None, None,
                                       ctypes.byref(prologue(conv_width=9)), None) == UNSUP
+
+
+# ------------------------------------------------------------------ backward
+def bwd_args(batch=1, L=64, d_inner=128, d_state=16, io=BF16, **over):
+    a = dict(batch=batch, L=L, d_inner=d_inner, d_state=d_state, io=io, x=fake(0), delta=fake(1), A=fake(2),
+             B=fake(3), C=fake(4), D=fake(5), z=fake(6), h0=fake(7), dy=fake(8), dhT=fake(9), dx=fake(16),
+             ddelta=fake(17), dz=fake(18), dA=fake(19), dB=fake(20), dC=fake(21), dD=fake(22), dh0=fake(23),
+             workspace=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return a
+
+
+def call_bwd(lib, a):
+    keys = ("batch", "L", "d_inner", "d_state", "io", "x", "delta", "A", "B", "C", "D", "z", "h0", "dy", "dhT",
+            "dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "dh0", "workspace", "ws_bytes", "stream")
+    return lib.jscan_backward(*(a[k] for k in keys))
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "B", "C", "z", "dy", "dx", "ddelta", "dz", "dB", "dC", "A", "D",
+                                  "dA", "dD"])
+def test_backward_null_required_pointer(lib, name):
+    assert call_bwd(lib, bwd_args(**{name: None})) == NULL
+
+
+@pytest.mark.parametrize("name", ["x", "dy", "dhT", "dx", "dA", "dB", "dh0"])
+def test_backward_alignment(lib, name):
+    a = bwd_args()
+    a[name] = ctypes.c_void_p(a[name].value + 4)
+    assert call_bwd(lib, a) == ALIGN
+
+
+def test_backward_validation(lib):
+    assert call_bwd(lib, bwd_args(L=-1)) == SHAPE
+    assert call_bwd(lib, bwd_args(d_state=8)) == UNSUP
+    assert call_bwd(lib, bwd_args(io=3)) == UNSUP
+    assert call_bwd(lib, bwd_args(dx=fake(0))) == ALIAS                 # dx on x
+    assert call_bwd(lib, bwd_args(dh0=fake(9))) == ALIAS                # dh0 on dhT (no in-place)
+    assert call_bwd(lib, bwd_args(dB=fake(16, 64))) == ALIAS            # dB inside dx
+    assert call_bwd(lib, bwd_args(dA=fake(5))) == ALIAS                 # dA on D
+    ws = js.backward_workspace_size(1, 64, 128)
+    assert ws > 0
+    assert call_bwd(lib, bwd_args(workspace=fake(30), ws_bytes=ws - 1)) == WS
+    assert call_bwd(lib, bwd_args(workspace=fake(8), ws_bytes=ws)) == ALIAS   # workspace over dy
+
+
+def test_backward_workspace_size():
+    # recomputed states (~8 B per channel-token) and the dB/dC partials dominate
+    L, d = 65536, 8192
+    assert js.backward_workspace_size(1, L, d) >= L * d * 8
+    assert js.backward_workspace_size(0, L, d) == 0
+    assert js.backward_workspace_size(1, L, d, 15) == 0
