@@ -562,7 +562,8 @@ bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner) {
   if (!mul_ok(batch, L, &t) || !mul_ok(t, d_inner, &t) || !mul_ok(t, 8, &t)) return false;
   if (!mul_ok(batch, d_inner, &t) || !mul_ok(t, NSTATE * 8, &t)) return false;
   if (!mul_ok(batch, L, &t) || !mul_ok(t, 32 * 8, &t)) return false;
-  return L <= INT32_MAX && batch <= 65535;
+  // 32-bit buffer offsets: a few rows of d_inner fp32 values, 64 chunks' tokens of B/C rows
+  return L <= INT32_MAX && batch <= 65535 && d_inner <= (1 << 24);
 }
 
 template <class T, int K, bool CONV, bool SP>

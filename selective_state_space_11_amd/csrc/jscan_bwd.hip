@@ -26,9 +26,9 @@
 //    chunk's delta sum give the (decay, offset) pair of the chunk.
 // 3. k_adj_combine folds the pairs from the last chunk down, seeded with
 //    dhT, giving the adjoint that enters each chunk from the later ones.
-// 4. k_bwd, per (chunk, 64 channels): a forward sweep from the chunk's
+// 4. Per (chunk, 64 channels): a forward sweep (k_bwd_fwd) from the chunk's
 //    starting state writes dz, the dC partial sums and a state checkpoint
-//    every kTok tokens; a reverse sweep then takes the chunk's pieces of kTok
+//    every kTok tokens; a reverse sweep (k_bwd_rev) takes the chunk's pieces of kTok
 //    tokens from the last: it recomputes the piece's states from its
 //    checkpoint (kept in registers) and steps the adjoint back through the
 //    piece, writing dx, ddelta and the dB partial sums and accumulating
@@ -56,6 +56,25 @@ namespace {
 using namespace jscan_detail;
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int PC = 4;    // tokens whose states the reverse sweep holds in registers at once
+static_assert(kTok % PC == 0, "a checkpointed block splits into whole pieces");
+
+// A copy of v the compiler cannot see through.  Recomputed decays would
+// otherwise be merged with earlier identical ones and held in registers
+// across the whole block, which costs more occupancy than the recompute.
+__device__ __forceinline__ float opaque(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// A wave-uniform pointer the compiler cannot see through: B rows read again
+// in the reverse step are then loaded again into SGPRs instead of being kept
+// (widened, in VGPRs) from the recompute.
+template <class T>
+__device__ __forceinline__ const T* opaque_ptr(const T* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -218,31 +237,55 @@ __global__ __launch_bounds__(256) void k_adj_combine(const float* __restrict__ A
 }
 
 // ------------------------------------------------------------ main backward
-// Grid: (d_inner / 64 groups, chunks, batch); one wave per block.  See the
-// file header for the two sweeps.  Padding tokens of a partial last block
-// read delta = 0 and dy = 0 (empty buffer resource): they change neither the
-// state nor the adjoint, and their outputs are not stored.  Lanes clamped
-// onto the last channel contribute zero to the channel sums.
-template <class T>
-__global__ __launch_bounds__(64) void k_bwd(
-    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dw, const T* __restrict__ z,
-    const T* __restrict__ dy, const float* __restrict__ hinit, const float* __restrict__ Min,
-    const float* __restrict__ dhT, T* __restrict__ dx, T* __restrict__ ddelta, T* __restrict__ dz,
-    float* __restrict__ dBp, float* __restrict__ dCp, float* __restrict__ dAp, float* __restrict__ dDp,
-    float* __restrict__ dh0, float* __restrict__ ck, int64_t L, int64_t d_inner, int64_t chunk_len,
-    int n_chunks) {
-  const int lane = threadIdx.x;
-  const int64_t g = blockIdx.x;
-  const int64_t G = gridDim.x;
-  const int64_t gbase = g * 64;
-  const int c = blockIdx.y;
-  const int64_t b = blockIdx.z;
-  const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
-  const int64_t d = gbase + lo;
-  const float lf = lo == lane ? 1.0f : 0.0f;
+// Grid: (d_inner / 64 groups, chunks, batch); one wave per block.  The two
+// sweeps over a chunk are separate kernels so that each gets its own
+// register budget.  Padding tokens of a partial last block read delta = 0
+// and dy = 0 (empty buffer resource): they change neither the state nor the
+// adjoint, and their outputs are not stored.  Lanes clamped onto the last
+// channel contribute zero to the channel sums.
+struct BwdArgs {
+  const void* x; const void* delta; const float* A; const void* B; const void* C; const float* D;
+  const void* z; const void* dy;
+  const float* hinit;     // hstart[b][c][n][d] (chunked) or h0[b][d][n] (single chunk), may be null
+  const float* Min;       // slot c + 1 = adjoint entering chunk c (chunked plans)
+  const float* dhT;
+  void* dx; void* ddelta; void* dz;
+  float* dBp; float* dCp;  // [b][group][L][16] partial channel sums
+  float* dAp; float* dDp;  // [b][chunk][16][d] and [b][chunk][d] partial token sums
+  float* dh0;
+  float* ck;               // [b][chunk][piece][16][d] states before each kTok-token piece
+  int64_t L, d_inner, chunk_len;
+  int n_chunks;
+};
 
-  float a2[NSTATE], h[NSTATE];
+// Per-wave coordinates shared by the two sweeps.
+struct WaveTile {
+  int lane, lo, c, nt, last;
+  int64_t g, G, gbase, b, d, t0, row0, pieces;
+  float lf;
+  uint32_t lb, rowb;
+  template <class T>
+  __device__ __forceinline__ void init(const BwdArgs& a) {
+    lane = threadIdx.x;
+    g = blockIdx.x;
+    G = gridDim.x;
+    gbase = g * 64;
+    c = blockIdx.y;
+    b = blockIdx.z;
+    lo = (int)std::min<int64_t>(lane, a.d_inner - 1 - gbase);
+    d = gbase + lo;
+    lf = lo == lane ? 1.0f : 0.0f;
+    t0 = (int64_t)c * a.chunk_len;
+    nt = (int)std::min<int64_t>(a.chunk_len, a.L - t0);
+    last = (nt - 1) / kTok * kTok;
+    row0 = (b * a.L + t0) * a.d_inner + gbase;
+    pieces = (a.chunk_len + kTok - 1) / kTok;
+    lb = (uint32_t)lo * sizeof(T);
+    rowb = (uint32_t)(a.d_inner * sizeof(T));
+  }
+};
+
+__device__ __forceinline__ void load_a2(float (&a2)[NSTATE], const float* A, int64_t d) {
   const float4* Ap = reinterpret_cast<const float4*>(A + d * NSTATE);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -250,178 +293,234 @@ __global__ __launch_bounds__(64) void k_bwd(
     a2[4 * q + 0] = v.x * kLog2e; a2[4 * q + 1] = v.y * kLog2e;
     a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
   }
-  if (n_chunks > 1) {
-    const float* hi = hinit + ((b * n_chunks + c) * NSTATE) * d_inner + d;
+}
+
+// kTok tokens of the four per-channel streams from block start bb (rows past
+// the chunk clamped onto its last token; their delta and dy read 0).
+template <class T, int NS>
+__device__ __forceinline__ void load_streams(const WaveTile& w, const T* const (&rows)[NS], int bb,
+                                             T (&v)[NS][kTok], int delta_slot, int dy_slot,
+                                             int64_t d_inner) {
+  const int64_t o = (int64_t)bb * d_inner;
+  const auto r0 = rsrc(rows[0], 0);
 #pragma unroll
-    for (int n = 0; n < NSTATE; ++n) h[n] = hi[(int64_t)n * d_inner];
+  for (int k = 0; k < NS; ++k) {
+    const auto r = rsrc(rows[k] + o);
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+      const bool real = bb + j < w.nt;
+      const uint32_t so = (uint32_t)(std::min(bb + j, w.nt - 1) - bb) * w.rowb;
+      buf_load(v[k][j], ((k == delta_slot || k == dy_slot) && !real) ? r0 : r, w.lb, so);
+    }
+  }
+}
+
+// Forward sweep from the chunk's starting state: checkpoints, dz, dC
+// partials, dD partial.
+template <class T>
+__global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__ Bm, const T* __restrict__ Cm) {
+  WaveTile w;
+  w.init<T>(a);
+  float a2[NSTATE], h[NSTATE];
+  load_a2(a2, a.A, w.d);
+  if (a.n_chunks > 1) {
+    const float* hi = a.hinit + ((w.b * a.n_chunks + w.c) * NSTATE) * a.d_inner + w.d;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) h[n] = hi[(int64_t)n * a.d_inner];
   } else {
-    const float* hi = hinit ? hinit + (b * d_inner + d) * NSTATE : nullptr;
+    const float* hi = a.hinit ? a.hinit + (w.b * a.d_inner + w.d) * NSTATE : nullptr;
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) h[n] = hi ? hi[n] : 0.0f;
   }
-  const float Dd = Dw[d];
+  const float Dd = a.D[w.d];
+  const T* const rows[4] = {static_cast<const T*>(a.delta) + w.row0, static_cast<const T*>(a.x) + w.row0,
+                            static_cast<const T*>(a.z) + w.row0, static_cast<const T*>(a.dy) + w.row0};
+  T* dzrow = static_cast<T*>(a.dz) + w.row0;
+  // B and C rows through the kernel's own restrict parameters, so that they
+  // are read with scalar loads
+  const T* brow = Bm + (w.b * a.L + w.t0) * NSTATE;
+  const T* crow = Cm + (w.b * a.L + w.t0) * NSTATE;
+  // checkpoints and partial sums through buffer instructions: wave-uniform
+  // bases, the lane's byte offset and a row offset
+  const float* ckb = a.ck + ((w.b * a.n_chunks + w.c) * w.pieces * NSTATE) * a.d_inner + w.gbase;
+  float* dcb = a.dCp + ((w.b * w.G + w.g) * a.L + w.t0) * NSTATE;
+  const uint32_t lb4 = (uint32_t)w.lo * 4, qoff = (uint32_t)(w.lane >> 2) * 4;
+  const uint32_t nrow4 = (uint32_t)(a.d_inner * 4);
 
-  const int64_t t0 = (int64_t)c * chunk_len;
-  const int nt = (int)std::min<int64_t>(chunk_len, L - t0);
-  const int64_t row0 = (b * L + t0) * d_inner + gbase;
-  const T* xrow = x + row0;
-  const T* drow = delta + row0;
-  const T* zrow = z + row0;
-  const T* grow = dy + row0;
-  T* dxrow = dx + row0;
-  T* ddrow = ddelta + row0;
-  T* dzrow = dz + row0;
-  const T* brow = Bm + (b * L + t0) * NSTATE;
-  const T* crow = Cm + (b * L + t0) * NSTATE;
-  const int64_t pieces = (chunk_len + kTok - 1) / kTok;
-  float* ckp = ck + ((b * n_chunks + c) * pieces * NSTATE) * d_inner + d;
-  float* dbp = dBp + ((b * G + g) * L + t0) * NSTATE + (lane >> 2);
-  float* dcp = dCp + ((b * G + g) * L + t0) * NSTATE + (lane >> 2);
-  const uint32_t lb = (uint32_t)lo * sizeof(T);
-  const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
-  const int last = (nt - 1) / kTok * kTok;
-
-  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&gg)[kTok]) {
-    const int64_t o = (int64_t)bb * d_inner;
-    const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), rg = rsrc(grow + o);
-    const auto r0 = rsrc(drow, 0);
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-      const bool real = bb + j < nt;
-      const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
-      buf_load(dd[j], real ? rd : r0, lb, so);
-      buf_load(xx[j], rx, lb, so);
-      buf_load(zz[j], rz, lb, so);
-      buf_load(gg[j], real ? rg : r0, lb, so);
-    }
-  };
-
-  // ---- forward sweep: dz, dC partials, checkpoints, dD
   float dD = 0.0f;
   Row<T, NSTATE> Bc, Bn, Cv;
-  auto fwd_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
-                       const T (&gg)[kTok]) {
-    float* cp = ckp + (int64_t)(bb / kTok) * NSTATE * d_inner;
+  auto block = [&](int bb, const T (&v)[4][kTok]) {
+    const auto rck = rsrc(ckb + (int64_t)(bb / kTok) * NSTATE * a.d_inner);
 #pragma unroll
-    for (int n = 0; n < NSTATE; ++n) cp[(int64_t)n * d_inner] = h[n];     // state before token bb
-    const auto rz = rsrc(dzrow + (int64_t)bb * d_inner);
+    for (int n = 0; n < NSTATE; ++n) buf_store(h[n], rck, lb4, (uint32_t)n * nrow4);   // state before token bb
+    const auto rz = rsrc(dzrow + (int64_t)bb * a.d_inner);
+    const auto rdc = rsrc(dcb + (int64_t)bb * NSTATE);
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-      Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
-      Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
-      const float dt = widen(dd[j]), xv = widen(xx[j]);
+      Cv.load(crow + (int64_t)std::min(bb + j, w.nt - 1) * NSTATE);
+      Bn.load(brow + (int64_t)std::min(bb + j + 1, w.nt - 1) * NSTATE);
+      const float dt = widen(v[0][j]), xv = widen(v[1][j]);
       const float dxv = dt * xv;
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Bc[n]);
       float acc = 0.0f;
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) acc = fmaf(Cv[n], h[n], acc);
-      const float zv = widen(zz[j]), gv = widen(gg[j]);
+      const float zv = widen(v[2][j]), gv = widen(v[3][j]);
       const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
       const float sl = zv * sg;
       const float dp = gv * sl;
       const float p = fmaf(Dd, xv, acc);
       dD = fmaf(dp, xv, dD);
-      float v[NSTATE];
-      const float dpl = dp * lf;
+      float u[NSTATE];
+      const float dpl = dp * w.lf;
 #pragma unroll
-      for (int n = 0; n < NSTATE; ++n) v[n] = dpl * h[n];
-      const float sum = wave_sum16(v, lane);
-      if (bb + j < nt) {
-        buf_store(to_io(gv * p * sg * (1.0f + zv - sl), T()), rz, lb, (uint32_t)j * rowb);
-        if ((lane & 3) == 0) dcp[(int64_t)(bb + j) * NSTATE] = sum;
+      for (int n = 0; n < NSTATE; ++n) u[n] = dpl * h[n];
+      const float sum = wave_sum16(u, w.lane);
+      if (bb + j < w.nt) {
+        buf_store(to_io(gv * p * sg * (1.0f + zv - sl), T()), rz, w.lb, (uint32_t)j * w.rowb);
+        if ((w.lane & 3) == 0) buf_store(sum, rdc, qoff, (uint32_t)j * NSTATE * 4);
       }
       Bc = Bn;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  {
-    T dA_[kTok], xA[kTok], zA[kTok], gA[kTok], dB_[kTok], xB[kTok], zB[kTok], gB[kTok];
-    load_block(0, dA_, xA, zA, gA);
-    Bc.load(brow);
-    __builtin_amdgcn_s_waitcnt(0);
-    for (int base = 0; base < nt; base += 2 * kTok) {
-      load_block(std::min(base + kTok, last), dB_, xB, zB, gB);
-      fwd_block(base, dA_, xA, zA, gA);
-      if (base + kTok >= nt) break;
-      load_block(std::min(base + 2 * kTok, last), dA_, xA, zA, gA);
-      fwd_block(base + kTok, dB_, xB, zB, gB);
-    }
+  T vA[4][kTok], vB[4][kTok];
+  load_streams(w, rows, 0, vA, 0, 3, a.d_inner);
+  Bc.load(brow);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int base = 0; base < w.nt; base += 2 * kTok) {
+    load_streams(w, rows, std::min(base + kTok, w.last), vB, 0, 3, a.d_inner);
+    block(base, vA);
+    if (base + kTok >= w.nt) break;
+    load_streams(w, rows, std::min(base + 2 * kTok, w.last), vA, 0, 3, a.d_inner);
+    block(base + kTok, vB);
   }
+  if (w.lo == w.lane) a.dDp[(w.b * a.n_chunks + w.c) * a.d_inner + w.d] = dD;
+}
 
-  // ---- reverse sweep: dx, ddelta, dB partials, dA
+// Reverse sweep over the checkpointed blocks from the last, each as pieces of
+// PC tokens from the last: a piece's states are recomputed from the block's
+// checkpoint into registers, then the adjoint steps back through the piece.
+// dx, ddelta, dB partials, dA partial, dh0.
+template <class T>
+__global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__ Bm, const T* __restrict__ Cm) {
+  WaveTile w;
+  w.init<T>(a);
+  float a2[NSTATE];
+  load_a2(a2, a.A, w.d);
+  const float Dd = a.D[w.d];
+  const T* const rows[4] = {static_cast<const T*>(a.delta) + w.row0, static_cast<const T*>(a.x) + w.row0,
+                            static_cast<const T*>(a.z) + w.row0, static_cast<const T*>(a.dy) + w.row0};
+  T* dxrow = static_cast<T*>(a.dx) + w.row0;
+  T* ddrow = static_cast<T*>(a.ddelta) + w.row0;
+  // B and C rows through the kernel's own restrict parameters, so that they
+  // are read with scalar loads
+  const T* brow = Bm + (w.b * a.L + w.t0) * NSTATE;
+  const T* crow = Cm + (w.b * a.L + w.t0) * NSTATE;
+  const float* ckb = a.ck + ((w.b * a.n_chunks + w.c) * w.pieces * NSTATE) * a.d_inner + w.gbase;
+  float* dbb = a.dBp + ((w.b * w.G + w.g) * a.L + w.t0) * NSTATE;
+  const uint32_t lb4 = (uint32_t)w.lo * 4, qoff = (uint32_t)(w.lane >> 2) * 4;
+  const uint32_t nrow4 = (uint32_t)(a.d_inner * 4);
+
   float mu[NSTATE], dA[NSTATE];
-  if (c == n_chunks - 1) {
-    const float* mi = dhT ? dhT + (b * d_inner + d) * NSTATE : nullptr;
+  if (w.c == a.n_chunks - 1) {
+    const float* mi = a.dhT ? a.dhT + (w.b * a.d_inner + w.d) * NSTATE : nullptr;
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) mu[n] = mi ? mi[n] : 0.0f;
   } else {
-    const float* mi = Min + ((b * n_chunks + c + 1) * NSTATE) * d_inner + d;
+    const float* mi = a.Min + ((w.b * a.n_chunks + w.c + 1) * NSTATE) * a.d_inner + w.d;
 #pragma unroll
-    for (int n = 0; n < NSTATE; ++n) mu[n] = mi[(int64_t)n * d_inner];
+    for (int n = 0; n < NSTATE; ++n) mu[n] = mi[(int64_t)n * a.d_inner];
+  }
+  __shared__ float dA_lds[64 * NSTATE];
+#pragma unroll
+  for (int n = 0; n < NSTATE; ++n) dA_lds[w.lane * NSTATE + n] = 0.0f;
+  Row<T, NSTATE> Br, Cv;
+  for (int pb = w.last; pb >= 0; pb -= kTok) {
+    T v[4][kTok];
+    load_streams(w, rows, pb, v, 0, 3, a.d_inner);
+    float dps[kTok];                   // dp = dy SiLU(z), so z and dy need not stay live
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) dps[j] = widen(v[3][j]) * silu(widen(v[2][j]));
+    const auto rck = rsrc(ckb + (int64_t)(pb / kTok) * NSTATE * a.d_inner);
+    const auto rdb = rsrc(dbb + (int64_t)pb * NSTATE);
+    const auto rx = rsrc(dxrow + (int64_t)pb * a.d_inner), rd = rsrc(ddrow + (int64_t)pb * a.d_inner);
+    // The block's two halves, later half first.  Each recomputes its states
+    // from the block's checkpoint, keeping only its own PC tokens' states.
+#pragma unroll
+    for (int hb = kTok - PC; hb >= 0; hb -= PC) {
+      float h[NSTATE];
+      // re-read the checkpoint for every piece rather than hold it in registers
+      uint32_t lbh = lb4;
+      asm volatile("" : "+v"(lbh));
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) buf_load(h[n], rck, lbh, (uint32_t)n * nrow4);
+      float hp[PC][NSTATE];            // states before each token of the half
+      float dAh[NSTATE];
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) dAh[n] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < hb + PC; ++j) {
+        Br.load(brow + (int64_t)std::min(pb + j, w.nt - 1) * NSTATE);
+        const float dt = opaque(widen(v[0][j]));
+        const float dxv = dt * widen(v[1][j]);
+#pragma unroll
+        for (int n = 0; n < NSTATE; ++n) {
+          if (j >= hb) hp[j - hb][n] = h[n];
+          if (j + 1 < hb + PC) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Br[n]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = hb + PC - 1; j >= hb; --j) {
+        Br.load(brow + (int64_t)std::min(pb + j, w.nt - 1) * NSTATE);
+        Cv.load(crow + (int64_t)std::min(pb + j, w.nt - 1) * NSTATE);
+        const float dt = opaque(widen(v[0][j])), xv = widen(v[1][j]);
+        const float dp = dps[j];
+        const float dxl = dt * xv * w.lf;
+        float sLB = 0.0f, sAW = 0.0f, u[NSTATE];
+#pragma unroll
+        for (int n = 0; n < NSTATE; ++n) {
+          const float lam = fmaf(dp, Cv[n], mu[n]);
+          sLB = fmaf(lam, Br[n], sLB);
+          const float m = fast_exp2(dt * a2[n]) * lam;
+          mu[n] = m;
+          const float wv = m * hp[j - hb][n];
+          sAW = fmaf(a2[n], wv, sAW);
+          dAh[n] = fmaf(dt, wv, dAh[n]);
+          u[n] = lam * dxl;
+        }
+        const float sum = wave_sum16(u, w.lane);
+        if (pb + j < w.nt) {
+          const uint32_t so = (uint32_t)j * w.rowb;
+          buf_store(to_io(fmaf(Dd, dp, dt * sLB), T()), rx, w.lb, so);
+          buf_store(to_io(fmaf(xv, sLB, kLn2 * sAW), T()), rd, w.lb, so);
+          if ((w.lane & 3) == 0) buf_store(sum, rdb, qoff, (uint32_t)j * NSTATE * 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // dA is carried in LDS: a register accumulator live across the block
+      // loop costs the kernel about a hundred VGPRs (and an occupancy step)
+      float4* acc = reinterpret_cast<float4*>(&dA_lds[w.lane * NSTATE]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 t = acc[q];
+        t.x += dAh[4 * q]; t.y += dAh[4 * q + 1]; t.z += dAh[4 * q + 2]; t.w += dAh[4 * q + 3];
+        acc[q] = t;
+      }
+    }
   }
 #pragma unroll
-  for (int n = 0; n < NSTATE; ++n) dA[n] = 0.0f;
-  Row<T, NSTATE> Br;
-  for (int pb = last; pb >= 0; pb -= kTok) {
-    T dd[kTok], xx[kTok], zz[kTok], gg[kTok];
-    load_block(pb, dd, xx, zz, gg);
-    const float* cp = ckp + (int64_t)(pb / kTok) * NSTATE * d_inner;
+  for (int n = 0; n < NSTATE; ++n) dA[n] = dA_lds[w.lane * NSTATE + n];
+  if (w.lo == w.lane) {
+    if (w.c == 0 && a.dh0) {
 #pragma unroll
-    for (int n = 0; n < NSTATE; ++n) h[n] = cp[(int64_t)n * d_inner];
-    // states before each token of the piece
-    float hp[kTok][NSTATE];
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-      Br.load(brow + (int64_t)std::min(pb + j, nt - 1) * NSTATE);
-      const float dt = widen(dd[j]);
-      const float dxv = dt * widen(xx[j]);
-#pragma unroll
-      for (int n = 0; n < NSTATE; ++n) {
-        hp[j][n] = h[n];
-        h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Br[n]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int n = 0; n < NSTATE; ++n) a.dh0[(w.b * a.d_inner + w.d) * NSTATE + n] = mu[n];
     }
-    const auto rx = rsrc(dxrow + (int64_t)pb * d_inner), rd = rsrc(ddrow + (int64_t)pb * d_inner);
+    const int64_t slot = w.b * a.n_chunks + w.c;
 #pragma unroll
-    for (int j = kTok - 1; j >= 0; --j) {
-      Br.load(brow + (int64_t)std::min(pb + j, nt - 1) * NSTATE);
-      Cv.load(crow + (int64_t)std::min(pb + j, nt - 1) * NSTATE);
-      const float dt = widen(dd[j]), xv = widen(xx[j]), zv = widen(zz[j]), gv = widen(gg[j]);
-      const float dp = gv * silu(zv);
-      const float dxl = dt * xv * lf;
-      float sLB = 0.0f, sAW = 0.0f, u[NSTATE];
-#pragma unroll
-      for (int n = 0; n < NSTATE; ++n) {
-        const float lam = fmaf(dp, Cv[n], mu[n]);
-        sLB = fmaf(lam, Br[n], sLB);
-        const float m = fast_exp2(dt * a2[n]) * lam;
-        mu[n] = m;
-        const float w = m * hp[j][n];
-        sAW = fmaf(a2[n], w, sAW);
-        dA[n] = fmaf(dt, w, dA[n]);
-        u[n] = lam * dxl;
-      }
-      const float sum = wave_sum16(u, lane);
-      if (pb + j < nt) {
-        const uint32_t so = (uint32_t)j * rowb;
-        buf_store(to_io(fmaf(Dd, dp, dt * sLB), T()), rx, lb, so);
-        buf_store(to_io(fmaf(xv, sLB, kLn2 * sAW), T()), rd, lb, so);
-        if ((lane & 3) == 0) dbp[(int64_t)(pb + j) * NSTATE] = sum;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  if (lo == lane) {
-    if (c == 0 && dh0) {
-#pragma unroll
-      for (int n = 0; n < NSTATE; ++n) dh0[(b * d_inner + d) * NSTATE + n] = mu[n];
-    }
-    const int64_t slot = b * n_chunks + c;
-#pragma unroll
-    for (int n = 0; n < NSTATE; ++n) dAp[(slot * NSTATE + n) * d_inner + d] = dA[n];
-    dDp[slot * d_inner + d] = dD;
+    for (int n = 0; n < NSTATE; ++n) a.dAp[(slot * NSTATE + n) * a.d_inner + w.d] = dA[n];
   }
 }
 
@@ -525,13 +624,13 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
     hipLaunchKernelGGL(k_adj_combine, g2, dim3(256), 0, st, A, dsum, dhT, M, d_inner, p.chunks);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "adjoint combine launch");
   }
+  const BwdArgs args{x, delta, A, B, C, D, z, dy, p.chunks > 1 ? hstart : h0, M, dhT, dx, ddelta, dz, dBp, dCp,
+                     dAp, dDp, dh0, ck, L, d_inner, p.chunk_len, p.chunks};
   dim3 g3((unsigned)G, (unsigned)p.chunks, (unsigned)batch);
-  hipLaunchKernelGGL((k_bwd<T>), g3, dim3(64), 0, st, static_cast<const T*>(x), static_cast<const T*>(delta), A,
-                     static_cast<const T*>(B), static_cast<const T*>(C), D, static_cast<const T*>(z),
-                     static_cast<const T*>(dy), p.chunks > 1 ? hstart : h0, M, dhT, static_cast<T*>(dx),
-                     static_cast<T*>(ddelta), static_cast<T*>(dz), dBp, dCp, dAp, dDp, dh0, ck, L, d_inner,
-                     p.chunk_len, p.chunks);
-  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "backward launch");
+  hipLaunchKernelGGL((k_bwd_fwd<T>), g3, dim3(64), 0, st, args, static_cast<const T*>(B), static_cast<const T*>(C));
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "backward forward-sweep launch");
+  hipLaunchKernelGGL((k_bwd_rev<T>), g3, dim3(64), 0, st, args, static_cast<const T*>(B), static_cast<const T*>(C));
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "backward reverse-sweep launch");
   dim3 g4((unsigned)((L * NSTATE + 255) / 256), (unsigned)batch);
   hipLaunchKernelGGL(k_reduce_bc, g4, dim3(256), 0, st, dBp, dCp, dB, dC, L, G);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dB/dC reduce launch");
