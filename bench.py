@@ -6,7 +6,9 @@ d_state 16, bf16 I/O (fp32 state and arithmetic), inputs resident in HBM.
 Reports channel-tokens/s (batch * L * d_inner per second), the fraction of the
 MI355X HBM roofline those algorithmic bytes reach, the roofline of the main
 scan kernel (timed on its own with HIP events recorded by the library on the
-launch stream), a decode-step measurement (256 sequences), and the fp64 CPU
+launch stream), a decode-step measurement (256 sequences), the same prefill
+with the fused input prologue (causal conv of width 4 + SiLU, softplus time
+step), the backward (gradient) scan of the same prefill, and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
@@ -78,7 +80,7 @@ def _db_rows(db, sql):
 
 
 def _short(name):
-    base = name.replace("(anonymous namespace)::", "")
+    base = name.replace("(anonymous namespace)::", "").replace("jscan_detail::", "")
     if base.startswith("void "):
         base = base[5:]
     return base.split("(")[0].strip()
@@ -129,7 +131,8 @@ def summarize_traffic(pmc_dir, out_md, out_json, command):
         res[k] = r + w
         lines.append(f"| {k} | {r / 1e6:.1f} | {w / 1e6:.1f} | {(r + w) / 1e6:.1f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
-    data = {"k_scan_64k": {"source_sha": source_digest(), "hbm_bytes_per_launch": res.get("k_scan<unsigned short, 1>"),
+    data = {"k_scan_64k": {"source_sha": source_digest(),
+                           "hbm_bytes_per_launch": res.get("k_scan<unsigned short, 1, false, false>"),
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     json.dump(data, open(out_json, "w"), indent=1)
     return res
@@ -191,6 +194,16 @@ def run_all_configs(log):
         ms = timed(lambda: js.prefill(x, dl, A, B, C, D, z, None, y=y, hT=hT, workspace=ws), 10)
         emit(name, batch * L * 8192, ms, alg_bytes_prefill(batch, L, 8192), cpu_rate(inp, 256),
              {"plan": js.plan(batch, L, 8192)})
+        if L <= 65536:
+            dy_np, dhT_np = synth.output_grads(batch, L, 8192, seed=seed)
+            dy, dhT = dio(dy_np), dio(dhT_np)
+            del dy_np
+            bws = torch.empty(js.backward_workspace_size(batch, L, 8192), dtype=torch.uint8, device=dev)
+            g = js.backward(x, dl, A, B, C, D, z, dy, None, dhT, workspace=bws)
+            bms = timed(lambda: js.backward(x, dl, A, B, C, D, z, dy, None, dhT, workspace=bws, out=g), 5)
+            emit("backward of " + name, batch * L * 8192, bms, alg_bytes_prefill(batch, L, 8192) * 2, None,
+                 {"over_forward": round(bms / ms, 3)})
+            del g, bws, dy
         if L == 262144:
             state = torch.zeros(1, 8192, 16, device=dev)
             ws2 = torch.empty(max(1, js.workspace_size(1, 4096, 8192)), dtype=torch.uint8, device=dev)
@@ -254,6 +267,7 @@ def main():
     ap.add_argument("--L", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--backward-steps", type=int, default=5, help="timed backward calls (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (read) to 1 GiB (write), --steps times, "
                          "to calibrate HBM byte counters")
@@ -385,6 +399,52 @@ def main():
               "note": "the 128 MiB state can stay resident in the 256 MB last-level cache"}
     log(f"[bench] decode {us_step:.2f} us/step")
 
+    # the same prefill with the fused input prologue (conv width 4 + SiLU, softplus(delta + dt_bias))
+    pro = synth.prologue_params(d_inner, 4, seed=2)
+    cw, cb, cs, dtb = (torch.from_numpy(pro[k]).to(dev) for k in ("conv_weight", "conv_bias", "conv_state",
+                                                                  "dt_bias"))
+    cso = torch.empty_like(cs)
+
+    def fused_step():
+        js.prefill_fused(x, delta, A, B, C, D, z, None, y=y, hT=hT, workspace=ws, conv_weight=cw, conv_bias=cb,
+                         conv_state_in=cs, conv_state_out=cso, dt_bias=dtb, softplus=True)
+    for _ in range(2):
+        fused_step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        fused_step()
+    e1.record()
+    torch.cuda.synchronize()
+    fused_ms = e0.elapsed_time(e1) / args.steps
+    fused = {"workload": "the same prefill with the input prologue fused (causal depthwise conv width 4 + SiLU "
+                         "on x, softplus(delta + dt_bias))",
+             "ms_per_step": round(fused_ms, 4), "channel_tokens_per_s": chtok / (fused_ms * 1e-3)}
+    log(f"[bench] fused prologue prefill {fused_ms:.4f} ms")
+
+    # backward of the same prefill, output gradients dy ~ N(0,1), dhT ~ N(0,1)
+    backward = None
+    if args.backward_steps > 0:
+        dy_np, dhT_np = synth.output_grads(batch, L, d_inner, seed=2)
+        dy = dio(dy_np)
+        del dy_np
+        dhT = torch.from_numpy(dhT_np).to(dev)
+        bws = torch.empty(js.backward_workspace_size(batch, L, d_inner), dtype=torch.uint8, device=dev)
+        grads = js.backward(x, delta, A, B, C, D, z, dy, None, dhT, workspace=bws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.backward_steps):
+            js.backward(x, delta, A, B, C, D, z, dy, None, dhT, workspace=bws, out=grads)
+        e1.record()
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / args.backward_steps
+        backward = {"workload": "gradients of the same prefill (dx, ddelta, dz, dA, dB, dC, dD, dh0)",
+                    "ms_per_step": round(bwd_ms, 4), "channel_tokens_per_s": chtok / (bwd_ms * 1e-3),
+                    "over_forward": round(bwd_ms / ms_per_step, 3),
+                    "workspace_GiB": round(bws.numel() / 2 ** 30, 2)}
+        log(f"[bench] backward {bwd_ms:.4f} ms")
+        del grads, bws, dy
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -426,6 +486,8 @@ def main():
                      "work": f"{SLOTS_PER_CHTOK} fp32 VALU slots (x2 flop) per channel-token, "
                              f"{chtok} channel-tokens per launch"},
         "decode": decode,
+        "prefill_fused_prologue": fused,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
