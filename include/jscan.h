@@ -177,7 +177,8 @@ jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_st
 
 /*
  * Backward (gradient) of jscan_prefill, for training.  The pages describe
- * training Jamba (paper notes, section 3.3 on the training framework) but
+ * training Jamba ("Jamba: A Hybrid Transformer-Mamba Language Model — 深度解读
+ * 报告", section 3.3 on the training infrastructure) but
  * give no backward; this is the reverse-mode derivative of the recurrence
  * above.  Given the forward's inputs and the gradients of a scalar loss with
  * respect to its outputs,

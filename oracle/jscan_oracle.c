@@ -202,12 +202,12 @@ void oracle_prologue(int64_t batch, int64_t L, int64_t d_inner, int64_t width,
 /*
  * Backward (gradient) of the prefill, for training (test infrastructure, same
  * caveats as above).  The pages name training with sequence and tensor
- * parallelism ("AI Engineering from Scratch" Jamba paper notes, section 3.3 on
- * the training framework) but give no backward; this is the reverse-mode
- * derivative of the recurrence defined at the top of this file, taken by hand
- * (adjoint method), for a scalar loss whose gradients with respect to the
- * outputs are dy [batch][L][d_inner] and dhT [batch][d_inner][d_state]
- * (dhT NULL: zero).
+ * parallelism ("Jamba: A Hybrid Transformer-Mamba Language Model — 深度解读
+ * 报告", section 3.3 on the training infrastructure) but give no backward;
+ * this is the reverse-mode derivative of the recurrence defined at the top of
+ * this file, taken by hand (adjoint method), for a scalar loss whose
+ * gradients with respect to the outputs are dy [batch][L][d_inner] and dhT
+ * [batch][d_inner][d_state] (dhT NULL: zero).
  *
  * Per (b, d), with the forward states h_t (h_{-1} = h0), decays
  * a_tn = exp(dt_t A_n), pre-gate output p_t = sum_n C_tn h_tn + D xv_t and
