@@ -28,8 +28,8 @@
 //    dhT, giving the adjoint that enters each chunk from the later ones.
 // 4. Per (chunk, 64 channels): a forward sweep (k_bwd_fwd) from the chunk's
 //    starting state writes dz, the dC partial sums and a state checkpoint
-//    every kTok tokens; a reverse sweep (k_bwd_rev) takes the chunk's pieces of kTok
-//    tokens from the last: it recomputes the piece's states from its
+//    every PC tokens; a reverse sweep (k_bwd_rev) takes the chunk's pieces of
+//    PC tokens from the last: it recomputes the piece's states from its
 //    checkpoint (kept in registers) and steps the adjoint back through the
 //    piece, writing dx, ddelta and the dB partial sums and accumulating
 //    dA and dD.
@@ -56,7 +56,7 @@ namespace {
 using namespace jscan_detail;
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int PC = 4;    // tokens whose states the reverse sweep holds in registers at once
+constexpr int PC = 4;    // checkpoint interval: tokens whose states the reverse sweep holds in registers
 static_assert(kTok % PC == 0, "a checkpointed block splits into whole pieces");
 
 // A copy of v the compiler cannot see through.  Recomputed decays would
@@ -279,7 +279,7 @@ struct WaveTile {
     nt = (int)std::min<int64_t>(a.chunk_len, a.L - t0);
     last = (nt - 1) / kTok * kTok;
     row0 = (b * a.L + t0) * a.d_inner + gbase;
-    pieces = (a.chunk_len + kTok - 1) / kTok;
+    pieces = (a.chunk_len + PC - 1) / PC;
     lb = (uint32_t)lo * sizeof(T);
     rowb = (uint32_t)(a.d_inner * sizeof(T));
   }
@@ -350,13 +350,15 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
   float dD = 0.0f;
   Row<T, NSTATE> Bc, Bn, Cv;
   auto block = [&](int bb, const T (&v)[4][kTok]) {
-    const auto rck = rsrc(ckb + (int64_t)(bb / kTok) * NSTATE * a.d_inner);
-#pragma unroll
-    for (int n = 0; n < NSTATE; ++n) buf_store(h[n], rck, lb4, (uint32_t)n * nrow4);   // state before token bb
     const auto rz = rsrc(dzrow + (int64_t)bb * a.d_inner);
     const auto rdc = rsrc(dcb + (int64_t)bb * NSTATE);
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
+      if (j % PC == 0 && bb + j < w.nt) {          // checkpoint: the state before token bb + j
+        const auto rck = rsrc(ckb + (int64_t)((bb + j) / PC) * NSTATE * a.d_inner);
+#pragma unroll
+        for (int n = 0; n < NSTATE; ++n) buf_store(h[n], rck, lb4, (uint32_t)n * nrow4);
+      }
       Cv.load(crow + (int64_t)std::min(bb + j, w.nt - 1) * NSTATE);
       Bn.load(brow + (int64_t)std::min(bb + j + 1, w.nt - 1) * NSTATE);
       const float dt = widen(v[0][j]), xv = widen(v[1][j]);
@@ -385,23 +387,20 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  T vA[4][kTok], vB[4][kTok];
-  load_streams(w, rows, 0, vA, 0, 3, a.d_inner);
+  // One register set: without a second one in flight the kernel fits five
+  // waves per SIMD (90 VGPRs instead of 131), which hide the block loads.
   Bc.load(brow);
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int base = 0; base < w.nt; base += 2 * kTok) {
-    load_streams(w, rows, std::min(base + kTok, w.last), vB, 0, 3, a.d_inner);
-    block(base, vA);
-    if (base + kTok >= w.nt) break;
-    load_streams(w, rows, std::min(base + 2 * kTok, w.last), vA, 0, 3, a.d_inner);
-    block(base + kTok, vB);
+  for (int base = 0; base < w.nt; base += kTok) {
+    T v[4][kTok];
+    load_streams(w, rows, base, v, 0, 3, a.d_inner);
+    block(base, v);
   }
   if (w.lo == w.lane) a.dDp[(w.b * a.n_chunks + w.c) * a.d_inner + w.d] = dD;
 }
 
-// Reverse sweep over the checkpointed blocks from the last, each as pieces of
-// PC tokens from the last: a piece's states are recomputed from the block's
-// checkpoint into registers, then the adjoint steps back through the piece.
+// Reverse sweep over the token blocks from the last, each as pieces of PC
+// tokens from the last: a piece's states are recomputed from its checkpoint
+// into registers, then the adjoint steps back through the piece.
 // dx, ddelta, dB partials, dA partial, dh0.
 template <class T>
 __global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__ Bm, const T* __restrict__ Cm) {
@@ -443,13 +442,14 @@ __global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__
     float dps[kTok];                   // dp = dy SiLU(z), so z and dy need not stay live
 #pragma unroll
     for (int j = 0; j < kTok; ++j) dps[j] = widen(v[3][j]) * silu(widen(v[2][j]));
-    const auto rck = rsrc(ckb + (int64_t)(pb / kTok) * NSTATE * a.d_inner);
     const auto rdb = rsrc(dbb + (int64_t)pb * NSTATE);
     const auto rx = rsrc(dxrow + (int64_t)pb * a.d_inner), rd = rsrc(ddrow + (int64_t)pb * a.d_inner);
-    // The block's two halves, later half first.  Each recomputes its states
-    // from the block's checkpoint, keeping only its own PC tokens' states.
+    // The block's pieces, the later first, each recomputed from its own
+    // checkpoint (pieces starting past the chunk's end have none).
 #pragma unroll
     for (int hb = kTok - PC; hb >= 0; hb -= PC) {
+      if (pb + hb >= w.nt) continue;
+      const auto rck = rsrc(ckb + (int64_t)((pb + hb) / PC) * NSTATE * a.d_inner);
       float h[NSTATE];
       // re-read the checkpoint for every piece rather than hold it in registers
       uint32_t lbh = lb4;
@@ -461,13 +461,13 @@ __global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) dAh[n] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < hb + PC; ++j) {
+      for (int j = hb; j < hb + PC; ++j) {
         Br.load(brow + (int64_t)std::min(pb + j, w.nt - 1) * NSTATE);
         const float dt = opaque(widen(v[0][j]));
         const float dxv = dt * widen(v[1][j]);
 #pragma unroll
         for (int n = 0; n < NSTATE; ++n) {
-          if (j >= hb) hp[j - hb][n] = h[n];
+          hp[j - hb][n] = h[n];
           if (j + 1 < hb + PC) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Br[n]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -577,7 +577,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   if (batch <= 0 || L <= 0 || d_inner <= 0) return w;
   const size_t B = (size_t)batch, C = (size_t)p.chunks, Dn = (size_t)d_inner;
   const size_t G = (size_t)((d_inner + 63) / 64);
-  const size_t pieces = (size_t)((p.chunk_len + kTok - 1) / kTok);
+  const size_t pieces = (size_t)((p.chunk_len + PC - 1) / PC);
   w.fwd = ws_layout(batch, L, d_inner, p).total;
   if (p.chunks > 1) {
     w.M = round_up(B * C * NSTATE * Dn * 4);
