@@ -11,6 +11,8 @@ Two implementations of the same definition live here:
   separately in C.
 * ``backward`` (C, ``oracle_backward``): the gradient of the prefill by the
   adjoint recurrence, every forward state kept, for training.
+* ``prefill_trap`` (C, ``oracle_prefill_trap``): the exponential-trapezoidal
+  variant of the recurrence (Mamba-3's discretisation as read from the pages).
 * ``twin.py``: the same loop in numpy, vectorised over channels only, for
   small shapes and as a cross-check of the C code.
 
@@ -63,6 +65,8 @@ def _load():
             lib.oracle_prologue.restype = None
             lib.oracle_backward.argtypes = [i64, i64, i64, i64] + [dp] * 18
             lib.oracle_backward.restype = ctypes.c_int
+            lib.oracle_prefill_trap.argtypes = [i64, i64, i64, i64] + [dp] * 15
+            lib.oracle_prefill_trap.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -204,3 +208,34 @@ def backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None):
     if rc:
         raise MemoryError("oracle_backward: out of memory")
     return out
+
+
+def prefill_trap(x, delta, A, B, C, D, z, h0=None, lam=None, x_prev=None, B_prev=None, want_state=True):
+    """Exponential-trapezoidal prefill (see jscan_oracle.c):
+    h_t = a_t h_{t-1} + dt_t ((1 - lam_t) a_t B_{t-1} x_{t-1} + lam_t B_t x_t).
+    lam: [batch, L, d_inner] or None (1/2); x_prev [batch, d_inner], B_prev
+    [batch, d_state] or None (0).  Returns (y, hT, x_last, B_last), float64."""
+    x = np.asarray(x)
+    batch, L, d_inner = x.shape
+    d_state = np.asarray(A).shape[1]
+    if d_state > 256:
+        raise ValueError("oracle supports d_state <= 256")
+    x = _f64(x, (batch, L, d_inner), "x")
+    delta = _f64(delta, (batch, L, d_inner), "delta")
+    z = _f64(z, (batch, L, d_inner), "z")
+    A = _f64(A, (d_inner, d_state), "A")
+    B = _f64(B, (batch, L, d_state), "B")
+    C = _f64(C, (batch, L, d_state), "C")
+    D = _f64(D, (d_inner,), "D")
+    h0 = None if h0 is None else _f64(h0, (batch, d_inner, d_state), "h0")
+    lam = None if lam is None else _f64(lam, (batch, L, d_inner), "lam")
+    x_prev = None if x_prev is None else _f64(x_prev, (batch, d_inner), "x_prev")
+    B_prev = None if B_prev is None else _f64(B_prev, (batch, d_state), "B_prev")
+    y = np.empty((batch, L, d_inner))
+    hT = np.empty((batch, d_inner, d_state)) if want_state else None
+    x_last = np.empty((batch, d_inner))
+    B_last = np.empty((batch, d_state))
+    _load().oracle_prefill_trap(batch, L, d_inner, d_state, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), _ptr(z), _ptr(h0), _ptr(lam), _ptr(x_prev), _ptr(B_prev), _ptr(y),
+                                _ptr(hT), _ptr(x_last), _ptr(B_last))
+    return y, hT, x_last, B_last

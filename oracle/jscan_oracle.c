@@ -332,3 +332,64 @@ int oracle_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
   free(accAD);
   return failed;
 }
+
+/*
+ * Exponential-trapezoidal variant of the prefill (Mamba-3's discretisation;
+ * test infrastructure, same caveats as above).  The "AI Engineering from
+ * Scratch" Jamba lesson (section "Mamba-3", and its glossary entry for the
+ * exponential-trapezoidal discretisation) describes it only in words: a more
+ * expressive recurrence that contains the Euler rule of the earlier models as
+ * a special case and applies a convolution-like operation to the state input
+ * inside the recurrence.  The reading taken: the input integral of
+ * h' = A h + B x over one step is approximated by a weighted two-point rule
+ * with the exponential kernel applied to the earlier point,
+ *
+ *   h_t = a_t h_{t-1} + dt_t ((1 - lam_t) a_t B_{t-1} x_{t-1} + lam_t B_t x_t),
+ *   a_t = exp(dt_t A),
+ *
+ * so lam_t = 1 is the Euler form of oracle_prefill and lam_t = 1/2 is the
+ * trapezoidal rule.  lam [batch][L][d_inner] (NULL: 1/2 everywhere).  The
+ * token before the first comes from x_prev [batch][d_inner] and B_prev
+ * [batch][d_state] (NULL: zero), and the last token's x and B row are
+ * written to x_last, B_last (NULL: not written).  Output as in
+ * oracle_prefill: y_t = (C_t . h_t + D x_t) SiLU(z_t).
+ */
+void oracle_prefill_trap(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                         const double* x, const double* delta, const double* A,
+                         const double* B, const double* C, const double* Dv,
+                         const double* z, const double* h0, const double* lam,
+                         const double* x_prev, const double* B_prev,
+                         double* y, double* hT, double* x_last, double* B_last) {
+  int64_t channels = batch * d_inner;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t bd = 0; bd < channels; ++bd) {
+    int64_t b = bd / d_inner;
+    int64_t d = bd % d_inner;
+    double h[256];
+    for (int64_t n = 0; n < d_state; ++n)
+      h[n] = h0 ? h0[(b * d_inner + d) * d_state + n] : 0.0;
+    double xp = x_prev ? x_prev[b * d_inner + d] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      int64_t i = (b * L + t) * d_inner + d;
+      const double* Bt = B + (b * L + t) * d_state;
+      const double* Ct = C + (b * L + t) * d_state;
+      double dt = delta[i], xv = x[i], lt = lam ? lam[i] : 0.5;
+      double acc = 0.0;
+      for (int64_t n = 0; n < d_state; ++n) {
+        double Bp = t > 0 ? B[(b * L + t - 1) * d_state + n] : (B_prev ? B_prev[b * d_state + n] : 0.0);
+        double a = exp(dt * A[d * d_state + n]);
+        h[n] = a * h[n] + dt * ((1.0 - lt) * a * Bp * xp + lt * Bt[n] * xv);
+        acc += Ct[n] * h[n];
+      }
+      double zv = z[i];
+      y[i] = (acc + Dv[d] * xv) * zv / (1.0 + exp(-zv));
+      xp = xv;
+    }
+    if (hT)
+      for (int64_t n = 0; n < d_state; ++n) hT[(b * d_inner + d) * d_state + n] = h[n];
+    if (x_last) x_last[b * d_inner + d] = L > 0 ? xp : (x_prev ? x_prev[b * d_inner + d] : 0.0);
+    if (B_last && d == 0)
+      for (int64_t n = 0; n < d_state; ++n)
+        B_last[b * d_state + n] = L > 0 ? B[(b * L + L - 1) * d_state + n] : (B_prev ? B_prev[b * d_state + n] : 0.0);
+  }
+}
