@@ -176,6 +176,49 @@ jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_st
                                     void* y, const jscan_prologue* prologue, void* stream);
 
 /*
+ * Exponential-trapezoidal recurrence (Mamba-3's discretisation).  The "AI
+ * Engineering from Scratch" Jamba lesson (section "Mamba-3" and its
+ * glossary) describes it only in words: a more expressive recurrence that
+ * contains the Euler rule above as a special case and applies a
+ * convolution-like operation to the state input inside the recurrence.  The
+ * reading implemented: the input integral of one step is a weighted
+ * two-point rule with the exponential kernel on the earlier point,
+ *   h_t = a_t h_{t-1} + delta_t ((1 - lam_t) a_t B_{t-1} x_{t-1} + lam_t B_t x_t),
+ *   a_t = exp(delta_t A),  y_t as in jscan_prefill,
+ * so lam_t = 1 is jscan_prefill's recurrence and lam_t = 1/2 the trapezoidal
+ * rule.  All arrays are device pointers in the I/O dtype, 16-byte aligned:
+ *   lam    [nseq][L][d_inner]  weight lam_t (NULL: 1/2 everywhere)
+ *   x_prev [nseq][d_inner]     x of the token before the first (NULL: zero)
+ *   B_prev [nseq][d_state]     B row of that token (NULL: zero)
+ * To continue a sequence, pass the last row of the previous call's x and B
+ * (or, when decoding, the previous step's x and B).
+ */
+typedef struct {
+  const void* lam;
+  const void* x_prev;
+  const void* B_prev;
+} jscan_trap;
+
+/*
+ * jscan_prefill with the exponential-trapezoidal recurrence (trap NULL: all
+ * fields NULL).  prologue may add softplus(delta + dt_bias); a convolution
+ * prologue returns JSCAN_ERR_UNSUPPORTED (Mamba-3 moves that operation inside
+ * the recurrence).  Otherwise as jscan_prefill_fused.
+ */
+jscan_status jscan_prefill_trap(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* h0, void* y, float* hT,
+                                const jscan_trap* trap, const jscan_prologue* prologue, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* jscan_step_batch with the exponential-trapezoidal recurrence (lam is
+ * [n_seq][d_inner]). */
+jscan_status jscan_step_batch_trap(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io, float* state,
+                                   const void* x, const void* delta, const float* A, const void* B,
+                                   const void* C, const float* D, const void* z, void* y,
+                                   const jscan_trap* trap, const jscan_prologue* prologue, void* stream);
+
+/*
  * Backward (gradient) of jscan_prefill, for training.  The pages describe
  * training Jamba ("Jamba: A Hybrid Transformer-Mamba Language Model — 深度解读
  * 报告", section 3.3 on the training infrastructure) but

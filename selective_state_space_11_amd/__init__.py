@@ -14,6 +14,8 @@ Entry points mirror the C ABI in ``include/jscan.h``:
 * ``prefill_fused`` / ``step_batch_fused``: the same with the layer's input
   prologue (causal depthwise conv + SiLU on x, softplus(delta + dt_bias))
   applied inside the scan kernels
+* ``prefill_trap`` / ``step_batch_trap``: the exponential-trapezoidal
+  recurrence (Mamba-3's discretisation as read from the pages)
 * ``backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None)`` -> dict of the
   gradients dx, ddelta, dz, dA, dB, dC, dD, dh0
 * ``workspace_size``, ``plan``, ``set_plan_override``, ``time_next_prefill``
@@ -36,7 +38,13 @@ IO_F32, IO_BF16 = 0, 1
 EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_step", "jscan_step_batch",
            "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
            "jscan_set_plan_override", "jscan_time_next_prefill", "jscan_prefill_fused",
-           "jscan_step_batch_fused", "jscan_backward_workspace_size", "jscan_backward")
+           "jscan_step_batch_fused", "jscan_backward_workspace_size", "jscan_backward", "jscan_prefill_trap",
+           "jscan_step_batch_trap")
+
+
+class Trap(ctypes.Structure):
+    """struct jscan_trap (device pointers as integers)."""
+    _fields_ = [("lam", ctypes.c_void_p), ("x_prev", ctypes.c_void_p), ("B_prev", ctypes.c_void_p)]
 
 
 class Prologue(ctypes.Structure):
@@ -99,6 +107,12 @@ def load_library(path: str = LIB_PATH):
         lib.jscan_prefill_fused.restype = st
         lib.jscan_step_batch_fused.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, pp, vp]
         lib.jscan_step_batch_fused.restype = st
+        tp = ctypes.POINTER(Trap)
+        lib.jscan_prefill_trap.argtypes = [i64, i64, i64, i64, st, vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, tp, pp, vp,
+                                           sz, vp]
+        lib.jscan_prefill_trap.restype = st
+        lib.jscan_step_batch_trap.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, tp, pp, vp]
+        lib.jscan_step_batch_trap.restype = st
         lib.jscan_backward_workspace_size.argtypes = [i64, i64, i64, i64, st]
         lib.jscan_backward_workspace_size.restype = sz
         lib.jscan_backward.argtypes = [i64, i64, i64, i64, st] + [vp] * 18 + [vp, sz, vp]
@@ -385,3 +399,77 @@ def backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None, *, want_dh0=True, o
                               _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(workspace), ws_bytes,
                               _stream(stream)))
     return out
+
+
+def _trap(x, nseq, L, d_inner, lam, x_prev, B_prev):
+    _dev(lam, "lam", x.dtype, (nseq, L, d_inner) if L is not None else (nseq, d_inner))
+    _dev(x_prev, "x_prev", x.dtype, (nseq, d_inner))
+    _dev(B_prev, "B_prev", x.dtype, (nseq, D_STATE))
+    t = Trap()
+    t.lam = None if lam is None else lam.data_ptr()
+    t.x_prev = None if x_prev is None else x_prev.data_ptr()
+    t.B_prev = None if B_prev is None else B_prev.data_ptr()
+    return t
+
+
+def prefill_trap(x, delta, A, B, C, D, z, h0=None, *, lam=None, x_prev=None, B_prev=None, dt_bias=None,
+                 softplus=False, y=None, hT=None, want_state=True, workspace=None, stream=None):
+    """Exponential-trapezoidal prefill: h_t = a_t h_{t-1} + dt_t ((1 - lam_t) a_t B_{t-1} x_{t-1}
+    + lam_t B_t x_t).  lam like x (None: 1/2); x_prev [batch, d_inner] and B_prev [batch, 16]
+    (like x, None: zero) give the token before the first.  Returns (y, hT)."""
+    torch = _torch()
+    lib = load_library()
+    _dev(x, "x")
+    batch, L, d_inner = x.shape
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (batch, L, D_STATE))
+    _dev(C, "C", x.dtype, (batch, L, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, D_STATE))
+    tr = _trap(x, batch, L, d_inner, lam, x_prev, B_prev)
+    pro = _prologue(batch, d_inner, None, None, None, None, dt_bias, softplus)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    if hT is None and want_state:
+        hT = torch.empty((batch, d_inner, D_STATE), dtype=torch.float32, device=x.device)
+    _dev(hT, "hT", torch.float32, (batch, d_inner, D_STATE))
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.jscan_prefill_trap(batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                  _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), ctypes.byref(tr),
+                                  ctypes.byref(pro), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y, hT
+
+
+def step_batch_trap(state, x, delta, A, B, C, D, z, *, lam=None, x_prev=None, B_prev=None, dt_bias=None,
+                    softplus=False, y=None, stream=None):
+    """step_batch with the exponential-trapezoidal recurrence; x_prev and B_prev are the
+    previous step's x [n_seq, d_inner] and B [n_seq, 16] (None: zero), lam like x."""
+    torch = _torch()
+    lib = load_library()
+    _dev(state, "state", torch.float32)
+    n_seq, d_inner, _ = state.shape
+    _dev(state, "state", torch.float32, (n_seq, d_inner, D_STATE))
+    _dev(x, "x", None, (n_seq, d_inner))
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (n_seq, D_STATE))
+    _dev(C, "C", x.dtype, (n_seq, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    tr = _trap(x, n_seq, None, d_inner, lam, x_prev, B_prev)
+    pro = _prologue(n_seq, d_inner, None, None, None, None, dt_bias, softplus)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    _check(lib.jscan_step_batch_trap(n_seq, d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                                     _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), ctypes.byref(tr),
+                                     ctypes.byref(pro), _stream(stream)))
+    return y

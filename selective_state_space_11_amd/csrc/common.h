@@ -53,6 +53,12 @@ struct ProArgs {
   float* hist_out;          // [batch][width-1][d_inner] history after it, or null
   const float* dt_bias;     // [d_inner], or null
   int width;
+  // Exponential-trapezoidal recurrence (I/O dtype arrays): the weight lam_t
+  // [nseq][L][d_inner] (null: 1/2), and x and the B row of the token before
+  // the first, [nseq][d_inner] and [nseq][16] (null: zero).
+  const void* lam = nullptr;
+  const void* x_prev = nullptr;
+  const void* B_prev = nullptr;
 };
 
 template <bool CONV, bool SP>
@@ -151,11 +157,69 @@ template <int S> struct Row<uint16_t, S> {
   __device__ __forceinline__ float operator[](int s) const {
     return (s & 1) ? __uint_as_float(w[s >> 1] & 0xffff0000u) : __uint_as_float(w[s >> 1] << 16);
   }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int q = 0; q < S / 2; ++q) w[q] = 0u;
+  }
+  // Force the words into SGPRs (after a load the compiler made per lane).
+  __device__ __forceinline__ void uniform() {
+#pragma unroll
+    for (int q = 0; q < S / 2; ++q) w[q] = __builtin_amdgcn_readfirstlane(w[q]);
+  }
 };
 template <int S> struct Row<float, S> {
   float w[S];
   __device__ __forceinline__ void load(const float* __restrict__ p) { load_row(w, p); }
   __device__ __forceinline__ float operator[](int s) const { return w[s]; }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int q = 0; q < S; ++q) w[q] = 0.0f;
+  }
+  __device__ __forceinline__ void uniform() {
+#pragma unroll
+    for (int q = 0; q < S; ++q) w[q] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w[q])));
+  }
+};
+
+// Exponential-trapezoidal input term, h_t = a_t h_{t-1} + dt_t ((1 - lam_t)
+// a_t B_{t-1} x_{t-1} + lam_t B_t x_t) = a_t (h_{t-1} + w_t . B_{t-1}) +
+// v_t . B_t with w_t = dt_t (1 - lam_t) x_{t-1} and v_t = dt_t lam_t x_t:
+// the previous token's raw x and B row (states [n0, n0 + S)), carried along
+// the scan.  With TR false it holds nothing.
+template <class T, int S, bool TR>
+struct TrapPrev {
+  float xprev = 0.0f;
+  float lam_add = 0.0f;          // 1/2 when no lam array is given (its loads read 0)
+  Row<T, S> Bp;
+  __device__ __forceinline__ void init(const ProArgs& p, const T* x, const T* Bm, int64_t b, int64_t L,
+                                       int64_t d_inner, int64_t t0, int64_t d, int n0) {
+    if constexpr (TR) {
+      lam_add = p.lam ? 0.0f : 0.5f;
+      if (t0 > 0) {
+        xprev = widen(x[(b * L + t0 - 1) * d_inner + d]);
+        Bp.load(Bm + (b * L + t0 - 1) * NSTATE + n0);
+      } else {
+        const T* xp = static_cast<const T*>(p.x_prev);
+        const T* bp = static_cast<const T*>(p.B_prev);
+        xprev = xp ? widen(xp[b * d_inner + d]) : 0.0f;
+        if (bp) Bp.load(bp + b * NSTATE + n0);
+        else Bp.zero();
+      }
+      Bp.uniform();
+    }
+  }
+  // For token values dt, x and the loaded lam bits: v (scales B_t) and w
+  // (scales B_{t-1}); without TR, v = dt x and w = 0.
+  __device__ __forceinline__ void weights(float dt, float xv, float lam_loaded, float* v, float* w) const {
+    if constexpr (TR) {
+      const float lam = lam_loaded + lam_add;
+      *v = dt * lam * xv;
+      *w = dt * (1.0f - lam) * xprev;
+    } else {
+      *v = dt * xv;
+      *w = 0.0f;
+    }
+  }
 };
 
 // Addressing: a wave covers 64 consecutive channels [gbase, gbase + 64).  Row

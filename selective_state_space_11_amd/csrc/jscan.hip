@@ -57,7 +57,7 @@ namespace jscan_detail {
 // sequence b: S[b][s][n][d] = state after the segment when it starts from
 // zero, dsum[b][s][d] = sum of delta over the segment (accumulated in fp64).
 // The workspace is state-major ([n][d]) so every access is a coalesced row.
-template <class T, bool CONV = false, bool SP = false>
+template <class T, bool CONV = false, bool SP = false, bool TR = false>
 __global__ __launch_bounds__(256) void k_chunk_state(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, float* __restrict__ S, float* __restrict__ dsum,
@@ -93,39 +93,53 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   Prologue<CONV, SP> pro;
   pro.init(pa, d);
   pro.start(pa, pa.hist, x, b, L, d_inner, t0, d);
+  TrapPrev<T, NSTATE, TR> tp;
+  tp.init(pa, x, Bm, b, L, d_inner, t0, d, 0);
+  const T* lrow = TR && pa.lam ? static_cast<const T*>(pa.lam) + (b * L + t0) * d_inner + gbase : drow;
 
   // Loads of token block bb (always kTok whole tokens: segments are multiples).
-  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok]) {
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&ll)[kTok]) {
     const int64_t o = (int64_t)bb * d_inner;
     const auto rd = rsrc(drow + o), rx = rsrc(xrow + o);
+    const auto rl = TR && pa.lam ? rsrc(lrow + o) : rsrc(drow, 0);
 #pragma unroll
-    for (int j = 0; j < kTok; ++j) { buf_load(dd[j], rd, lb, j * rowb); buf_load(xx[j], rx, lb, j * rowb); }
+    for (int j = 0; j < kTok; ++j) {
+      buf_load(dd[j], rd, lb, j * rowb);
+      buf_load(xx[j], rx, lb, j * rowb);
+      if constexpr (TR) buf_load(ll[j], rl, lb, j * rowb);
+    }
   };
   Row<T, NSTATE> Bc, Bn;
-  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok]) {
+  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&ll)[kTok]) {
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
       const float dt = pro.dt(widen(dd[j]));
-      const float dx = dt * pro.xin(widen(xx[j]));
+      const float xv = pro.xin(widen(xx[j]));
+      float dx, wv;
+      tp.weights(dt, xv, TR ? widen(ll[j]) : 0.0f, &dx, &wv);
       dacc += (double)dt;
 #pragma unroll
-      for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
+      for (int n = 0; n < NSTATE; ++n) {
+        if constexpr (TR) h[n] = fmaf(fast_exp2(dt * a2[n]), fmaf(wv, tp.Bp[n], h[n]), dx * Bc[n]);
+        else h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
+      }
+      if constexpr (TR) { tp.xprev = xv; tp.Bp = Bc; }
       Bc = Bn;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Two register sets in turn: block i+1 is in flight while block i computes.
-  T dA[kTok], xA[kTok], dB[kTok], xB[kTok];
-  load_block(0, dA, xA);
+  T dA[kTok], xA[kTok], lA[kTok], dB[kTok], xB[kTok], lB[kTok];
+  load_block(0, dA, xA, lA);
   Bc.load(brow);
   __builtin_amdgcn_s_waitcnt(0);
   for (int base = 0; base < nt; base += 2 * kTok) {
-    load_block(std::min(base + kTok, nt - kTok), dB, xB);
-    do_block(base, dA, xA);
+    load_block(std::min(base + kTok, nt - kTok), dB, xB, lB);
+    do_block(base, dA, xA, lA);
     if (base + kTok >= nt) break;
-    load_block(std::min(base + 2 * kTok, nt - kTok), dA, xA);
-    do_block(base + kTok, dB, xB);
+    load_block(std::min(base + 2 * kTok, nt - kTok), dA, xA, lA);
+    do_block(base + kTok, dB, xB, lB);
   }
   if (lo == lane) {
     const int64_t slot = b * n_segs + seg;
@@ -208,13 +222,15 @@ struct ScanArgs {
 // 0 * x * B = 0 for finite x and B) and their output equals the last token's,
 // which they store again to the same address.  Every block therefore runs the
 // same branch-free code.
-template <class T, int K, bool CONV = false, bool SP = false>
+template <class T, int K, bool CONV = false, bool SP = false, bool TR = false>
 __global__ __launch_bounds__(64 * K) void k_scan(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dw, const T* __restrict__ z,
     const float* __restrict__ hinit, T* __restrict__ y, float* __restrict__ hT,
     int64_t L, int64_t d_inner, int64_t chunk_len, int n_chunks, ProArgs pa) {
-  static_assert(K == 1 || !(CONV || SP), "the input prologue runs with one wave per 64 channels");
+  static_assert(K == 1 || !(CONV || SP || TR), "the input prologue and the trapezoidal form run with one wave "
+                                              "per 64 channels");
+  static_assert(!(CONV && TR), "the trapezoidal form takes no outer convolution");
   constexpr int S = NSTATE / K;
   constexpr int F = kTok / K;          // tokens of a block finished by each wave
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -259,18 +275,24 @@ __global__ __launch_bounds__(64 * K) void k_scan(
   Prologue<CONV, SP> pro;
   pro.init(pa, d);
   pro.start(pa, pa.hist, x, b, L, d_inner, t0, d);
+  TrapPrev<T, S, TR> tp;
+  tp.init(pa, x, Bm, b, L, d_inner, t0, d, n0);
+  const T* lrow = TR && pa.lam ? static_cast<const T*>(pa.lam) + row0 : drow;
 
   // Loads of token block bb.  Rows past the chunk's end are clamped onto its
   // last token, and their delta is read through an empty resource (0).
-  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&xff)[F], T (&zff)[F]) {
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&ll)[kTok], T (&xff)[F],
+                        T (&zff)[F]) {
     const int64_t o = (int64_t)bb * d_inner;
     const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), r0 = rsrc(drow, 0);
+    const auto rl = TR && pa.lam ? rsrc(lrow + o) : r0;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
       buf_load(dd[j], bb + j < nt ? rd : r0, lb, so);
       buf_load(xx[j], rx, lb, so);
       if constexpr (K == 1) buf_load(zz[j], rz, lb, so);
+      if constexpr (TR) buf_load(ll[j], rl, lb, so);
     }
     if constexpr (K > 1) {
 #pragma unroll
@@ -294,7 +316,7 @@ __global__ __launch_bounds__(64 * K) void k_scan(
     if (!CONV || bb + j < nt) buf_store(to_io(fmaf(Dd, xv, acc) * silu(zv), T()), ry, lb, so);
   };
   auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
-                      const T (&xff)[F], const T (&zff)[F]) {
+                      const T (&ll)[kTok], const T (&xff)[F], const T (&zff)[F]) {
     const auto ry = rsrc(yrow + (int64_t)bb * d_inner);
     float part[kTok];
 #pragma unroll
@@ -305,14 +327,19 @@ __global__ __launch_bounds__(64 * K) void k_scan(
       // positive step, so it is forced back to 0 (a wave-uniform select).
       const float dt = SP ? (bb + j < nt ? pro.dt(widen(dd[j])) : 0.0f) : widen(dd[j]);
       const float xv = pro.xin(widen(xx[j]));
-      const float dx = dt * xv;
+      float dx, wv;
+      tp.weights(dt, xv, TR ? widen(ll[j]) : 0.0f, &dx, &wv);
 #pragma unroll
-      for (int s = 0; s < S; ++s) h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bc[s]);
+      for (int s = 0; s < S; ++s) {
+        if constexpr (TR) h[s] = fmaf(fast_exp2(dt * a2[s]), fmaf(wv, tp.Bp[s], h[s]), dx * Bc[s]);
+        else h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bc[s]);
+      }
       float acc = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) acc = fmaf(Cv[s], h[s], acc);
       if constexpr (K == 1) finish(ry, bb, j, acc, xv, widen(zz[j]));
       else part[j] = acc;
+      if constexpr (TR) { tp.xprev = xv; tp.Bp = Bc; }
       Bc = Bn;
       // Keep each token's scalar B/C loads in its own token: hoisting them
       // across tokens would hold several rows in SGPRs at once and spill.
@@ -337,20 +364,20 @@ __global__ __launch_bounds__(64 * K) void k_scan(
   };
 
   // Two register sets in turn: block i+1 is in flight while block i computes.
-  T dA[kTok], xA[kTok], zA[kTok], fxA[F], fzA[F];
-  T dB[kTok], xB[kTok], zB[kTok], fxB[F], fzB[F];
-  load_block(0, dA, xA, zA, fxA, fzA);
+  T dA[kTok], xA[kTok], zA[kTok], lA[kTok], fxA[F], fzA[F];
+  T dB[kTok], xB[kTok], zB[kTok], lB[kTok], fxB[F], fzB[F];
+  load_block(0, dA, xA, zA, lA, fxA, fzA);
   Bc.load(brow);
   __builtin_amdgcn_s_waitcnt(0);
   // Prefetches past the chunk's end are clamped to its last block (valid rows,
   // values unused), so every row offset below stays non-negative.
   const int last = (nt - 1) / kTok * kTok;
   for (int base = 0; base < nt; base += 2 * kTok) {
-    load_block(std::min(base + kTok, last), dB, xB, zB, fxB, fzB);
-    do_block(base, dA, xA, zA, fxA, fzA);
+    load_block(std::min(base + kTok, last), dB, xB, zB, lB, fxB, fzB);
+    do_block(base, dA, xA, zA, lA, fxA, fzA);
     if (base + kTok >= nt) break;
-    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, fxA, fzA);
-    do_block(base + kTok, dB, xB, zB, fxB, fzB);
+    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, lA, fxA, fzA);
+    do_block(base + kTok, dB, xB, zB, lB, fxB, fzB);
   }
   if (hT && c == n_chunks - 1 && lo == lane) {
     float* ho = hT + (b * d_inner + d) * NSTATE + n0;
@@ -386,7 +413,7 @@ __global__ __launch_bounds__(256) void k_copy_state(const float* __restrict__ sr
 // (pa.hist[s][j][d], width-1 raw x) is read first and the shifted history,
 // ending with this token's x, written by the quad's first lane (in place
 // allowed).
-template <class T, bool CONV = false, bool SP = false>
+template <class T, bool CONV = false, bool SP = false, bool TR = false>
 __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T* __restrict__ x,
                                               const T* __restrict__ delta, const float* __restrict__ A,
                                               const T* __restrict__ B, const T* __restrict__ C,
@@ -421,7 +448,21 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
   const float dt = pro.dt(widen(delta[sd]));
   const T* Bs = B + s * NSTATE + 4 * q;
   const T* Cs = C + s * NSTATE + 4 * q;
-  const float dx = dt * xv;
+  float dx = dt * xv;
+  if constexpr (TR) {
+    // h = a (h + w B_prev) + v B with w = dt (1 - lam) x_prev, v = dt lam x
+    const float lam = pa.lam ? widen(static_cast<const T*>(pa.lam)[sd]) : 0.5f;
+    const float xp = pa.x_prev ? widen(static_cast<const T*>(pa.x_prev)[sd]) : 0.0f;
+    const T* Bq = pa.B_prev ? static_cast<const T*>(pa.B_prev) + s * NSTATE + 4 * q : nullptr;
+    const float wv = dt * (1.0f - lam) * xp;
+    dx *= lam;
+    if (Bq) {
+      hv.x = fmaf(wv, widen(Bq[0]), hv.x);
+      hv.y = fmaf(wv, widen(Bq[1]), hv.y);
+      hv.z = fmaf(wv, widen(Bq[2]), hv.z);
+      hv.w = fmaf(wv, widen(Bq[3]), hv.w);
+    }
+  }
   hv.x = fmaf(fast_exp2(dt * (av.x * kLog2e)), hv.x, dx * widen(Bs[0]));
   hv.y = fmaf(fast_exp2(dt * (av.y * kLog2e)), hv.y, dx * widen(Bs[1]));
   hv.z = fmaf(fast_exp2(dt * (av.z * kLog2e)), hv.z, dx * widen(Bs[2]));
@@ -566,31 +607,31 @@ bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner) {
   return L <= INT32_MAX && batch <= 65535 && d_inner <= (1 << 24);
 }
 
-template <class T, int K, bool CONV, bool SP>
+template <class T, int K, bool CONV, bool SP, bool TR>
 hipError_t launch_scan(const ScanArgs& a, int64_t batch, hipStream_t st) {
   dim3 grid((unsigned)((a.d_inner + 63) / 64), (unsigned)a.n_chunks, (unsigned)batch);
-  hipLaunchKernelGGL((k_scan<T, K, CONV, SP>), grid, dim3(64 * K), 0, st, static_cast<const T*>(a.x),
+  hipLaunchKernelGGL((k_scan<T, K, CONV, SP, TR>), grid, dim3(64 * K), 0, st, static_cast<const T*>(a.x),
                      static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
                      a.D, static_cast<const T*>(a.z), a.hinit,
                      static_cast<T*>(a.y), a.hT, a.L, a.d_inner, a.chunk_len, a.n_chunks, a.pa);
   return hipGetLastError();
 }
 
-template <class T, bool CONV, bool SP>
+template <class T, bool CONV, bool SP, bool TR>
 hipError_t launch_scan_k(int K, const ScanArgs& a, int64_t batch, hipStream_t st) {
-  if constexpr (CONV || SP) {
-    return launch_scan<T, 1, CONV, SP>(a, batch, st);     // the prologue runs with K = 1
+  if constexpr (CONV || SP || TR) {
+    return launch_scan<T, 1, CONV, SP, TR>(a, batch, st);     // these run with K = 1
   } else {
     switch (K) {
-      case 1: return launch_scan<T, 1, false, false>(a, batch, st);
-      case 2: return launch_scan<T, 2, false, false>(a, batch, st);
-      case 4: return launch_scan<T, 4, false, false>(a, batch, st);
-      default: return launch_scan<T, 8, false, false>(a, batch, st);
+      case 1: return launch_scan<T, 1, false, false, false>(a, batch, st);
+      case 2: return launch_scan<T, 2, false, false, false>(a, batch, st);
+      case 4: return launch_scan<T, 4, false, false, false>(a, batch, st);
+      default: return launch_scan<T, 8, false, false, false>(a, batch, st);
     }
   }
 }
 
-template <class T, bool CONV, bool SP>
+template <class T, bool CONV, bool SP, bool TR>
 jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* x, const void* delta,
                          const float* A, const void* B, const void* C, const float* D, const void* z,
                          const float* h0, void* y, float* hT, char* ws, const Plan& p, const ProArgs& pa,
@@ -606,7 +647,7 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
   if (p.chunks > 1) {
     const int segs = (int)p.segments();
     dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)segs, (unsigned)batch);
-    hipLaunchKernelGGL((k_chunk_state<T, CONV, SP>), g1, dim3(256), 0, st, static_cast<const T*>(x),
+    hipLaunchKernelGGL((k_chunk_state<T, CONV, SP, TR>), g1, dim3(256), 0, st, static_cast<const T*>(x),
                        static_cast<const T*>(delta), A, static_cast<const T*>(B), S, dsum, L, d_inner, p.seg_len,
                        segs, pa);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
@@ -622,7 +663,7 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
   hipEvent_t eb = t_ev_before, ea = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
   if (eb && ea && (e = hipEventRecord(eb, st)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = launch_scan_k<T, CONV, SP>(p.K, a, batch, st)) != hipSuccess) return hip_fail(e, "scan launch");
+  if ((e = launch_scan_k<T, CONV, SP, TR>(p.K, a, batch, st)) != hipSuccess) return hip_fail(e, "scan launch");
   if (eb && ea && (e = hipEventRecord(ea, st)) != hipSuccess) return hip_fail(e, "event record");
   return JSCAN_OK;
 }
@@ -657,13 +698,18 @@ jscan_status forward_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t
   return JSCAN_OK;
 }
 
-// Calls f(integral_constant<bool, CONV>, integral_constant<bool, SP>).
+// Calls f(integral_constant<bool, CONV>, integral_constant<bool, SP>,
+// integral_constant<bool, TR>) for the supported combinations (the
+// trapezoidal form takes no convolution; callers reject that pair first).
 template <class F>
-auto with_prologue(bool conv, bool sp, F&& f) {
-  if (conv && sp) return f(std::true_type{}, std::true_type{});
-  if (conv) return f(std::true_type{}, std::false_type{});
-  if (sp) return f(std::false_type{}, std::true_type{});
-  return f(std::false_type{}, std::false_type{});
+auto with_flags(bool conv, bool sp, bool tr, F&& f) {
+  using Y = std::true_type;
+  using N = std::false_type;
+  if (tr) return sp ? f(N{}, Y{}, Y{}) : f(N{}, N{}, Y{});
+  if (conv && sp) return f(Y{}, Y{}, N{});
+  if (conv) return f(Y{}, N{}, N{});
+  if (sp) return f(N{}, Y{}, N{});
+  return f(N{}, N{}, N{});
 }
 
 jscan_status check_common(int64_t d_state, jscan_io io) {
@@ -687,12 +733,12 @@ jscan_status check_ranges(const Range* in, int n_in, const Range* out, int n_out
   return JSCAN_OK;
 }
 
-template <class T, bool CONV, bool SP>
+template <class T, bool CONV, bool SP, bool TR>
 jscan_status run_step(int64_t n_seq, int64_t d_inner, float* state, const void* x, const void* delta,
                       const float* A, const void* B, const void* C, const float* D, const void* z,
                       void* y, const ProArgs& pa, hipStream_t st) {
   const int64_t total = n_seq * d_inner * 4;
-  hipLaunchKernelGGL((k_step<T, CONV, SP>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, state,
+  hipLaunchKernelGGL((k_step<T, CONV, SP, TR>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, state,
                      static_cast<const T*>(x), static_cast<const T*>(delta), A, static_cast<const T*>(B),
                      static_cast<const T*>(C), D, static_cast<const T*>(z), static_cast<T*>(y), n_seq,
                      d_inner, pa);
@@ -733,10 +779,29 @@ jscan_status check_prologue(const jscan_prologue* pro, int64_t nseq, int64_t d_i
   return JSCAN_OK;
 }
 
+// Validates the optional trapezoidal descriptor (I/O dtype arrays of element
+// size es) and fills its fields of `pa`; appends its inputs to the range list.
+jscan_status check_trap(const jscan_trap* tr, int64_t nseq, int64_t L, int64_t d_inner, size_t es, ProArgs* pa,
+                        Range* in, int* n_in) {
+  if (!tr) return JSCAN_OK;
+  if (pa->conv_w) return fail(JSCAN_ERR_UNSUPPORTED, "the trapezoidal form takes no convolution prologue");
+  const void* ptrs[] = {tr->lam, tr->x_prev, tr->B_prev};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  pa->lam = tr->lam;
+  pa->x_prev = tr->x_prev;
+  pa->B_prev = tr->B_prev;
+  in[(*n_in)++] = Range{tr->lam, (size_t)nseq * (size_t)L * (size_t)d_inner * es, "lam"};
+  in[(*n_in)++] = Range{tr->x_prev, (size_t)nseq * (size_t)d_inner * es, "x_prev"};
+  in[(*n_in)++] = Range{tr->B_prev, (size_t)nseq * NSTATE * es, "B_prev"};
+  return JSCAN_OK;
+}
+
 jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
                           const void* x, const void* delta, const float* A, const void* B, const void* C,
                           const float* D, const void* z, const float* h0, void* y, float* hT,
-                          const jscan_prologue* pro, void* workspace, size_t workspace_bytes, void* stream) {
+                          const jscan_prologue* pro, const jscan_trap* trap, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   t_last_error.clear();
   jscan_status s = check_common(d_state, io);
   if (s != JSCAN_OK) return s;
@@ -753,12 +818,13 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
   const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
   Plan plan = choose_plan(batch, L, d_inner);
   const size_t need = ws_layout(batch, L, d_inner, plan).total;
-  Range in[12] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
+  Range in[16] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
                   {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"}};
   Range out[4] = {{y, tok, "y"}, {hT, stb, "hT"}, {workspace, workspace ? need : 0, "workspace"}};
   int n_in = 8, n_out = 3;
   ProArgs pa;
   if ((s = check_prologue(pro, batch, d_inner, &pa, in, &n_in, out, &n_out)) != JSCAN_OK) return s;
+  if ((s = check_trap(trap, batch, L, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
   // An output may be the very same buffer as one input: hT == h0, or an
   // in-place conv history.
   for (int i = 0; i < n_out; ++i)
@@ -796,8 +862,8 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
     t_ev_before = t_ev_after = nullptr;
     return JSCAN_OK;
   }
-  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus;
-  if (conv || sp) plan.K = 1;                              // the prologue runs with one wave per group
+  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
+  if (conv || sp || tr) plan.K = 1;                        // these run with one wave per group
   char* ws = static_cast<char*>(workspace);
   bool owned = false;
   if (!ws && need > 0) {
@@ -805,13 +871,13 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
       return hip_fail(e, "hipMallocAsync(workspace)");
     owned = true;
   }
-  s = with_prologue(conv, sp, [&](auto cv, auto spv) {
-    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value;
+  s = with_flags(conv, sp, tr, [&](auto cv, auto spv, auto trv) {
+    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value;
     return io == JSCAN_IO_BF16
-               ? run_prefill<uint16_t, CV, SPV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws, plan,
-                                                pa, st)
-               : run_prefill<float, CV, SPV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws, plan, pa,
-                                             st);
+               ? run_prefill<uint16_t, CV, SPV, TRV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws,
+                                                     plan, pa, st)
+               : run_prefill<float, CV, SPV, TRV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws,
+                                                  plan, pa, st);
   });
   if (owned) {
     e = hipFreeAsync(ws, st);
@@ -822,7 +888,8 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
 
 jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io, float* state,
                        const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const void* z, void* y, const jscan_prologue* pro, void* stream) {
+                       const float* D, const void* z, void* y, const jscan_prologue* pro,
+                       const jscan_trap* trap, void* stream) {
   t_last_error.clear();
   jscan_status s = check_common(d_state, io);
   if (s != JSCAN_OK) return s;
@@ -831,10 +898,11 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
       t / (NSTATE * 16) > ((int64_t)1 << 37))
     return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
   if (n_seq == 0 || d_inner == 0) {                       // nothing to do; the prologue is still checked
-    Range in[5], out[1];
+    Range in[8], out[1];
     int n_in = 0, n_out = 0;
     ProArgs pa;
-    return check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out);
+    jscan_status s2 = check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out);
+    return s2 != JSCAN_OK ? s2 : check_trap(trap, n_seq, 1, d_inner, 4, &pa, in, &n_in);
   }
   if (!state || !x || !delta || !A || !B || !C || !D || !z || !y)
     return fail(JSCAN_ERR_NULL, "every pointer is required");
@@ -845,22 +913,23 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
   const size_t tok = (size_t)n_seq * (size_t)d_inner * es;
   const size_t rowb = (size_t)n_seq * NSTATE * es;
   const size_t stb = (size_t)n_seq * (size_t)d_inner * NSTATE * 4;
-  Range in[11] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
+  Range in[14] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
                   {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}};
   Range out[3] = {{y, tok, "y"}, {state, stb, "state"}};
   int n_in = 7, n_out = 2;
   ProArgs pa;
   if ((s = check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out)) != JSCAN_OK) return s;
+  if ((s = check_trap(trap, n_seq, 1, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
   if ((s = check_ranges(in, n_in, out, n_out, pa.hist_out && pa.hist_out == pa.hist ? pa.hist : nullptr)) !=
       JSCAN_OK)
     return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus;
-  return with_prologue(conv, sp, [&](auto cv, auto spv) {
-    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value;
+  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
+  return with_flags(conv, sp, tr, [&](auto cv, auto spv, auto trv) {
+    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value;
     return io == JSCAN_IO_BF16
-               ? run_step<uint16_t, CV, SPV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st)
-               : run_step<float, CV, SPV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st);
+               ? run_step<uint16_t, CV, SPV, TRV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st)
+               : run_step<float, CV, SPV, TRV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st);
   });
 }
 
@@ -927,8 +996,8 @@ jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
                            const void* C, const float* D, const void* z, const float* h0,
                            void* y, float* hT, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, nullptr, workspace,
-                      workspace_bytes, stream);
+  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, nullptr, nullptr,
+                      workspace, workspace_bytes, stream);
 }
 
 jscan_status jscan_prefill_fused(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
@@ -936,28 +1005,47 @@ jscan_status jscan_prefill_fused(int64_t batch, int64_t L, int64_t d_inner, int6
                                  const void* C, const float* D, const void* z, const float* h0,
                                  void* y, float* hT, const jscan_prologue* prologue, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, prologue, workspace,
-                      workspace_bytes, stream);
+  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, prologue, nullptr,
+                      workspace, workspace_bytes, stream);
 }
 
 jscan_status jscan_step_batch(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
                               float* state, const void* x, const void* delta, const float* A,
                               const void* B, const void* C, const float* D, const void* z,
                               void* y, void* stream) {
-  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, nullptr, stream);
+  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, nullptr, nullptr, stream);
 }
 
 jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
                                     float* state, const void* x, const void* delta, const float* A,
                                     const void* B, const void* C, const float* D, const void* z,
                                     void* y, const jscan_prologue* prologue, void* stream) {
-  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, prologue, stream);
+  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, prologue, nullptr, stream);
+}
+
+jscan_status jscan_prefill_trap(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* h0, void* y, float* hT,
+                                const jscan_trap* trap, const jscan_prologue* prologue, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  static const jscan_trap plain{nullptr, nullptr, nullptr};
+  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, prologue,
+                      trap ? trap : &plain, workspace, workspace_bytes, stream);
+}
+
+jscan_status jscan_step_batch_trap(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io, float* state,
+                                   const void* x, const void* delta, const float* A, const void* B,
+                                   const void* C, const float* D, const void* z, void* y,
+                                   const jscan_trap* trap, const jscan_prologue* prologue, void* stream) {
+  static const jscan_trap plain{nullptr, nullptr, nullptr};
+  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, prologue,
+                   trap ? trap : &plain, stream);
 }
 
 jscan_status jscan_step(int64_t d_inner, int64_t d_state, jscan_io io, float* state, const void* x,
                         const void* delta, const float* A, const void* B, const void* C, const float* D,
                         const void* z, void* y, void* stream) {
-  return step_impl(1, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, nullptr, stream);
+  return step_impl(1, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, nullptr, nullptr, stream);
 }
 
 }  // extern "C"

@@ -31,6 +31,10 @@ Recipe (Jamba-shaped inputs: hidden 4096, d_inner 8192, d_state 16):
   GRAD_STREAM, block])`` per block of ``CHUNK`` tokens as dy ~ N(0, 1)
   [batch, block, d_inner] in the I/O dtype, and dhT ~ N(0, 1) [batch, d_inner,
   d_state] fp32 from ``PCG64([seed, GRAD_STREAM])``.
+* Trapezoidal-recurrence inputs come from ``PCG64([seed, TRAP_STREAM])``:
+  lam ~ U(0, 1) [batch, L, d_inner], then the token before the first,
+  x_prev ~ N(0, 1) [batch, d_inner] and B_prev ~ N(0, 1) / 4 [batch,
+  d_state], all in the I/O dtype.
 * Decode inputs for step k of a run seeded ``seed`` come from
   ``PCG64([seed, DECODE_STREAM, k])`` in the order x, delta, z ([n_seq,
   d_inner]), B, C ([n_seq, d_state]); the initial decode state (~N(0, 1)) from
@@ -54,6 +58,7 @@ DECODE_STREAM = 2_000_003
 STATE_STREAM = 3_000_017
 PROLOGUE_STREAM = 4_000_037
 GRAD_STREAM = 5_000_011
+TRAP_STREAM = 6_000_013
 
 IO_BF16 = "bf16"
 IO_F32 = "f32"
@@ -208,6 +213,15 @@ def output_grads(batch, L, d_inner, d_state=16, seed=0, io=IO_BF16, t_begin=0, t
     g = np.random.Generator(np.random.PCG64([seed, GRAD_STREAM]))
     dhT = g.standard_normal(size=(batch, d_inner, d_state)).astype(np.float32)
     return dy, dhT
+
+
+def trap_inputs(batch, L, d_inner, d_state=16, seed=0, io=IO_BF16):
+    """lam [batch, L, d_inner], x_prev [batch, d_inner], B_prev [batch, d_state] (I/O dtype)."""
+    g = np.random.Generator(np.random.PCG64([seed, TRAP_STREAM]))
+    lam = _round(g.uniform(0.0, 1.0, size=(batch, L, d_inner)), io)
+    x_prev = _round(g.standard_normal(size=(batch, d_inner)), io)
+    B_prev = _round(g.standard_normal(size=(batch, d_state)) / 4.0, io)
+    return lam, x_prev, B_prev
 
 
 def decode_state(n_seq, d_inner, d_state=16, seed=3):

@@ -326,3 +326,32 @@ def test_backward_workspace_size():
     assert js.backward_workspace_size(1, L, d) >= L * d * 8
     assert js.backward_workspace_size(0, L, d) == 0
     assert js.backward_workspace_size(1, L, d, 15) == 0
+
+
+# ------------------------------------------------------------- trapezoidal
+def test_prefill_trap_validation(lib):
+    a = prefill_args()
+    keys = ("batch", "L", "d_inner", "d_state", "io", "x", "delta", "A", "B", "C", "D", "z", "h0", "y", "hT")
+
+    def call(trap, pro=None, **over):
+        b = dict(a, **over)
+        return lib.jscan_prefill_trap(*(b[k] for k in keys), ctypes.byref(trap) if trap is not None else None,
+                                      ctypes.byref(pro) if pro is not None else None, b["workspace"],
+                                      b["ws_bytes"], b["stream"])
+    t = js.Trap()
+    t.lam, t.x_prev, t.B_prev = fake(11).value, fake(12).value, fake(13).value
+    assert call(t, prologue()) == UNSUP                          # no convolution with the trapezoidal form
+    bad = js.Trap()
+    bad.lam = fake(11).value + 2
+    assert call(bad) == ALIGN
+    alias = js.Trap()
+    alias.lam = fake(8).value                                    # lam on top of y
+    assert call(alias) == ALIAS
+    assert call(t, batch=0) == OK                                # nothing to do
+    # the decode step: lam [n_seq][d_inner] over the state is an alias
+    s = step_args()
+    st = js.Trap()
+    st.lam = fake(0, 128).value
+    assert lib.jscan_step_batch_trap(s["n_seq"], s["d_inner"], s["d_state"], s["io"], s["state"], s["x"],
+                                     s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["y"],
+                                     ctypes.byref(st), None, None) == ALIAS
