@@ -181,46 +181,57 @@ template <int S> struct Row<float, S> {
   }
 };
 
-// Exponential-trapezoidal input term, h_t = a_t h_{t-1} + dt_t ((1 - lam_t)
-// a_t B_{t-1} x_{t-1} + lam_t B_t x_t) = a_t (h_{t-1} + w_t . B_{t-1}) +
-// v_t . B_t with w_t = dt_t (1 - lam_t) x_{t-1} and v_t = dt_t lam_t x_t:
-// the previous token's raw x and B row (states [n0, n0 + S)), carried along
-// the scan.  With TR false it holds nothing.
-template <class T, int S, bool TR>
-struct TrapPrev {
-  float xprev = 0.0f;
-  float lam_add = 0.0f;          // 1/2 when no lam array is given (its loads read 0)
-  Row<T, S> Bp;
-  __device__ __forceinline__ void init(const ProArgs& p, const T* x, const T* Bm, int64_t b, int64_t L,
-                                       int64_t d_inner, int64_t t0, int64_t d, int n0) {
-    if constexpr (TR) {
-      lam_add = p.lam ? 0.0f : 0.5f;
-      if (t0 > 0) {
-        xprev = widen(x[(b * L + t0 - 1) * d_inner + d]);
-        Bp.load(Bm + (b * L + t0 - 1) * NSTATE + n0);
-      } else {
-        const T* xp = static_cast<const T*>(p.x_prev);
-        const T* bp = static_cast<const T*>(p.B_prev);
-        xprev = xp ? widen(xp[b * d_inner + d]) : 0.0f;
-        if (bp) Bp.load(bp + b * NSTATE + n0);
-        else Bp.zero();
-      }
-      Bp.uniform();
-    }
+// DPP move within rows of 16 lanes (ctrl: quad_perm, row_ror, row_half_mirror ...).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Two adjacent B or C values of one token, read per lane (bf16 pairs packed in
+// one dword), for the per-token products C_t . B_t.
+template <class T> struct Pair;
+template <> struct Pair<uint16_t> {
+  uint32_t w;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    w = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
   }
-  // For token values dt, x and the loaded lam bits: v (scales B_t) and w
-  // (scales B_{t-1}); without TR, v = dt x and w = 0.
-  __device__ __forceinline__ void weights(float dt, float xv, float lam_loaded, float* v, float* w) const {
-    if constexpr (TR) {
-      const float lam = lam_loaded + lam_add;
-      *v = dt * lam * xv;
-      *w = dt * (1.0f - lam) * xprev;
-    } else {
-      *v = dt * xv;
-      *w = 0.0f;
-    }
+  __device__ __forceinline__ float dot(const Pair& o) const {
+    return fmaf(__uint_as_float(w & 0xffff0000u), __uint_as_float(o.w & 0xffff0000u),
+                __uint_as_float(w << 16) * __uint_as_float(o.w << 16));
   }
 };
+template <> struct Pair<float> {
+  float a, b;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+    b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4, 0, 0));
+  }
+  __device__ __forceinline__ float dot(const Pair& o) const { return fmaf(b, o.b, a * o.a); }
+};
+
+// Exponential-trapezoidal recurrence,
+//   h_t = a_t h_{t-1} + dt_t ((1 - lam_t) a_t B_{t-1} x_{t-1} + lam_t B_t x_t),
+// scanned as an Euler-form recurrence on the shifted state
+//   g_t = h_t + w_{t+1} B_t,   w_{t+1} = dt_{t+1} (1 - lam_{t+1}) x_t,
+// which satisfies g_t = a_t g_{t-1} + (dt_t lam_t x_t + w_{t+1}) B_t: the
+// same per-state work as the Euler scan.  The output uses
+// C_t . h_t = C_t . g_t - w_{t+1} (C_t . B_t), and after the last token of a
+// sequence w = 0, so g = h there.  Before the first token,
+// g_{-1} = h_{-1} + w_0 B_prev; trap_seed adds w_0 B_prev.
+template <class T, int S, bool CONV, bool SP>
+__device__ __forceinline__ void trap_seed(float (&h)[S], const ProArgs& pa, const Prologue<CONV, SP>& pro,
+                                          const T* delta, int64_t b, int64_t L, int64_t d_inner, int64_t d,
+                                          int n0) {
+  const T* xp = static_cast<const T*>(pa.x_prev);
+  const T* bp = static_cast<const T*>(pa.B_prev);
+  if (!xp || !bp) return;
+  const int64_t i0 = (b * L) * d_inner + d;                 // token 0 of sequence b
+  const float dt0 = pro.dt(widen(delta[i0]));
+  const float lam0 = pa.lam ? widen(static_cast<const T*>(pa.lam)[i0]) : 0.5f;
+  const float w0 = dt0 * (1.0f - lam0) * widen(xp[b * d_inner + d]);
+#pragma unroll
+  for (int s = 0; s < S; ++s) h[s] = fmaf(w0, widen(bp[b * NSTATE + n0 + s]), h[s]);
+}
 
 // Addressing: a wave covers 64 consecutive channels [gbase, gbase + 64).  Row
 // pointers (token t, channel gbase) are wave-uniform and live in SGPRs; a lane

@@ -93,12 +93,18 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   Prologue<CONV, SP> pro;
   pro.init(pa, d);
   pro.start(pa, pa.hist, x, b, L, d_inner, t0, d);
-  TrapPrev<T, NSTATE, TR> tp;
-  tp.init(pa, x, Bm, b, L, d_inner, t0, d, 0);
+  // Trapezoidal form: the scan runs on the shifted state g (see trap_seed);
+  // segment 0 starts from g_{-1} - h0 = w_0 B_prev, the combine adds h0.
   const T* lrow = TR && pa.lam ? static_cast<const T*>(pa.lam) + (b * L + t0) * d_inner + gbase : drow;
+  const float lam_add = TR && !pa.lam ? 0.5f : 0.0f;      // a missing lam reads 0 through the empty resource
+  if constexpr (TR) {
+    if (t0 == 0) trap_seed(h, pa, pro, delta, b, L, d_inner, d, 0);
+  }
 
-  // Loads of token block bb (always kTok whole tokens: segments are multiples).
-  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&ll)[kTok]) {
+  // Loads of token block bb (always kTok whole tokens: segments are multiples),
+  // and with TR delta and lam of the token after the block (a segment never
+  // ends the sequence, so that token exists).
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&ll)[kTok], T& dn, T& ln) {
     const int64_t o = (int64_t)bb * d_inner;
     const auto rd = rsrc(drow + o), rx = rsrc(xrow + o);
     const auto rl = TR && pa.lam ? rsrc(lrow + o) : rsrc(drow, 0);
@@ -108,38 +114,46 @@ __global__ __launch_bounds__(256) void k_chunk_state(
       buf_load(xx[j], rx, lb, j * rowb);
       if constexpr (TR) buf_load(ll[j], rl, lb, j * rowb);
     }
+    if constexpr (TR) {
+      buf_load(dn, rd, lb, kTok * rowb);
+      buf_load(ln, rl, lb, kTok * rowb);
+    }
   };
   Row<T, NSTATE> Bc, Bn;
-  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&ll)[kTok]) {
+  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&ll)[kTok], const T& dn,
+                      const T& ln) {
+    float dtv[kTok + 1], lv[kTok + 1];             // TR: delta and lam of the block's tokens and the next
+    if constexpr (TR) {
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) { dtv[j] = pro.dt(widen(dd[j])); lv[j] = widen(ll[j]) + lam_add; }
+      dtv[kTok] = pro.dt(widen(dn));
+      lv[kTok] = widen(ln) + lam_add;
+    }
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
-      const float dt = pro.dt(widen(dd[j]));
+      const float dt = TR ? dtv[j] : pro.dt(widen(dd[j]));
       const float xv = pro.xin(widen(xx[j]));
-      float dx, wv;
-      tp.weights(dt, xv, TR ? widen(ll[j]) : 0.0f, &dx, &wv);
+      float dx = dt * xv;
+      if constexpr (TR) dx = fmaf(dtv[j + 1] * (1.0f - lv[j + 1]), xv, dx * lv[j]);
       dacc += (double)dt;
 #pragma unroll
-      for (int n = 0; n < NSTATE; ++n) {
-        if constexpr (TR) h[n] = fmaf(fast_exp2(dt * a2[n]), fmaf(wv, tp.Bp[n], h[n]), dx * Bc[n]);
-        else h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
-      }
-      if constexpr (TR) { tp.xprev = xv; tp.Bp = Bc; }
+      for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
       Bc = Bn;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Two register sets in turn: block i+1 is in flight while block i computes.
-  T dA[kTok], xA[kTok], lA[kTok], dB[kTok], xB[kTok], lB[kTok];
-  load_block(0, dA, xA, lA);
+  T dA[kTok], xA[kTok], lA[kTok], dB[kTok], xB[kTok], lB[kTok], dnA, lnA, dnB, lnB;
+  load_block(0, dA, xA, lA, dnA, lnA);
   Bc.load(brow);
   __builtin_amdgcn_s_waitcnt(0);
   for (int base = 0; base < nt; base += 2 * kTok) {
-    load_block(std::min(base + kTok, nt - kTok), dB, xB, lB);
-    do_block(base, dA, xA, lA);
+    load_block(std::min(base + kTok, nt - kTok), dB, xB, lB, dnB, lnB);
+    do_block(base, dA, xA, lA, dnA, lnA);
     if (base + kTok >= nt) break;
-    load_block(std::min(base + 2 * kTok, nt - kTok), dA, xA, lA);
-    do_block(base + kTok, dB, xB, lB);
+    load_block(std::min(base + 2 * kTok, nt - kTok), dA, xA, lA, dnA, lnA);
+    do_block(base + kTok, dB, xB, lB, dnB, lnB);
   }
   if (lo == lane) {
     const int64_t slot = b * n_segs + seg;
@@ -275,14 +289,21 @@ __global__ __launch_bounds__(64 * K) void k_scan(
   Prologue<CONV, SP> pro;
   pro.init(pa, d);
   pro.start(pa, pa.hist, x, b, L, d_inner, t0, d);
-  TrapPrev<T, S, TR> tp;
-  tp.init(pa, x, Bm, b, L, d_inner, t0, d, n0);
+  // Trapezoidal form: the scan runs on the shifted state g (see trap_seed);
+  // chunk 0 starts from h0 + w_0 B_prev, later chunks from the combine's g.
   const T* lrow = TR && pa.lam ? static_cast<const T*>(pa.lam) + row0 : drow;
+  const float lam_add = TR && !pa.lam ? 0.5f : 0.0f;      // a missing lam reads 0 through the empty resource
+  if constexpr (TR) {
+    if (c == 0) trap_seed(h, pa, pro, delta, b, L, d_inner, d, n0);
+  }
 
   // Loads of token block bb.  Rows past the chunk's end are clamped onto its
-  // last token, and their delta is read through an empty resource (0).
+  // last token, and their delta is read through an empty resource (0).  With
+  // TR also: delta and lam of the token after the block (0 past the
+  // sequence's end), and for the block's C_t . B_t products lane l's pair of
+  // states 2 (l & 7) + {0, 1} of token bb + (l >> 3), B and C.
   auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&ll)[kTok], T (&xff)[F],
-                        T (&zff)[F]) {
+                        T (&zff)[F], T& dn, T& ln, Pair<T>& pb, Pair<T>& pc) {
     const int64_t o = (int64_t)bb * d_inner;
     const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), r0 = rsrc(drow, 0);
     const auto rl = TR && pa.lam ? rsrc(lrow + o) : r0;
@@ -293,6 +314,15 @@ __global__ __launch_bounds__(64 * K) void k_scan(
       buf_load(xx[j], rx, lb, so);
       if constexpr (K == 1) buf_load(zz[j], rz, lb, so);
       if constexpr (TR) buf_load(ll[j], rl, lb, so);
+    }
+    if constexpr (TR) {
+      const bool next = t0 + bb + kTok < L;
+      buf_load(dn, next ? rd : r0, lb, kTok * rowb);
+      buf_load(ln, next ? rl : r0, lb, kTok * rowb);
+      const int jj = std::min(lane >> 3, nt - 1 - bb);
+      const uint32_t vo = (uint32_t)(jj * NSTATE + 2 * (lane & 7)) * sizeof(T);
+      pb.load(rsrc(brow + (int64_t)bb * NSTATE), vo);
+      pc.load(rsrc(crow + (int64_t)bb * NSTATE), vo);
     }
     if constexpr (K > 1) {
 #pragma unroll
@@ -316,30 +346,48 @@ __global__ __launch_bounds__(64 * K) void k_scan(
     if (!CONV || bb + j < nt) buf_store(to_io(fmaf(Dd, xv, acc) * silu(zv), T()), ry, lb, so);
   };
   auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
-                      const T (&ll)[kTok], const T (&xff)[F], const T (&zff)[F]) {
+                      const T (&ll)[kTok], const T (&xff)[F], const T (&zff)[F], const T& dn, const T& ln,
+                      const Pair<T>& pb, const Pair<T>& pc) {
     const auto ry = rsrc(yrow + (int64_t)bb * d_inner);
     float part[kTok];
+    // TR: delta and lam of the block's tokens and of the one after it (a
+    // padding token's or a missing one's delta is 0), and C_t . B_t summed
+    // over the 8 lanes of each token (lane 8 j holds token j's).
+    float dtv[kTok + 1], lv[kTok + 1], cbl = 0.0f;
+    if constexpr (TR) {
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) {
+        dtv[j] = bb + j < nt ? pro.dt(widen(dd[j])) : 0.0f;
+        lv[j] = widen(ll[j]) + lam_add;
+      }
+      dtv[kTok] = t0 + bb + kTok < L ? pro.dt(widen(dn)) : 0.0f;
+      lv[kTok] = widen(ln) + lam_add;
+      cbl = pb.dot(pc);
+      cbl += dpp_mov<0xB1>(cbl);        // lane ^ 1
+      cbl += dpp_mov<0x4E>(cbl);        // lane ^ 2
+      cbl += dpp_mov<0x141>(cbl);       // lane ^ 7 within 8 lanes
+    }
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
       // A padding token's delta reads 0; softplus would turn that into a
       // positive step, so it is forced back to 0 (a wave-uniform select).
-      const float dt = SP ? (bb + j < nt ? pro.dt(widen(dd[j])) : 0.0f) : widen(dd[j]);
+      const float dt = TR ? dtv[j] : SP ? (bb + j < nt ? pro.dt(widen(dd[j])) : 0.0f) : widen(dd[j]);
       const float xv = pro.xin(widen(xx[j]));
-      float dx, wv;
-      tp.weights(dt, xv, TR ? widen(ll[j]) : 0.0f, &dx, &wv);
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        if constexpr (TR) h[s] = fmaf(fast_exp2(dt * a2[s]), fmaf(wv, tp.Bp[s], h[s]), dx * Bc[s]);
-        else h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bc[s]);
+      float dx = dt * xv, wn = 0.0f;
+      if constexpr (TR) {
+        wn = dtv[j + 1] * (1.0f - lv[j + 1]) * xv;        // w_{t+1}
+        dx = fmaf(dx, lv[j], wn);                          // dt lam x + w_{t+1}
       }
+#pragma unroll
+      for (int s = 0; s < S; ++s) h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bc[s]);
       float acc = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) acc = fmaf(Cv[s], h[s], acc);
+      if constexpr (TR) acc = fmaf(-wn, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbl), 8 * j)), acc);
       if constexpr (K == 1) finish(ry, bb, j, acc, xv, widen(zz[j]));
       else part[j] = acc;
-      if constexpr (TR) { tp.xprev = xv; tp.Bp = Bc; }
       Bc = Bn;
       // Keep each token's scalar B/C loads in its own token: hoisting them
       // across tokens would hold several rows in SGPRs at once and spill.
@@ -364,20 +412,21 @@ __global__ __launch_bounds__(64 * K) void k_scan(
   };
 
   // Two register sets in turn: block i+1 is in flight while block i computes.
-  T dA[kTok], xA[kTok], zA[kTok], lA[kTok], fxA[F], fzA[F];
-  T dB[kTok], xB[kTok], zB[kTok], lB[kTok], fxB[F], fzB[F];
-  load_block(0, dA, xA, zA, lA, fxA, fzA);
+  T dA[kTok], xA[kTok], zA[kTok], lA[kTok], fxA[F], fzA[F], dnA, lnA;
+  T dB[kTok], xB[kTok], zB[kTok], lB[kTok], fxB[F], fzB[F], dnB, lnB;
+  Pair<T> pbA, pcA, pbB, pcB;
+  load_block(0, dA, xA, zA, lA, fxA, fzA, dnA, lnA, pbA, pcA);
   Bc.load(brow);
   __builtin_amdgcn_s_waitcnt(0);
   // Prefetches past the chunk's end are clamped to its last block (valid rows,
   // values unused), so every row offset below stays non-negative.
   const int last = (nt - 1) / kTok * kTok;
   for (int base = 0; base < nt; base += 2 * kTok) {
-    load_block(std::min(base + kTok, last), dB, xB, zB, lB, fxB, fzB);
-    do_block(base, dA, xA, zA, lA, fxA, fzA);
+    load_block(std::min(base + kTok, last), dB, xB, zB, lB, fxB, fzB, dnB, lnB, pbB, pcB);
+    do_block(base, dA, xA, zA, lA, fxA, fzA, dnA, lnA, pbA, pcA);
     if (base + kTok >= nt) break;
-    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, lA, fxA, fzA);
-    do_block(base + kTok, dB, xB, zB, lB, fxB, fzB);
+    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, lA, fxA, fzA, dnA, lnA, pbA, pcA);
+    do_block(base + kTok, dB, xB, zB, lB, fxB, fzB, dnB, lnB, pbB, pcB);
   }
   if (hT && c == n_chunks - 1 && lo == lane) {
     float* ho = hT + (b * d_inner + d) * NSTATE + n0;

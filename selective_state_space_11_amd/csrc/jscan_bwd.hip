@@ -76,11 +76,6 @@ __device__ __forceinline__ const T* opaque_ptr(const T* p) {
   return p;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
 // Sum of v[n] over the 64 lanes of the wave for each n; lane i returns the sum
 // for n = i >> 2.  Each step pairs every lane with a partner, keeps half of
 // its values and adds the partner's copy of them:
