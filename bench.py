@@ -8,8 +8,9 @@ MI355X HBM roofline those algorithmic bytes reach, the roofline of the main
 scan kernel (timed on its own with HIP events recorded by the library on the
 launch stream), a decode-step measurement (256 sequences), the same prefill
 with the fused input prologue (causal conv of width 4 + SiLU, softplus time
-step), the backward (gradient) scan of the same prefill, and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+step), the exponential-trapezoidal recurrence, the backward (gradient) scan
+of the same prefill, and the fp64 CPU oracle timed on a bounded sample of the
+same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -422,6 +423,28 @@ def main():
              "ms_per_step": round(fused_ms, 4), "channel_tokens_per_s": chtok / (fused_ms * 1e-3)}
     log(f"[bench] fused prologue prefill {fused_ms:.4f} ms")
 
+    # the exponential-trapezoidal recurrence on the same inputs (lam ~ U(0,1), token before the first)
+    lam_np, xp_np, Bp_np = synth.trap_inputs(batch, L, d_inner, seed=2)
+    lam_t, xp_t, Bp_t = dio(lam_np), dio(xp_np), dio(Bp_np)
+    del lam_np
+
+    def trap_step():
+        js.prefill_trap(x, delta, A, B, C, D, z, None, lam=lam_t, x_prev=xp_t, B_prev=Bp_t, y=y, hT=hT,
+                        workspace=ws)
+    for _ in range(2):
+        trap_step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        trap_step()
+    e1.record()
+    torch.cuda.synchronize()
+    trap_ms = e0.elapsed_time(e1) / args.steps
+    trap = {"workload": "the same prefill with the exponential-trapezoidal recurrence (lam per channel-token)",
+            "ms_per_step": round(trap_ms, 4), "channel_tokens_per_s": chtok / (trap_ms * 1e-3)}
+    log(f"[bench] trapezoidal prefill {trap_ms:.4f} ms")
+    del lam_t
+
     # backward of the same prefill, output gradients dy ~ N(0,1), dhT ~ N(0,1)
     backward = None
     if args.backward_steps > 0:
@@ -487,6 +510,7 @@ def main():
                              f"{chtok} channel-tokens per launch"},
         "decode": decode,
         "prefill_fused_prologue": fused,
+        "prefill_trapezoidal": trap,
         "backward": backward,
         "cpu_baseline": cpu,
     }
