@@ -13,6 +13,8 @@ Two implementations of the same definition live here:
   adjoint recurrence, every forward state kept, for training.
 * ``prefill_trap`` (C, ``oracle_prefill_trap``): the exponential-trapezoidal
   variant of the recurrence (Mamba-3's discretisation as read from the pages).
+* ``rmsnorm_inputs`` (C, ``oracle_rmsnorm_inputs``): RMSNorm of the time step
+  and the B, C rows before the scan (Jamba's stabilising normalisation).
 * ``twin.py``: the same loop in numpy, vectorised over channels only, for
   small shapes and as a cross-check of the C code.
 
@@ -67,6 +69,8 @@ def _load():
             lib.oracle_backward.restype = ctypes.c_int
             lib.oracle_prefill_trap.argtypes = [i64, i64, i64, i64] + [dp] * 15
             lib.oracle_prefill_trap.restype = None
+            lib.oracle_rmsnorm_inputs.argtypes = [i64, i64, i64, i64] + [dp] * 6 + [ctypes.c_double] + [dp] * 3
+            lib.oracle_rmsnorm_inputs.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -239,3 +243,22 @@ def prefill_trap(x, delta, A, B, C, D, z, h0=None, lam=None, x_prev=None, B_prev
                                 _ptr(D), _ptr(z), _ptr(h0), _ptr(lam), _ptr(x_prev), _ptr(B_prev), _ptr(y),
                                 _ptr(hT), _ptr(x_last), _ptr(B_last))
     return y, hT, x_last, B_last
+
+
+def rmsnorm_inputs(delta, B, C, w_dt=None, w_B=None, w_C=None, eps=1e-6):
+    """RMSNorm of delta over d_inner and of the B, C rows over d_state, per token
+    (see jscan_oracle.c).  A None weight leaves that tensor unchanged.
+    Returns (delta_out, B_out, C_out), float64."""
+    delta = np.asarray(delta)
+    batch, L, d_inner = delta.shape
+    d_state = np.asarray(B).shape[2]
+    delta = _f64(delta, (batch, L, d_inner), "delta")
+    B = _f64(B, (batch, L, d_state), "B")
+    C = _f64(C, (batch, L, d_state), "C")
+    w_dt = None if w_dt is None else _f64(w_dt, (d_inner,), "w_dt")
+    w_B = None if w_B is None else _f64(w_B, (d_state,), "w_B")
+    w_C = None if w_C is None else _f64(w_C, (d_state,), "w_C")
+    outs = (np.empty_like(delta), np.empty_like(B), np.empty_like(C))
+    _load().oracle_rmsnorm_inputs(batch, L, d_inner, d_state, _ptr(delta), _ptr(B), _ptr(C), _ptr(w_dt), _ptr(w_B),
+                                  _ptr(w_C), float(eps), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]))
+    return outs

@@ -393,3 +393,48 @@ void oracle_prefill_trap(int64_t batch, int64_t L, int64_t d_inner, int64_t d_st
         B_last[b * d_state + n] = L > 0 ? B[(b * L + L - 1) * d_state + n] : (B_prev ? B_prev[b * d_state + n] : 0.0);
   }
 }
+
+/*
+ * RMSNorm of the scan's inputs (test infrastructure, same caveats as above).
+ * Jamba inserts RMSNorm at internal activations of its Mamba layers to stop
+ * loss spikes at scale ("Jamba: A Hybrid Transformer-Mamba Language Model —
+ * 深度解读报告", sections 3.1 and 4.9) without saying which; the reading taken
+ * is the time step and the B and C rows before the scan:
+ *
+ *   RMSNorm(v)_i = v_i / sqrt(mean_j v_j^2 + eps) * w_i
+ *
+ * over the d_inner channels of each token's delta (weights w_dt [d_inner]) and
+ * over the d_state entries of each token's B and C rows (w_B, w_C [d_state]).
+ * A NULL weight leaves that tensor unchanged.  Layouts as for oracle_prefill;
+ * outputs have the inputs' shapes.
+ */
+void oracle_rmsnorm_inputs(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                           const double* delta, const double* B, const double* C,
+                           const double* w_dt, const double* w_B, const double* w_C, double eps,
+                           double* delta_out, double* B_out, double* C_out) {
+  for (int64_t bt = 0; bt < batch * L; ++bt) {
+    const double* dv = delta + bt * d_inner;
+    double* dout = delta_out + bt * d_inner;
+    if (w_dt) {
+      double ss = 0.0;
+      for (int64_t d = 0; d < d_inner; ++d) ss += dv[d] * dv[d];
+      double inv = 1.0 / sqrt(ss / (double)d_inner + eps);
+      for (int64_t d = 0; d < d_inner; ++d) dout[d] = dv[d] * inv * w_dt[d];
+    } else {
+      for (int64_t d = 0; d < d_inner; ++d) dout[d] = dv[d];
+    }
+    const double* rows[2] = {B + bt * d_state, C + bt * d_state};
+    double* outs[2] = {B_out + bt * d_state, C_out + bt * d_state};
+    const double* ws[2] = {w_B, w_C};
+    for (int k = 0; k < 2; ++k) {
+      if (ws[k]) {
+        double ss = 0.0;
+        for (int64_t n = 0; n < d_state; ++n) ss += rows[k][n] * rows[k][n];
+        double inv = 1.0 / sqrt(ss / (double)d_state + eps);
+        for (int64_t n = 0; n < d_state; ++n) outs[k][n] = rows[k][n] * inv * ws[k][n];
+      } else {
+        for (int64_t n = 0; n < d_state; ++n) outs[k][n] = rows[k][n];
+      }
+    }
+  }
+}

@@ -396,3 +396,36 @@ def test_prologue_state_carry_equals_one_call():
     np.testing.assert_array_equal(np.concatenate([xa, xb, xz], axis=1), xc)
     np.testing.assert_array_equal(np.concatenate([da, db, dz], axis=1), dout)
     np.testing.assert_array_equal(sz, st)
+
+
+# ------------------------------------------------------------ input RMSNorm
+def test_rmsnorm_inputs_matches_torch_rms_norm():
+    """Against torch.nn.functional.rms_norm (float64) over the last dimension."""
+    import torch
+    rng = np.random.default_rng(70)
+    delta = rng.standard_normal((2, 7, 40))
+    B = rng.standard_normal((2, 7, 16)) / 4
+    C = rng.standard_normal((2, 7, 16)) * 3
+    w_dt, w_B, w_C = rng.uniform(0.5, 2, 40), rng.uniform(0.5, 2, 16), rng.uniform(0.5, 2, 16)
+    eps = 1e-5
+    d2, B2, C2 = oracle.rmsnorm_inputs(delta, B, C, w_dt, w_B, w_C, eps)
+    ref = lambda v, w: torch.nn.functional.rms_norm(torch.tensor(v), (v.shape[-1],), torch.tensor(w), eps).numpy()
+    np.testing.assert_allclose(d2, ref(delta, w_dt), rtol=1e-13)
+    np.testing.assert_allclose(B2, ref(B, w_B), rtol=1e-13)
+    np.testing.assert_allclose(C2, ref(C, w_C), rtol=1e-13)
+
+
+def test_rmsnorm_inputs_properties():
+    """Unit weights give unit root-mean-square (eps = 0); a positive scale of the
+    input does not change the output; a missing weight leaves the tensor as is."""
+    rng = np.random.default_rng(71)
+    delta = rng.standard_normal((1, 5, 33))
+    B = rng.standard_normal((1, 5, 16))
+    C = rng.standard_normal((1, 5, 16))
+    d2, B2, _ = oracle.rmsnorm_inputs(delta, B, C, np.ones(33), np.ones(16), None, eps=0.0)
+    np.testing.assert_allclose(np.sqrt((d2 ** 2).mean(-1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(np.sqrt((B2 ** 2).mean(-1)), 1.0, rtol=1e-14)
+    d3, B3, C3 = oracle.rmsnorm_inputs(7.5 * delta, 0.01 * B, C, np.ones(33), np.ones(16), None, eps=0.0)
+    np.testing.assert_allclose(d3, d2, rtol=1e-13)
+    np.testing.assert_allclose(B3, B2, rtol=1e-13)
+    assert np.array_equal(C3, C)
