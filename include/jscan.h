@@ -124,7 +124,10 @@ jscan_status jscan_step_batch(int64_t n_seq, int64_t d_inner, int64_t d_state, j
 
 /*
  * Optional input prologue of a Mamba layer, fused into the scan: the steps
- * Mamba-1/2 apply to x and delta before the recurrence.  The "AI Engineering
+ * Mamba-1/2 apply to x and delta before the recurrence, and the RMSNorm Jamba
+ * adds to Mamba-internal activations ("Jamba: A Hybrid Transformer-Mamba
+ * Language Model — 深度解读报告", sections 3.1 and 4.9, which do not say which
+ * activations; here the time step and the B, C rows).  The "AI Engineering
  * from Scratch" Jamba lesson (section "Mamba-3") contrasts Mamba-3's
  * in-recurrence form with the "outer convolution on x_t" of the earlier
  * models; the pages give no kernel width (1..4 here, Mamba's usual 4).
@@ -152,6 +155,16 @@ typedef struct {
   const float* dt_bias;       /* [d_inner] */
   int32_t conv_width;         /* 1..4 */
   int32_t dt_softplus;        /* nonzero: softplus(delta + dt_bias) */
+  /* RMSNorm before everything above, v_i / sqrt(mean_j v_j^2 + rms_eps) * w_i:
+   * of delta over its d_inner channels per token, and of the B and C rows
+   * over their d_state entries per token (NULL weight: not normalised).  The
+   * normalised values are rounded to the I/O dtype, as a separate layer would
+   * store them, into scratch the library allocates and frees stream-ordered.
+   * Not combined with the trapezoidal form (JSCAN_ERR_UNSUPPORTED). */
+  const float* rms_dt_weight; /* [d_inner] */
+  const float* rms_B_weight;  /* [d_state] */
+  const float* rms_C_weight;  /* [d_state] */
+  float rms_eps;
 } jscan_prologue;
 
 /*

@@ -69,7 +69,10 @@ def _load():
             lib.oracle_backward.restype = ctypes.c_int
             lib.oracle_prefill_trap.argtypes = [i64, i64, i64, i64] + [dp] * 15
             lib.oracle_prefill_trap.restype = None
-            lib.oracle_rmsnorm_inputs.argtypes = [i64, i64, i64, i64] + [dp] * 6 + [ctypes.c_double] + [dp] * 3
+            lib.oracle_rmsnorm_inputs.argtypes = ([i64, i64, i64, i64] + [dp] * 6 + [ctypes.c_double, ctypes.c_int]
+                                                  + [dp] * 3)
+            lib.oracle_round.argtypes = [ctypes.c_double, ctypes.c_int]
+            lib.oracle_round.restype = ctypes.c_double
             lib.oracle_rmsnorm_inputs.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
@@ -245,9 +248,18 @@ def prefill_trap(x, delta, A, B, C, D, z, h0=None, lam=None, x_prev=None, B_prev
     return y, hT, x_last, B_last
 
 
-def rmsnorm_inputs(delta, B, C, w_dt=None, w_B=None, w_C=None, eps=1e-6):
+ROUND = {None: 0, "bf16": 1, "f32": 2}
+
+
+def round_value(v, to):
+    """One value rounded as the oracle rounds normalised inputs ("bf16", "f32")."""
+    return _load().oracle_round(float(v), ROUND[to])
+
+
+def rmsnorm_inputs(delta, B, C, w_dt=None, w_B=None, w_C=None, eps=1e-6, round_to=None):
     """RMSNorm of delta over d_inner and of the B, C rows over d_state, per token
-    (see jscan_oracle.c).  A None weight leaves that tensor unchanged.
+    (see jscan_oracle.c).  A None weight leaves that tensor unchanged; round_to
+    ("bf16", "f32" or None) rounds the normalised values to the I/O dtype.
     Returns (delta_out, B_out, C_out), float64."""
     delta = np.asarray(delta)
     batch, L, d_inner = delta.shape
@@ -260,5 +272,6 @@ def rmsnorm_inputs(delta, B, C, w_dt=None, w_B=None, w_C=None, eps=1e-6):
     w_C = None if w_C is None else _f64(w_C, (d_state,), "w_C")
     outs = (np.empty_like(delta), np.empty_like(B), np.empty_like(C))
     _load().oracle_rmsnorm_inputs(batch, L, d_inner, d_state, _ptr(delta), _ptr(B), _ptr(C), _ptr(w_dt), _ptr(w_B),
-                                  _ptr(w_C), float(eps), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]))
+                                  _ptr(w_C), float(eps), ROUND[round_to], _ptr(outs[0]), _ptr(outs[1]),
+                                  _ptr(outs[2]))
     return outs

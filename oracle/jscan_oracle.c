@@ -407,11 +407,38 @@ void oracle_prefill_trap(int64_t batch, int64_t L, int64_t d_inner, int64_t d_st
  * over the d_state entries of each token's B and C rows (w_B, w_C [d_state]).
  * A NULL weight leaves that tensor unchanged.  Layouts as for oracle_prefill;
  * outputs have the inputs' shapes.
+ *
+ * The normalisation is read as a layer of its own whose output is stored in
+ * the model's I/O dtype before the scan reads it: round_to = 1 rounds each
+ * normalised value to float32 and then to bfloat16 (both round to nearest,
+ * ties to even), 2 rounds to float32, 0 keeps fp64.
  */
+static double to_f32(double v) { return (double)(float)v; }
+
+static double to_bf16(double v) {
+  float f = (float)v;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7f800000u) == 0x7f800000u) {           /* inf or NaN: keep (quiet NaN) */
+    if (u & 0x007fffffu) u |= 0x00400000u;
+    u &= 0xffff0000u;
+  } else {
+    uint32_t rest = u & 0xffffu, keep = u >> 16;
+    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;
+    u = keep << 16;
+  }
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+double oracle_round(double v, int round_to) {
+  return round_to == 1 ? to_bf16(v) : round_to == 2 ? to_f32(v) : v;
+}
+
 void oracle_rmsnorm_inputs(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
                            const double* delta, const double* B, const double* C,
                            const double* w_dt, const double* w_B, const double* w_C, double eps,
-                           double* delta_out, double* B_out, double* C_out) {
+                           int round_to, double* delta_out, double* B_out, double* C_out) {
   for (int64_t bt = 0; bt < batch * L; ++bt) {
     const double* dv = delta + bt * d_inner;
     double* dout = delta_out + bt * d_inner;
@@ -419,7 +446,7 @@ void oracle_rmsnorm_inputs(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
       double ss = 0.0;
       for (int64_t d = 0; d < d_inner; ++d) ss += dv[d] * dv[d];
       double inv = 1.0 / sqrt(ss / (double)d_inner + eps);
-      for (int64_t d = 0; d < d_inner; ++d) dout[d] = dv[d] * inv * w_dt[d];
+      for (int64_t d = 0; d < d_inner; ++d) dout[d] = oracle_round(dv[d] * inv * w_dt[d], round_to);
     } else {
       for (int64_t d = 0; d < d_inner; ++d) dout[d] = dv[d];
     }
@@ -431,7 +458,7 @@ void oracle_rmsnorm_inputs(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
         double ss = 0.0;
         for (int64_t n = 0; n < d_state; ++n) ss += rows[k][n] * rows[k][n];
         double inv = 1.0 / sqrt(ss / (double)d_state + eps);
-        for (int64_t n = 0; n < d_state; ++n) outs[k][n] = rows[k][n] * inv * ws[k][n];
+        for (int64_t n = 0; n < d_state; ++n) outs[k][n] = oracle_round(rows[k][n] * inv * ws[k][n], round_to);
       } else {
         for (int64_t n = 0; n < d_state; ++n) outs[k][n] = rows[k][n];
       }

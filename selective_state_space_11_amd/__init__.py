@@ -51,7 +51,9 @@ class Prologue(ctypes.Structure):
     """struct jscan_prologue (device pointers as integers)."""
     _fields_ = [("conv_weight", ctypes.c_void_p), ("conv_bias", ctypes.c_void_p),
                 ("conv_state_in", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p),
-                ("dt_bias", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("dt_softplus", ctypes.c_int32)]
+                ("dt_bias", ctypes.c_void_p), ("conv_width", ctypes.c_int32), ("dt_softplus", ctypes.c_int32),
+                ("rms_dt_weight", ctypes.c_void_p), ("rms_B_weight", ctypes.c_void_p),
+                ("rms_C_weight", ctypes.c_void_p), ("rms_eps", ctypes.c_float)]
 
 
 class JscanUnavailable(RuntimeError):
@@ -269,7 +271,9 @@ def step(state, x, delta, A, B, C, D, z, *, y=None, stream=None):
     return y
 
 
-def _prologue(nseq, d_inner, conv_weight, conv_bias, conv_state_in, conv_state_out, dt_bias, softplus):
+def _prologue(nseq, d_inner, conv_weight, conv_bias, conv_state_in, conv_state_out, dt_bias, softplus,
+              rms=None):
+    """rms: None or (w_dt [d_inner] or None, w_B [16] or None, w_C [16] or None, eps)."""
     torch = _torch()
     width = 1
     if conv_weight is not None:
@@ -289,15 +293,26 @@ def _prologue(nseq, d_inner, conv_weight, conv_bias, conv_state_in, conv_state_o
     p.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
     p.conv_width = width
     p.dt_softplus = 1 if softplus else 0
+    if rms is not None:
+        w_dt, w_B, w_C, eps = rms
+        _dev(w_dt, "rms_dt_weight", torch.float32, (d_inner,))
+        _dev(w_B, "rms_B_weight", torch.float32, (D_STATE,))
+        _dev(w_C, "rms_C_weight", torch.float32, (D_STATE,))
+        p.rms_dt_weight = None if w_dt is None else w_dt.data_ptr()
+        p.rms_B_weight = None if w_B is None else w_B.data_ptr()
+        p.rms_C_weight = None if w_C is None else w_C.data_ptr()
+        p.rms_eps = float(eps)
     return p
 
 
 def prefill_fused(x, delta, A, B, C, D, z, h0=None, *, conv_weight=None, conv_bias=None, conv_state_in=None,
-                  conv_state_out=None, dt_bias=None, softplus=False, y=None, hT=None, want_state=True,
+                  conv_state_out=None, dt_bias=None, softplus=False, rms=None, y=None, hT=None, want_state=True,
                   workspace=None, stream=None):
     """prefill with the input prologue: x -> SiLU(causal depthwise conv(x) + conv_bias)
     (conv_weight [d_inner, width], width 1..4; conv_state_in/out [batch, width-1, d_inner],
-    may be one tensor) and, with softplus, delta -> softplus(delta + dt_bias).  Returns (y, hT)."""
+    may be one tensor) and, with softplus, delta -> softplus(delta + dt_bias); rms =
+    (w_dt, w_B, w_C, eps) first applies RMSNorm to delta (over d_inner) and to the B, C rows
+    (over 16), a None weight skipping that tensor.  Returns (y, hT)."""
     torch = _torch()
     lib = load_library()
     _dev(x, "x")
@@ -310,7 +325,7 @@ def prefill_fused(x, delta, A, B, C, D, z, h0=None, *, conv_weight=None, conv_bi
     _dev(A, "A", torch.float32, (d_inner, D_STATE))
     _dev(D, "D", torch.float32, (d_inner,))
     _dev(h0, "h0", torch.float32, (batch, d_inner, D_STATE))
-    pro = _prologue(batch, d_inner, conv_weight, conv_bias, conv_state_in, conv_state_out, dt_bias, softplus)
+    pro = _prologue(batch, d_inner, conv_weight, conv_bias, conv_state_in, conv_state_out, dt_bias, softplus, rms)
     if y is None:
         y = torch.empty_like(x)
     _dev(y, "y", x.dtype, x.shape)
@@ -328,7 +343,7 @@ def prefill_fused(x, delta, A, B, C, D, z, h0=None, *, conv_weight=None, conv_bi
 
 
 def step_batch_fused(state, x, delta, A, B, C, D, z, *, conv_weight=None, conv_bias=None, conv_state=None,
-                     dt_bias=None, softplus=False, y=None, stream=None):
+                     dt_bias=None, softplus=False, rms=None, y=None, stream=None):
     """step_batch with the input prologue; conv_state [n_seq, width-1, d_inner] holds the last
     width-1 raw x of each sequence and is updated in place, like state."""
     torch = _torch()
@@ -344,7 +359,7 @@ def step_batch_fused(state, x, delta, A, B, C, D, z, *, conv_weight=None, conv_b
     _dev(C, "C", x.dtype, (n_seq, D_STATE))
     _dev(A, "A", torch.float32, (d_inner, D_STATE))
     _dev(D, "D", torch.float32, (d_inner,))
-    pro = _prologue(n_seq, d_inner, conv_weight, conv_bias, conv_state, conv_state, dt_bias, softplus)
+    pro = _prologue(n_seq, d_inner, conv_weight, conv_bias, conv_state, conv_state, dt_bias, softplus, rms)
     if y is None:
         y = torch.empty_like(x)
     _dev(y, "y", x.dtype, x.shape)

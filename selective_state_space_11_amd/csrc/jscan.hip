@@ -446,6 +446,58 @@ __global__ __launch_bounds__(64 * K) void k_scan(
   }
 }
 
+// ------------------------------------------------------------ input RMSNorm
+// RMSNorm before the scan, v / sqrt(mean v^2 + eps) * w, fp32 inside and the
+// result rounded to the I/O dtype.  Rows of B and C: one thread per (token,
+// tensor), all 16 entries; a null weight copies the row unchanged.
+template <class T>
+__global__ __launch_bounds__(256) void k_rms_rows(const T* __restrict__ B, const T* __restrict__ C,
+                                                  const float* __restrict__ wB, const float* __restrict__ wC,
+                                                  float eps, T* __restrict__ Bo, T* __restrict__ Co,
+                                                  int64_t rows) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * rows; i += (int64_t)gridDim.x * 256) {
+    const bool isC = i >= rows;
+    const int64_t r = isC ? i - rows : i;
+    const T* src = (isC ? C : B) + r * NSTATE;
+    T* dst = (isC ? Co : Bo) + r * NSTATE;
+    const float* w = isC ? wC : wB;
+    float v[NSTATE], ss = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) {
+      v[n] = widen(src[n]);
+      ss = fmaf(v[n], v[n], ss);
+    }
+    const float inv = w ? 1.0f / sqrtf(ss * (1.0f / NSTATE) + eps) : 1.0f;
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) store_io(dst + n, w ? v[n] * inv * w[n] : v[n]);
+  }
+}
+
+// The time step over the d_inner channels of each token: one workgroup per
+// token row (grid-stride over rows), the sum of squares reduced in-wave by
+// shuffles and across the four waves through LDS.
+template <class T>
+__global__ __launch_bounds__(256) void k_rms_dt(const T* __restrict__ delta, const float* __restrict__ w, float eps,
+                                                T* __restrict__ out, int64_t rows, int64_t d_inner) {
+  __shared__ float part[4];
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const T* src = delta + row * d_inner;
+    T* dst = out + row * d_inner;
+    float ss = 0.0f;
+    for (int64_t d = threadIdx.x; d < d_inner; d += 256) {
+      const float v = widen(src[d]);
+      ss = fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    __syncthreads();                                 // part[] of the previous row is consumed
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d_inner + eps);
+    for (int64_t d = threadIdx.x; d < d_inner; d += 256) store_io(dst + d, widen(src[d]) * inv * w[d]);
+  }
+}
+
 // Copy (or zero) the state for an empty sequence: hT = h0, or 0 when h0 is null.
 __global__ __launch_bounds__(256) void k_copy_state(const float* __restrict__ src, float* __restrict__ dst,
                                                     int64_t n) {
@@ -796,6 +848,10 @@ jscan_status run_step(int64_t n_seq, int64_t d_inner, float* state, const void* 
   return JSCAN_OK;
 }
 
+bool has_rms(const jscan_prologue* pro) {
+  return pro && (pro->rms_dt_weight || pro->rms_B_weight || pro->rms_C_weight);
+}
+
 // Validates the optional prologue and fills `pa`; appends its arrays to the
 // input and output range lists for the alias check.  nseq = batch (prefill)
 // or n_seq (step).
@@ -803,6 +859,16 @@ jscan_status check_prologue(const jscan_prologue* pro, int64_t nseq, int64_t d_i
                             Range* in, int* n_in, Range* out, int* n_out) {
   *pa = ProArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 1};
   if (!pro) return JSCAN_OK;
+  if (has_rms(pro)) {
+    if (!(pro->rms_eps >= 0.0f) || !std::isfinite(pro->rms_eps))
+      return fail(JSCAN_ERR_UNSUPPORTED, "rms_eps must be finite and >= 0");
+    const void* rp[] = {pro->rms_dt_weight, pro->rms_B_weight, pro->rms_C_weight};
+    for (const void* p : rp)
+      if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    in[(*n_in)++] = Range{pro->rms_dt_weight, (size_t)d_inner * 4, "rms_dt_weight"};
+    in[(*n_in)++] = Range{pro->rms_B_weight, NSTATE * 4, "rms_B_weight"};
+    in[(*n_in)++] = Range{pro->rms_C_weight, NSTATE * 4, "rms_C_weight"};
+  }
   if (pro->conv_weight) {
     if (pro->conv_width < 1 || pro->conv_width > 4)
       return fail(JSCAN_ERR_UNSUPPORTED, "conv_width must be 1..4");
@@ -828,12 +894,60 @@ jscan_status check_prologue(const jscan_prologue* pro, int64_t nseq, int64_t d_i
   return JSCAN_OK;
 }
 
+// Normalises delta (over d_inner) and the B, C rows (over d_state) per token
+// into stream-ordered scratch and points delta, B, C at the results; the
+// caller frees *scratch after the scan.
+jscan_status apply_rms(const jscan_prologue* pro, jscan_io io, int64_t nseq, int64_t L, int64_t d_inner,
+                       const void** delta, const void** B, const void** C, void** scratch, hipStream_t st) {
+  *scratch = nullptr;
+  if (!has_rms(pro) || nseq == 0 || L == 0 || d_inner == 0) return JSCAN_OK;
+  const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
+  const int64_t rows = nseq * L;
+  const size_t dbytes = pro->rms_dt_weight ? round_up((size_t)rows * (size_t)d_inner * es) : 0;
+  const size_t rbytes = (pro->rms_B_weight || pro->rms_C_weight) ? round_up((size_t)rows * NSTATE * es) : 0;
+  char* p = nullptr;
+  hipError_t e;
+  if ((e = hipMallocAsync(reinterpret_cast<void**>(&p), dbytes + 2 * rbytes, st)) != hipSuccess)
+    return hip_fail(e, "hipMallocAsync(rmsnorm scratch)");
+  *scratch = p;
+  const unsigned grid_rows = (unsigned)std::min<int64_t>(rows, 1 << 20);
+  if (pro->rms_dt_weight) {
+    if (io == JSCAN_IO_BF16)
+      hipLaunchKernelGGL((k_rms_dt<uint16_t>), dim3(grid_rows), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(*delta), pro->rms_dt_weight, pro->rms_eps,
+                         reinterpret_cast<uint16_t*>(p), rows, d_inner);
+    else
+      hipLaunchKernelGGL((k_rms_dt<float>), dim3(grid_rows), dim3(256), 0, st, static_cast<const float*>(*delta),
+                         pro->rms_dt_weight, pro->rms_eps, reinterpret_cast<float*>(p), rows, d_inner);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
+    *delta = p;
+  }
+  if (rbytes) {
+    char* bo = p + dbytes;
+    char* co = bo + rbytes;
+    const unsigned grid = (unsigned)std::min<int64_t>((2 * rows + 255) / 256, 1 << 20);
+    if (io == JSCAN_IO_BF16)
+      hipLaunchKernelGGL((k_rms_rows<uint16_t>), dim3(grid), dim3(256), 0, st, static_cast<const uint16_t*>(*B),
+                         static_cast<const uint16_t*>(*C), pro->rms_B_weight, pro->rms_C_weight, pro->rms_eps,
+                         reinterpret_cast<uint16_t*>(bo), reinterpret_cast<uint16_t*>(co), rows);
+    else
+      hipLaunchKernelGGL((k_rms_rows<float>), dim3(grid), dim3(256), 0, st, static_cast<const float*>(*B),
+                         static_cast<const float*>(*C), pro->rms_B_weight, pro->rms_C_weight, pro->rms_eps,
+                         reinterpret_cast<float*>(bo), reinterpret_cast<float*>(co), rows);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
+    *B = bo;
+    *C = co;
+  }
+  return JSCAN_OK;
+}
+
 // Validates the optional trapezoidal descriptor (I/O dtype arrays of element
 // size es) and fills its fields of `pa`; appends its inputs to the range list.
-jscan_status check_trap(const jscan_trap* tr, int64_t nseq, int64_t L, int64_t d_inner, size_t es, ProArgs* pa,
-                        Range* in, int* n_in) {
+jscan_status check_trap(const jscan_trap* tr, bool rms, int64_t nseq, int64_t L, int64_t d_inner, size_t es,
+                        ProArgs* pa, Range* in, int* n_in) {
   if (!tr) return JSCAN_OK;
   if (pa->conv_w) return fail(JSCAN_ERR_UNSUPPORTED, "the trapezoidal form takes no convolution prologue");
+  if (rms) return fail(JSCAN_ERR_UNSUPPORTED, "the trapezoidal form takes no RMSNorm prologue");
   const void* ptrs[] = {tr->lam, tr->x_prev, tr->B_prev};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
@@ -867,13 +981,13 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
   const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
   Plan plan = choose_plan(batch, L, d_inner);
   const size_t need = ws_layout(batch, L, d_inner, plan).total;
-  Range in[16] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
+  Range in[20] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
                   {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"}};
   Range out[4] = {{y, tok, "y"}, {hT, stb, "hT"}, {workspace, workspace ? need : 0, "workspace"}};
   int n_in = 8, n_out = 3;
   ProArgs pa;
   if ((s = check_prologue(pro, batch, d_inner, &pa, in, &n_in, out, &n_out)) != JSCAN_OK) return s;
-  if ((s = check_trap(trap, batch, L, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
+  if ((s = check_trap(trap, has_rms(pro), batch, L, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
   // An output may be the very same buffer as one input: hT == h0, or an
   // in-place conv history.
   for (int i = 0; i < n_out; ++i)
@@ -913,24 +1027,36 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
   }
   const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
   if (conv || sp || tr) plan.K = 1;                        // these run with one wave per group
+  const void *dl = delta, *Bs = B, *Cs = C;
+  void* rms_scratch = nullptr;
+  if ((s = apply_rms(pro, io, batch, L, d_inner, &dl, &Bs, &Cs, &rms_scratch, st)) != JSCAN_OK) {
+    if (rms_scratch) (void)hipFreeAsync(rms_scratch, st);
+    return s;
+  }
   char* ws = static_cast<char*>(workspace);
   bool owned = false;
   if (!ws && need > 0) {
-    if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess)
+    if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess) {
+      if (rms_scratch) (void)hipFreeAsync(rms_scratch, st);
       return hip_fail(e, "hipMallocAsync(workspace)");
+    }
     owned = true;
   }
   s = with_flags(conv, sp, tr, [&](auto cv, auto spv, auto trv) {
     constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value;
     return io == JSCAN_IO_BF16
-               ? run_prefill<uint16_t, CV, SPV, TRV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws,
+               ? run_prefill<uint16_t, CV, SPV, TRV>(batch, L, d_inner, x, dl, A, Bs, Cs, D, z, h0, y, hT, ws,
                                                      plan, pa, st)
-               : run_prefill<float, CV, SPV, TRV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws,
+               : run_prefill<float, CV, SPV, TRV>(batch, L, d_inner, x, dl, A, Bs, Cs, D, z, h0, y, hT, ws,
                                                   plan, pa, st);
   });
   if (owned) {
     e = hipFreeAsync(ws, st);
-    if (s == JSCAN_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
+    if (s == JSCAN_OK && e != hipSuccess) s = hip_fail(e, "hipFreeAsync(workspace)");
+  }
+  if (rms_scratch) {
+    e = hipFreeAsync(rms_scratch, st);
+    if (s == JSCAN_OK && e != hipSuccess) s = hip_fail(e, "hipFreeAsync(rmsnorm scratch)");
   }
   return s;
 }
@@ -947,11 +1073,11 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
       t / (NSTATE * 16) > ((int64_t)1 << 37))
     return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
   if (n_seq == 0 || d_inner == 0) {                       // nothing to do; the prologue is still checked
-    Range in[8], out[1];
+    Range in[12], out[1];
     int n_in = 0, n_out = 0;
     ProArgs pa;
     jscan_status s2 = check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out);
-    return s2 != JSCAN_OK ? s2 : check_trap(trap, n_seq, 1, d_inner, 4, &pa, in, &n_in);
+    return s2 != JSCAN_OK ? s2 : check_trap(trap, has_rms(pro), n_seq, 1, d_inner, 4, &pa, in, &n_in);
   }
   if (!state || !x || !delta || !A || !B || !C || !D || !z || !y)
     return fail(JSCAN_ERR_NULL, "every pointer is required");
@@ -962,24 +1088,35 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
   const size_t tok = (size_t)n_seq * (size_t)d_inner * es;
   const size_t rowb = (size_t)n_seq * NSTATE * es;
   const size_t stb = (size_t)n_seq * (size_t)d_inner * NSTATE * 4;
-  Range in[14] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
+  Range in[20] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
                   {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}};
   Range out[3] = {{y, tok, "y"}, {state, stb, "state"}};
   int n_in = 7, n_out = 2;
   ProArgs pa;
   if ((s = check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out)) != JSCAN_OK) return s;
-  if ((s = check_trap(trap, n_seq, 1, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
+  if ((s = check_trap(trap, has_rms(pro), n_seq, 1, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
   if ((s = check_ranges(in, n_in, out, n_out, pa.hist_out && pa.hist_out == pa.hist ? pa.hist : nullptr)) !=
       JSCAN_OK)
     return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
-  return with_flags(conv, sp, tr, [&](auto cv, auto spv, auto trv) {
+  const void *dl = delta, *Bs = B, *Cs = C;
+  void* rms_scratch = nullptr;
+  if ((s = apply_rms(pro, io, n_seq, 1, d_inner, &dl, &Bs, &Cs, &rms_scratch, st)) != JSCAN_OK) {
+    if (rms_scratch) (void)hipFreeAsync(rms_scratch, st);
+    return s;
+  }
+  s = with_flags(conv, sp, tr, [&](auto cv, auto spv, auto trv) {
     constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value;
     return io == JSCAN_IO_BF16
-               ? run_step<uint16_t, CV, SPV, TRV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st)
-               : run_step<float, CV, SPV, TRV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st);
+               ? run_step<uint16_t, CV, SPV, TRV>(n_seq, d_inner, state, x, dl, A, Bs, Cs, D, z, y, pa, st)
+               : run_step<float, CV, SPV, TRV>(n_seq, d_inner, state, x, dl, A, Bs, Cs, D, z, y, pa, st);
   });
+  if (rms_scratch) {
+    const hipError_t e = hipFreeAsync(rms_scratch, st);
+    if (s == JSCAN_OK && e != hipSuccess) s = hip_fail(e, "hipFreeAsync(rmsnorm scratch)");
+  }
+  return s;
 }
 
 }  // namespace jscan_detail

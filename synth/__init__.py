@@ -24,6 +24,8 @@ Recipe (Jamba-shaped inputs: hidden 4096, d_inner 8192, d_state 16):
   conv_weight [d_inner, W] ~ N(0, 1) / sqrt(W), conv_bias [d_inner] ~
   N(0, 1) / 4, conv_state [batch, W-1, d_inner] ~ N(0, 1), dt_bias
   [d_inner] = log(expm1(dt0)) with log dt0 ~ U(log 1e-3, log 1e-1), all fp32.
+  RMSNorm weights (time step [d_inner], B and C rows [d_state]) ~ U(0.5, 1.5)
+  come from ``PCG64([seed, PROLOGUE_STREAM, 2])``.
   Raw (pre-softplus) time steps for tokens [0, L) come from
   ``PCG64([seed, PROLOGUE_STREAM, 1])`` as N(0, 1) [batch, L, d_inner] in the
   I/O dtype.
@@ -188,6 +190,13 @@ def prologue_params(d_inner, width, seed=0, batch=1):
     dt0 = np.exp(g.uniform(np.log(1e-3), np.log(1e-1), size=(d_inner,)))
     dtb = np.log(np.expm1(dt0)).astype(np.float32)
     return {"conv_weight": w, "conv_bias": b, "conv_state": st, "dt_bias": dtb}
+
+
+def rms_weights(d_inner, d_state=16, seed=0):
+    """RMSNorm weights for the time step [d_inner] and the B, C rows [d_state],
+    ~ U(0.5, 1.5) fp32, from PCG64([seed, PROLOGUE_STREAM, 2])."""
+    g = np.random.Generator(np.random.PCG64([seed, PROLOGUE_STREAM, 2]))
+    return tuple(g.uniform(0.5, 1.5, size=(n,)).astype(np.float32) for n in (d_inner, d_state, d_state))
 
 
 def raw_time_steps(batch, L, d_inner, seed=0, io=IO_BF16):

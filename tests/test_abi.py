@@ -211,11 +211,13 @@ def test_binding_fails_loudly_without_library(tmp_path):
 # ------------------------------------------------------------ fused prologue
 def prologue(**over):
     p = dict(conv_weight=fake(11), conv_bias=fake(12), conv_state_in=fake(13), conv_state_out=fake(14),
-             dt_bias=fake(15), conv_width=4, dt_softplus=1)
+             dt_bias=fake(15), conv_width=4, dt_softplus=1, rms_dt_weight=None, rms_B_weight=None,
+             rms_C_weight=None)
     p.update(over)
     s = js.Prologue()
     for k, v in p.items():
         setattr(s, k, v.value if isinstance(v, ctypes.c_void_p) else v)
+    s.rms_eps = 1e-6
     return s
 
 
@@ -355,3 +357,23 @@ def test_prefill_trap_validation(lib):
     assert lib.jscan_step_batch_trap(s["n_seq"], s["d_inner"], s["d_state"], s["io"], s["state"], s["x"],
                                      s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["y"],
                                      ctypes.byref(st), None, None) == ALIAS
+
+
+def test_prologue_rmsnorm_validation(lib):
+    a = prefill_args()
+    base = dict(conv_weight=None, conv_bias=None, conv_state_in=None, conv_state_out=None, dt_bias=None)
+    p = prologue(**base, rms_dt_weight=fake(24), rms_B_weight=fake(25), rms_C_weight=fake(26))
+    p.rms_eps = -1.0
+    assert call_prefill_fused(lib, a, p) == UNSUP                 # eps must be >= 0
+    p.rms_eps = float("nan")
+    assert call_prefill_fused(lib, a, p) == UNSUP
+    p.rms_eps = 1e-6
+    p.rms_B_weight = fake(25).value + 4
+    assert call_prefill_fused(lib, a, p) == ALIGN
+    p.rms_B_weight = fake(8).value                                # weight on top of y
+    assert call_prefill_fused(lib, a, p) == ALIAS
+    # with the trapezoidal form: unsupported
+    q = prologue(**base, rms_dt_weight=fake(24))
+    t = js.Trap()
+    keys = ("batch", "L", "d_inner", "d_state", "io", "x", "delta", "A", "B", "C", "D", "z", "h0", "y", "hT")
+    assert lib.jscan_prefill_trap(*(a[k] for k in keys), ctypes.byref(t), ctypes.byref(q), None, 0, None) == UNSUP

@@ -429,3 +429,19 @@ def test_rmsnorm_inputs_properties():
     np.testing.assert_allclose(d3, d2, rtol=1e-13)
     np.testing.assert_allclose(B3, B2, rtol=1e-13)
     assert np.array_equal(C3, C)
+
+
+def test_oracle_bf16_rounding_matches_torch():
+    """The oracle's rounding of normalised inputs to bf16 (via float32, ties to
+    even) against torch's float32 -> bfloat16 conversion, on values that
+    include exact ties, near ties, subnormals and large magnitudes."""
+    import torch
+    rng = np.random.default_rng(72)
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-40, 38, 4000),
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -2.5,
+                                  1e-40, 3e38, 0.0, -0.0])])
+    got = np.array([oracle.round_value(x, "bf16") for x in v])
+    ref = torch.tensor(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    got32 = np.array([oracle.round_value(x, "f32") for x in v[:100]])
+    assert np.array_equal(got32, v[:100].astype(np.float32).astype(np.float64))

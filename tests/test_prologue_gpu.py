@@ -275,3 +275,102 @@ def test_fused_prefill_64k_sampled():
     assert_y(y[:, :, ch], yr, bf16=True)
     assert_state(hT[:, ch], hr, "hT")
     assert np.array_equal(host64(so)[:, :, ch], st)
+
+
+# ------------------------------------------------------------ input RMSNorm
+EPS = 1e-5
+
+
+def rms_case(inp, pro, seed, which=(True, True, True), width=4, softplus=True):
+    """Oracle: RMSNorm of delta, B, C, then the prologue, then the scan."""
+    w_dt, w_B, w_C = synth.rms_weights(inp["x"].shape[2], seed=seed)
+    ws = tuple(w if k else None for w, k in zip((w_dt, w_B, w_C), which))
+    o = oracle_inputs(inp)
+    # the normalised values are stored in the I/O dtype before the scan reads them
+    rnd = "bf16" if inp["x"].dtype == np.uint16 else "f32"
+    dn, Bn, Cn = oracle.rmsnorm_inputs(o["delta"], o["B"], o["C"], *ws, eps=EPS, round_to=rnd)
+    xc, dt, st = oracle.prologue(o["x"], dn, pro["conv_weight"] if width else None,
+                                 pro["conv_bias"] if width else None, pro["conv_state"] if width else None,
+                                 pro["dt_bias"] if softplus else None, softplus)
+    y, hT = oracle.prefill(xc, dt, o["A"], Bn, Cn, o["D"], o["z"], o["h0"])
+    return ws, y, hT, st
+
+
+def gpu_rms(t, pro, ws, width=4, softplus=True):
+    batch, L, d = t["x"].shape
+    rms = tuple(dev_f32(w) for w in ws) + (EPS,)
+    cs_out = torch.empty((batch, width - 1, d), device="cuda") if width else None
+    y, hT = js.prefill_fused(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                             conv_weight=dev_f32(pro["conv_weight"]) if width else None,
+                             conv_bias=dev_f32(pro["conv_bias"]) if width else None,
+                             conv_state_in=dev_f32(pro["conv_state"]) if width else None, conv_state_out=cs_out,
+                             dt_bias=dev_f32(pro["dt_bias"]) if softplus else None, softplus=softplus, rms=rms)
+    torch.cuda.synchronize()
+    return y, hT, cs_out
+
+
+@pytest.mark.parametrize("chunks", [1, 5])
+@pytest.mark.parametrize("io", [synth.IO_BF16, synth.IO_F32])
+def test_prefill_rmsnorm_conv_softplus(chunks, io):
+    """RMSNorm of delta, B and C, then conv(4) + SiLU and softplus, ragged shape."""
+    print_case(f"rmsnorm + conv + softplus chunks={chunks} io={io}")
+    inp, pro = problem(2, 777, 200, 4, seed=60, io=io)
+    ws, yr, hr, sr = rms_case(inp, pro, seed=60)
+    y, hT, so = with_plan(1, chunks, lambda: gpu_rms(to_device(inp), pro, ws))
+    assert_y(y, yr, bf16=io == synth.IO_BF16)
+    assert_state(hT, hr, "hT")
+    assert np.array_equal(host64(so), sr)
+
+
+@pytest.mark.parametrize("which", [(False, True, False), (True, False, False), (False, False, True)])
+def test_prefill_rmsnorm_one_tensor(which):
+    """Only one of delta, B, C normalised; no conv, no softplus (delta from the
+    scan's own positive recipe)."""
+    print_case(f"rmsnorm {which}")
+    inp, pro = problem(1, 300, 128, 4, seed=61, io=synth.IO_BF16, raw_dt=False)
+    ws, yr, hr, _ = rms_case(inp, pro, seed=61, which=which, width=0, softplus=False)
+    y, hT, _ = gpu_rms(to_device(inp), pro, ws, width=0, softplus=False)
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+
+
+def test_step_rmsnorm_matches_oracle():
+    """Three fused decode steps with RMSNorm, conv history and softplus."""
+    print_case("rmsnorm decode")
+    n_seq, d, width = 3, 200, 4
+    pro = synth.prologue_params(d, width, seed=62, batch=n_seq)
+    w_dt, w_B, w_C = synth.rms_weights(d, seed=62)
+    A, D, _ = synth.params(d, seed=62)
+    st64 = synth.decode_state(n_seq, d, seed=62).astype(np.float64)
+    cs64 = pro["conv_state"].astype(np.float64)
+    state = dev_f32(synth.decode_state(n_seq, d, seed=62))
+    cs = dev_f32(pro["conv_state"])
+    rms = (dev_f32(w_dt), dev_f32(w_B), dev_f32(w_C), EPS)
+    for k in range(3):
+        s = synth.decode_inputs(n_seq, d, seed=62, step=k)
+        s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=200 + k)[:, 0, :]
+        dn, Bn, Cn = oracle.rmsnorm_inputs(synth.widen(s["delta"])[:, None, :], synth.widen(s["B"])[:, None, :],
+                                           synth.widen(s["C"])[:, None, :], w_dt, w_B, w_C, eps=EPS,
+                                           round_to="bf16")
+        xc, dt, cs64 = oracle.prologue(synth.widen(s["x"])[:, None, :], dn, pro["conv_weight"], pro["conv_bias"],
+                                       cs64, pro["dt_bias"], True)
+        yr, st64 = oracle.step(st64, xc[:, 0], dt[:, 0], A.astype(np.float64), Bn[:, 0], Cn[:, 0],
+                               D.astype(np.float64), synth.widen(s["z"]))
+        y = js.step_batch_fused(state, dev_io(s["x"]), dev_io(s["delta"]), dev_f32(A), dev_io(s["B"]),
+                                dev_io(s["C"]), dev_f32(D), dev_io(s["z"]), conv_weight=dev_f32(pro["conv_weight"]),
+                                conv_bias=dev_f32(pro["conv_bias"]), conv_state=cs,
+                                dt_bias=dev_f32(pro["dt_bias"]), softplus=True, rms=rms)
+        torch.cuda.synchronize()
+        assert_y(y, yr, bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+        assert np.array_equal(host64(cs), cs64)
+
+
+def test_prefill_rmsnorm_jamba_shape():
+    """Batch 2 x 4096 x 8192 bf16 with RMSNorm and softplus: every output."""
+    print_case("rmsnorm 2x4096x8192")
+    inp, pro = problem(2, 4096, 8192, 1, seed=63, io=synth.IO_BF16)
+    ws, yr, hr, _ = rms_case(inp, pro, seed=63, width=0)
+    y, hT, _ = gpu_rms(to_device(inp), pro, ws, width=0)
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
