@@ -418,10 +418,26 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     fused_ms = e0.elapsed_time(e1) / args.steps
+    w_dt, w_B, w_C = (torch.from_numpy(w).to(dev) for w in synth.rms_weights(d_inner, seed=2))
+
+    def rms_step():
+        js.prefill_fused(x, delta, A, B, C, D, z, None, y=y, hT=hT, workspace=ws, conv_weight=cw, conv_bias=cb,
+                         conv_state_in=cs, conv_state_out=cso, dt_bias=dtb, softplus=True,
+                         rms=(w_dt, w_B, w_C, 1e-5))
+    for _ in range(2):
+        rms_step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        rms_step()
+    e1.record()
+    torch.cuda.synchronize()
+    rms_ms = e0.elapsed_time(e1) / args.steps
     fused = {"workload": "the same prefill with the input prologue fused (causal depthwise conv width 4 + SiLU "
                          "on x, softplus(delta + dt_bias))",
-             "ms_per_step": round(fused_ms, 4), "channel_tokens_per_s": chtok / (fused_ms * 1e-3)}
-    log(f"[bench] fused prologue prefill {fused_ms:.4f} ms")
+             "ms_per_step": round(fused_ms, 4), "channel_tokens_per_s": chtok / (fused_ms * 1e-3),
+             "with_rmsnorm_ms_per_step": round(rms_ms, 4)}
+    log(f"[bench] fused prologue prefill {fused_ms:.4f} ms, with RMSNorm of delta, B, C {rms_ms:.4f} ms")
 
     # the exponential-trapezoidal recurrence on the same inputs (lam ~ U(0,1), token before the first)
     lam_np, xp_np, Bp_np = synth.trap_inputs(batch, L, d_inner, seed=2)
