@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -132,8 +133,10 @@ def summarize_traffic(pmc_dir, out_md, out_json, command):
         res[k] = r + w
         lines.append(f"| {k} | {r / 1e6:.1f} | {w / 1e6:.1f} | {(r + w) / 1e6:.1f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
+    # the plain main scan: bf16, one wave per 64 channels, every optional stage off
+    plain = [k for k in res if re.fullmatch(r"k_scan<unsigned short, 1(, false)*>", k)]
     data = {"k_scan_64k": {"source_sha": source_digest(),
-                           "hbm_bytes_per_launch": res.get("k_scan<unsigned short, 1, false, false>"),
+                           "hbm_bytes_per_launch": res[plain[0]] if plain else None,
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     json.dump(data, open(out_json, "w"), indent=1)
     return res
