@@ -475,18 +475,31 @@ __global__ __launch_bounds__(256) void k_rms_rows(const T* __restrict__ B, const
 
 // The time step over the d_inner channels of each token: one workgroup per
 // token row (grid-stride over rows), the sum of squares reduced in-wave by
-// shuffles and across the four waves through LDS.
+// shuffles and across the four waves through LDS.  Rows whose byte size is a
+// multiple of 16 move through 16-byte vectors (8 bf16 or 4 fp32 per lane);
+// the second pass re-reads the row from cache.
 template <class T>
 __global__ __launch_bounds__(256) void k_rms_dt(const T* __restrict__ delta, const float* __restrict__ w, float eps,
                                                 T* __restrict__ out, int64_t rows, int64_t d_inner) {
+  constexpr int V = 16 / sizeof(T);                  // elements per 16-byte vector
   __shared__ float part[4];
+  const bool vec = d_inner % V == 0;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const T* src = delta + row * d_inner;
     T* dst = out + row * d_inner;
     float ss = 0.0f;
-    for (int64_t d = threadIdx.x; d < d_inner; d += 256) {
-      const float v = widen(src[d]);
-      ss = fmaf(v, v, ss);
+    if (vec) {
+      for (int64_t d = (int64_t)threadIdx.x * V; d < d_inner; d += 256 * V) {
+        T v[V];
+        *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + d);
+#pragma unroll
+        for (int k = 0; k < V; ++k) ss = fmaf(widen(v[k]), widen(v[k]), ss);
+      }
+    } else {
+      for (int64_t d = threadIdx.x; d < d_inner; d += 256) {
+        const float v = widen(src[d]);
+        ss = fmaf(v, v, ss);
+      }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
@@ -494,7 +507,17 @@ __global__ __launch_bounds__(256) void k_rms_dt(const T* __restrict__ delta, con
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d_inner + eps);
-    for (int64_t d = threadIdx.x; d < d_inner; d += 256) store_io(dst + d, widen(src[d]) * inv * w[d]);
+    if (vec) {
+      for (int64_t d = (int64_t)threadIdx.x * V; d < d_inner; d += 256 * V) {
+        T v[V];
+        *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + d);
+#pragma unroll
+        for (int k = 0; k < V; ++k) v[k] = to_io(widen(v[k]) * inv * w[d + k], T());
+        *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(v);
+      }
+    } else {
+      for (int64_t d = threadIdx.x; d < d_inner; d += 256) store_io(dst + d, widen(src[d]) * inv * w[d]);
+    }
   }
 }
 

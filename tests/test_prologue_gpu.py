@@ -322,12 +322,14 @@ def test_prefill_rmsnorm_conv_softplus(chunks, io):
     assert np.array_equal(host64(so), sr)
 
 
+@pytest.mark.parametrize("d", [128, 100])
 @pytest.mark.parametrize("which", [(False, True, False), (True, False, False), (False, False, True)])
-def test_prefill_rmsnorm_one_tensor(which):
+def test_prefill_rmsnorm_one_tensor(which, d):
     """Only one of delta, B, C normalised; no conv, no softplus (delta from the
-    scan's own positive recipe)."""
-    print_case(f"rmsnorm {which}")
-    inp, pro = problem(1, 300, 128, 4, seed=61, io=synth.IO_BF16, raw_dt=False)
+    scan's own positive recipe).  d_inner 100 is not a whole number of 16-byte
+    vectors of bf16, so the time step's normalisation takes its scalar path."""
+    print_case(f"rmsnorm {which} d={d}")
+    inp, pro = problem(1, 300, d, 4, seed=61, io=synth.IO_BF16, raw_dt=False)
     ws, yr, hr, _ = rms_case(inp, pro, seed=61, which=which, width=0, softplus=False)
     y, hT, _ = gpu_rms(to_device(inp), pro, ws, width=0, softplus=False)
     assert_y(y, yr, bf16=True)
