@@ -18,6 +18,9 @@ Entry points mirror the C ABI in ``include/jscan.h``:
   recurrence (Mamba-3's discretisation as read from the pages)
 * ``backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None)`` -> dict of the
   gradients dx, ddelta, dz, dA, dB, dC, dD, dh0
+* ``selective_scan(x, delta, A, B, C, D, z, h0=None)`` -> ``(y, hT)`` with
+  torch autograd support: forward through jscan_prefill, backward through
+  jscan_backward (recomputing the forward states; nothing else is saved)
 * ``workspace_size``, ``plan``, ``set_plan_override``, ``time_next_prefill``
 """
 from __future__ import annotations
@@ -488,3 +491,42 @@ def step_batch_trap(state, x, delta, A, B, C, D, z, *, lam=None, x_prev=None, B_
                                      _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), ctypes.byref(tr),
                                      ctypes.byref(pro), _stream(stream)))
     return y
+
+
+_ScanFn = None
+
+
+def _scan_fn():
+    """torch.autograd.Function pairing jscan_prefill with jscan_backward (built
+    on first use so that importing this module does not import torch)."""
+    global _ScanFn
+    if _ScanFn is not None:
+        return _ScanFn
+    torch = _torch()
+
+    class ScanFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, delta, A, B, C, D, z, h0):
+            y, hT = prefill(x, delta, A, B, C, D, z, h0)
+            ctx.save_for_backward(x, delta, A, B, C, D, z, h0)
+            ctx.has_h0 = h0 is not None
+            return y, hT
+
+        @staticmethod
+        def backward(ctx, dy, dhT):
+            x, delta, A, B, C, D, z, h0 = ctx.saved_tensors
+            if dy is None:
+                dy = torch.zeros_like(x)
+            g = backward(x, delta, A, B, C, D, z, dy.contiguous(), h0 if ctx.has_h0 else None,
+                         None if dhT is None else dhT.contiguous(), want_dh0=ctx.has_h0)
+            return (g["dx"], g["ddelta"], g["dA"], g["dB"].to(B.dtype), g["dC"].to(C.dtype), g["dD"], g["dz"],
+                    g["dh0"] if ctx.has_h0 else None)
+
+    _ScanFn = ScanFn
+    return ScanFn
+
+
+def selective_scan(x, delta, A, B, C, D, z, h0=None):
+    """Differentiable prefill: (y, hT) = prefill(...), with gradients for every
+    input from jscan_backward.  dB and dC are returned in B's and C's dtype."""
+    return _scan_fn().apply(x, delta, A, B, C, D, z, h0)

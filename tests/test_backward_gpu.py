@@ -190,3 +190,21 @@ def test_backward_64k_sampled():
         assert_y(g[k][:, L - W:], ref[k], bf16=True, what=f"{k} (last {W})")
     for k in ("dB", "dC"):
         assert_state(g[k][:, L - W:], ref[k], f"{k} (last {W})")
+
+
+def test_autograd_function_matches_oracle():
+    """selective_scan through torch.autograd: a loss sum(y * dy) + sum(hT * dhT)
+    gives the oracle's gradients for every input."""
+    print_case("autograd selective_scan")
+    inp, dy, dhT = problem(2, 300, 136, seed=38, io=synth.IO_F32)
+    t = {k: (v.clone().requires_grad_(True) if v is not None else None) for k, v in to_device(inp).items()}
+    y, hT = js.selective_scan(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"])
+    ((y * dev_io(dy)).sum() + (hT * dev_f32(dhT)).sum()).backward()
+    torch.cuda.synchronize()
+    ref = oracle_grads(inp, dy, dhT)
+    names = {"x": "dx", "delta": "ddelta", "z": "dz", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "h0": "dh0"}
+    for k, gname in names.items():
+        if gname in TOKEN_GRADS:
+            assert_y(t[k].grad, ref[gname], bf16=False, what=gname)
+        else:
+            assert_state(t[k].grad, ref[gname], gname)
