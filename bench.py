@@ -142,6 +142,56 @@ def summarize_traffic(pmc_dir, out_md, out_json, command):
     return res
 
 
+def summarize_counters(pmc_dir, out_md, command, trace_db=None):
+    """Per-kernel medians of every SQ_/GRBM_ counter found in the rocprofv3
+    --pmc runs under pmc_dir (one sub-folder per run), with the VALU issue
+    figures derived from them.
+
+    A VALU wave instruction covers 64 lanes.  A transcendental (exp2, log2,
+    rcp) takes the issue time of four plain fp32 instructions, so the fp32
+    slot count is SQ_INSTS_VALU + 3 * SQ_INSTS_VALU_TRANS_F32.  The chip's
+    plain fp32 rate is 157.3e12 / 2 lane-instructions per second."""
+    import glob
+    per = {}
+    for db in sorted(glob.glob(os.path.join(pmc_dir, "*", "run_results.db"))):
+        rows = _db_rows(db, "select name, dispatch_id, counter_name, counter_value from pmc_events")
+        acc = {}
+        for name, disp, cname, val in rows:
+            key = (_short(name), cname)
+            acc.setdefault(key, {}).setdefault(disp, 0.0)
+            acc[key][disp] += val
+        for (k, c), v in acc.items():
+            vals = sorted(v.values())
+            per.setdefault(k, {})[c] = vals[len(vals) // 2]
+    durs = {}
+    if trace_db:
+        for name, dur in _db_rows(trace_db, "select name, duration from kernels"):
+            durs.setdefault(_short(name), []).append(dur / 1e9)
+    counters = sorted({c for v in per.values() for c in v})
+    lines = ["# SQ counters per dispatch (rocprofv3 --pmc, median over dispatches)", "",
+             "Commands (on the MI355X box, from the repository root):", "", "```", command, "```", "",
+             "`fp32 slots` = SQ_INSTS_VALU + 3 x SQ_INSTS_VALU_TRANS_F32 (a transcendental issues in the time "
+             "of four plain instructions), in wave instructions of 64 lanes. `VALU issue` = fp32 slots x 64 / "
+             "(median kernel-trace duration x 78.65e12 lane-instructions/s), the fraction of the chip's plain "
+             "fp32 issue rate the kernel kept busy (trace durations include the profiler's own overhead).", "",
+             "| kernel | " + " | ".join(counters) + " | fp32 slots | VALU issue |",
+             "|---|" + "---|" * (len(counters) + 2)]
+    order = sorted(per, key=lambda k: -per[k].get("SQ_INSTS_VALU", 0.0))
+    for k in order:
+        if k.startswith("__amd") or k.startswith("at::"):
+            continue
+        v = per[k]
+        slots = v.get("SQ_INSTS_VALU", 0.0) + 3 * v.get("SQ_INSTS_VALU_TRANS_F32", 0.0)
+        busy = ""
+        if k in durs and slots and "SQ_INSTS_VALU_TRANS_F32" in v:
+            d = sorted(durs[k])[len(durs[k]) // 2]
+            busy = f"{slots * 64 / (d * 78.65e12):.3f}"
+        cells = [f"{v[c]:.4g}" if c in v else "" for c in counters]
+        lines.append(f"| {k} | " + " | ".join(cells) + f" | {slots:.4g} | {busy} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    return per
+
+
 def run_all_configs(log):
     """Time every workload of the task once (GPU) beside the oracle on a sample.
 
@@ -280,6 +330,9 @@ def main():
                          "7-layer hybrid block) with the oracle on a sample; one JSON line each")
     ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR", help="write the HBM traffic summary (no GPU work)")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="write the SQ counter summary of the --pmc runs under PMC_DIR (no GPU work)")
+    ap.add_argument("--trace-db", help="kernel-trace database giving the durations for --summarize-counters")
     ap.add_argument("--out", help="output file of a summary")
     ap.add_argument("--command", default="", help="the profiling command, recorded in a summary")
     args = ap.parse_args()
@@ -289,6 +342,9 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic, args.out, os.path.join(ROOT, "profiles", "traffic.json"),
                           args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.out, args.command, args.trace_db)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -490,7 +546,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        n_ch = 2048
+        n_ch = 4096
         chans = np.arange(0, d_inner, d_inner // n_ch)[:n_ch]
         sub = synth.channel_slice(inp, chans)
         t0 = time.time()
@@ -499,7 +555,7 @@ def main():
         cpu = {"value": n_ch * L / dt, "unit": "channel-tokens/s", "cores": oracle.num_threads(),
                "kind": "oracle",
                "sample": f"{n_ch} of the {d_inner} channels (every {d_inner // n_ch}th) over all {L} tokens "
-                         f"of the same inputs; fp64 C oracle, {dt:.2f} s wall"}
+                         f"of the same inputs; fp64 C oracle, {dt:.2f} s wall on {oracle.num_threads()} threads"}
         log(f"[bench] cpu oracle {cpu['value']:.3e} ch-tok/s on {cpu['cores']} threads")
 
     out = {
