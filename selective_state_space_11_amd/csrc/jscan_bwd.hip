@@ -28,11 +28,13 @@
 //    dhT, giving the adjoint that enters each chunk from the later ones.
 // 4. Per (chunk, 64 channels): a forward sweep (k_bwd_fwd) from the chunk's
 //    starting state writes dz, the dC partial sums and a state checkpoint
-//    every PC tokens; a reverse sweep (k_bwd_rev) takes the chunk's pieces of
-//    PC tokens from the last: it recomputes the piece's states from its
-//    checkpoint (kept in registers) and steps the adjoint back through the
-//    piece, writing dx, ddelta and the dB partial sums and accumulating
-//    dA and dD.
+//    before every kTok-token block; a reverse sweep (k_bwd_rev) takes the
+//    blocks from the last, each as two pieces of PC tokens, the later first:
+//    it recomputes a piece's states from the block's checkpoint (into
+//    registers) and steps the adjoint back through the piece, writing dx,
+//    ddelta and the dB partial sums and accumulating dA.  The recompute of
+//    the later piece passes through the states the earlier one needs; two of
+//    them are kept in LDS for it.
 // 5. Reductions: dB and dC over the 64-channel groups, dA and dD over chunks
 //    and sequences (fixed order, so results are deterministic).
 // dB_t and dC_t are sums over channels: inside a wave a transposing
@@ -56,8 +58,8 @@ namespace {
 using namespace jscan_detail;
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int PC = 4;    // checkpoint interval: tokens whose states the reverse sweep holds in registers
-static_assert(kTok % PC == 0, "a checkpointed block splits into whole pieces");
+constexpr int PC = 4;    // a piece: tokens whose states the reverse sweep holds in registers
+static_assert(kTok == 2 * PC, "a checkpointed block is two pieces");
 
 // A copy of v the compiler cannot see through.  Recomputed decays would
 // otherwise be merged with earlier identical ones and held in registers
@@ -248,7 +250,7 @@ struct BwdArgs {
   float* dBp; float* dCp;  // [b][group][L][16] partial channel sums
   float* dAp; float* dDp;  // [b][chunk][16][d] and [b][chunk][d] partial token sums
   float* dh0;
-  float* ck;               // [b][chunk][piece][16][d] states before each kTok-token piece
+  float* ck;               // [b][chunk][block][16][d] states before each kTok-token block
   int64_t L, d_inner, chunk_len;
   int n_chunks;
 };
@@ -256,7 +258,7 @@ struct BwdArgs {
 // Per-wave coordinates shared by the two sweeps.
 struct WaveTile {
   int lane, lo, c, nt, last;
-  int64_t g, G, gbase, b, d, t0, row0, pieces;
+  int64_t g, G, gbase, b, d, t0, row0, blocks;
   float lf;
   uint32_t lb, rowb;
   template <class T>
@@ -274,7 +276,7 @@ struct WaveTile {
     nt = (int)std::min<int64_t>(a.chunk_len, a.L - t0);
     last = (nt - 1) / kTok * kTok;
     row0 = (b * a.L + t0) * a.d_inner + gbase;
-    pieces = (a.chunk_len + PC - 1) / PC;
+    blocks = (a.chunk_len + kTok - 1) / kTok;
     lb = (uint32_t)lo * sizeof(T);
     rowb = (uint32_t)(a.d_inner * sizeof(T));
   }
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
   const T* crow = Cm + (w.b * a.L + w.t0) * NSTATE;
   // checkpoints and partial sums through buffer instructions: wave-uniform
   // bases, the lane's byte offset and a row offset
-  const float* ckb = a.ck + ((w.b * a.n_chunks + w.c) * w.pieces * NSTATE) * a.d_inner + w.gbase;
+  const float* ckb = a.ck + ((w.b * a.n_chunks + w.c) * w.blocks * NSTATE) * a.d_inner + w.gbase;
   float* dcb = a.dCp + ((w.b * w.G + w.g) * a.L + w.t0) * NSTATE;
   const uint32_t lb4 = (uint32_t)w.lo * 4, qoff = (uint32_t)(w.lane >> 2) * 4;
   const uint32_t nrow4 = (uint32_t)(a.d_inner * 4);
@@ -349,8 +351,8 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
     const auto rdc = rsrc(dcb + (int64_t)bb * NSTATE);
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-      if (j % PC == 0 && bb + j < w.nt) {          // checkpoint: the state before token bb + j
-        const auto rck = rsrc(ckb + (int64_t)((bb + j) / PC) * NSTATE * a.d_inner);
+      if (j == 0) {          // checkpoint: the state before the block's first token
+        const auto rck = rsrc(ckb + (int64_t)(bb / kTok) * NSTATE * a.d_inner);
 #pragma unroll
         for (int n = 0; n < NSTATE; ++n) buf_store(h[n], rck, lb4, (uint32_t)n * nrow4);
       }
@@ -393,12 +395,15 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
   if (w.lo == w.lane) a.dDp[(w.b * a.n_chunks + w.c) * a.d_inner + w.d] = dD;
 }
 
-// Reverse sweep over the token blocks from the last, each as pieces of PC
-// tokens from the last: a piece's states are recomputed from its checkpoint
-// into registers, then the adjoint steps back through the piece.
-// dx, ddelta, dB partials, dA partial, dh0.
+// Reverse sweep over the token blocks from the last.  A block is two pieces
+// of PC tokens, the later first.  The later piece's states are recomputed
+// from the block's checkpoint; that recompute passes through the states
+// after the block's first two tokens, which go to LDS, so the earlier piece
+// needs one step instead of three.  dx, ddelta, dB partials, dA partial, dh0.
+// Three waves per SIMD need at most 168 VGPRs (granule 8 of 512); the bound
+// makes the compiler fit them, spilling one dword per block to scratch.
 template <class T>
-__global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__ Bm, const T* __restrict__ Cm) {
+__global__ __launch_bounds__(64, 3) void k_bwd_rev(BwdArgs a, const T* __restrict__ Bm, const T* __restrict__ Cm) {
   WaveTile w;
   w.init<T>(a);
   float a2[NSTATE];
@@ -412,12 +417,12 @@ __global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__
   // are read with scalar loads
   const T* brow = Bm + (w.b * a.L + w.t0) * NSTATE;
   const T* crow = Cm + (w.b * a.L + w.t0) * NSTATE;
-  const float* ckb = a.ck + ((w.b * a.n_chunks + w.c) * w.pieces * NSTATE) * a.d_inner + w.gbase;
+  const float* ckb = a.ck + ((w.b * a.n_chunks + w.c) * w.blocks * NSTATE) * a.d_inner + w.gbase;
   float* dbb = a.dBp + ((w.b * w.G + w.g) * a.L + w.t0) * NSTATE;
   const uint32_t lb4 = (uint32_t)w.lo * 4, qoff = (uint32_t)(w.lane >> 2) * 4;
   const uint32_t nrow4 = (uint32_t)(a.d_inner * 4);
 
-  float mu[NSTATE], dA[NSTATE];
+  float mu[NSTATE];
   if (w.c == a.n_chunks - 1) {
     const float* mi = a.dhT ? a.dhT + (w.b * a.d_inner + w.d) * NSTATE : nullptr;
 #pragma unroll
@@ -427,9 +432,23 @@ __global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) mu[n] = mi[(int64_t)n * a.d_inner];
   }
-  __shared__ float dA_lds[64 * NSTATE];
+  // LDS indexed (state or quad of states, lane), so that a wave's accesses
+  // are consecutive.  dA is carried here (a register accumulator live across
+  // the block loop costs the kernel about a hundred VGPRs); st holds, per
+  // block, the states after its first and second tokens (4-byte accesses:
+  // 16-byte ones need register quads that cost the kernel VGPRs).
+  __shared__ float4 dA_lds[4 * 64];
+  __shared__ float st_lds[2 * NSTATE * 64];
+  auto put = [&](float* base, const float (&h)[NSTATE]) {
 #pragma unroll
-  for (int n = 0; n < NSTATE; ++n) dA_lds[w.lane * NSTATE + n] = 0.0f;
+    for (int n = 0; n < NSTATE; ++n) base[n * 64 + w.lane] = h[n];
+  };
+  auto get = [&](const float* base, float (&h)[NSTATE]) {
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) h[n] = base[n * 64 + w.lane];
+  };
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dA_lds[q * 64 + w.lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   Row<T, NSTATE> Br, Cv;
   for (int pb = w.last; pb >= 0; pb -= kTok) {
     T v[4][kTok];
@@ -439,34 +458,28 @@ __global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__
     for (int j = 0; j < kTok; ++j) dps[j] = widen(v[3][j]) * silu(widen(v[2][j]));
     const auto rdb = rsrc(dbb + (int64_t)pb * NSTATE);
     const auto rx = rsrc(dxrow + (int64_t)pb * a.d_inner), rd = rsrc(ddrow + (int64_t)pb * a.d_inner);
-    // The block's pieces, the later first, each recomputed from its own
-    // checkpoint (pieces starting past the chunk's end have none).
+    const auto rck = rsrc(ckb + (int64_t)(pb / kTok) * NSTATE * a.d_inner);
+    // the state after token pb + j, from the one before it
+    auto step = [&](float (&h)[NSTATE], int j) {
+      Br.load(brow + (int64_t)std::min(pb + j, w.nt - 1) * NSTATE);
+      const float dt = opaque(widen(v[0][j]));
+      const float dxv = dt * widen(v[1][j]);
 #pragma unroll
-    for (int hb = kTok - PC; hb >= 0; hb -= PC) {
-      if (pb + hb >= w.nt) continue;
-      const auto rck = rsrc(ckb + (int64_t)((pb + hb) / PC) * NSTATE * a.d_inner);
-      float h[NSTATE];
-      // re-read the checkpoint for every piece rather than hold it in registers
+      for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Br[n]);
+    };
+    // the block's checkpoint, read again for each piece rather than held
+    auto load_ck = [&](float (&h)[NSTATE]) {
       uint32_t lbh = lb4;
       asm volatile("" : "+v"(lbh));
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) buf_load(h[n], rck, lbh, (uint32_t)n * nrow4);
-      float hp[PC][NSTATE];            // states before each token of the half
+    };
+    // the adjoint back through the piece at hb, given the states before each
+    // of its tokens
+    auto reverse = [&](int hb, const float (&hp)[PC][NSTATE]) {
       float dAh[NSTATE];
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) dAh[n] = 0.0f;
-#pragma unroll
-      for (int j = hb; j < hb + PC; ++j) {
-        Br.load(brow + (int64_t)std::min(pb + j, w.nt - 1) * NSTATE);
-        const float dt = opaque(widen(v[0][j]));
-        const float dxv = dt * widen(v[1][j]);
-#pragma unroll
-        for (int n = 0; n < NSTATE; ++n) {
-          hp[j - hb][n] = h[n];
-          if (j + 1 < hb + PC) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dxv * Br[n]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
 #pragma unroll
       for (int j = hb + PC - 1; j >= hb; --j) {
         Br.load(brow + (int64_t)std::min(pb + j, w.nt - 1) * NSTATE);
@@ -495,19 +508,58 @@ __global__ __launch_bounds__(64) void k_bwd_rev(BwdArgs a, const T* __restrict__
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // dA is carried in LDS: a register accumulator live across the block
-      // loop costs the kernel about a hundred VGPRs (and an occupancy step)
-      float4* acc = reinterpret_cast<float4*>(&dA_lds[w.lane * NSTATE]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float4 t = acc[q];
+        float4 t = dA_lds[q * 64 + w.lane];
         t.x += dAh[4 * q]; t.y += dAh[4 * q + 1]; t.z += dAh[4 * q + 2]; t.w += dAh[4 * q + 3];
-        acc[q] = t;
+        dA_lds[q * 64 + w.lane] = t;
+      }
+    };
+    {
+      // later piece (tokens PC .. kTok - 1; none past the chunk's end)
+      float h[NSTATE];
+      load_ck(h);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        step(h, j);
+        put(&st_lds[j * NSTATE * 64], h);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (pb + PC < w.nt) {
+        step(h, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(h, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        float hp[PC][NSTATE];          // states before each token of the piece
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+#pragma unroll
+          for (int n = 0; n < NSTATE; ++n) hp[j][n] = h[n];
+          if (j + 1 < PC) step(h, PC + j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        reverse(PC, hp);
       }
     }
-  }
+    {
+      // earlier piece (tokens 0 .. PC - 1)
+      float hp[PC][NSTATE];
+      load_ck(hp[0]);
+      get(&st_lds[0], hp[1]);
+      get(&st_lds[NSTATE * 64], hp[2]);
 #pragma unroll
-  for (int n = 0; n < NSTATE; ++n) dA[n] = dA_lds[w.lane * NSTATE + n];
+      for (int n = 0; n < NSTATE; ++n) hp[3][n] = hp[2][n];
+      step(hp[3], 2);
+      __builtin_amdgcn_sched_barrier(0);
+      reverse(0, hp);
+    }
+  }
+  float dA[NSTATE];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = dA_lds[q * 64 + w.lane];
+    dA[4 * q] = v.x; dA[4 * q + 1] = v.y; dA[4 * q + 2] = v.z; dA[4 * q + 3] = v.w;
+  }
   if (w.lo == w.lane) {
     if (w.c == 0 && a.dh0) {
 #pragma unroll
@@ -572,13 +624,13 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   if (batch <= 0 || L <= 0 || d_inner <= 0) return w;
   const size_t B = (size_t)batch, C = (size_t)p.chunks, Dn = (size_t)d_inner;
   const size_t G = (size_t)((d_inner + 63) / 64);
-  const size_t pieces = (size_t)((p.chunk_len + PC - 1) / PC);
+  const size_t blocks = (size_t)((p.chunk_len + kTok - 1) / kTok);
   w.fwd = ws_layout(batch, L, d_inner, p).total;
   if (p.chunks > 1) {
     w.M = round_up(B * C * NSTATE * Dn * 4);
     w.dsum = round_up(B * C * Dn * 4);
   }
-  w.ck = round_up(B * C * pieces * NSTATE * Dn * 4);
+  w.ck = round_up(B * C * blocks * NSTATE * Dn * 4);
   w.dBp = round_up(B * G * (size_t)L * NSTATE * 4);
   w.dCp = w.dBp;
   w.dAp = round_up(B * C * NSTATE * Dn * 4);
