@@ -536,11 +536,23 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         bwd_ms = e0.elapsed_time(e1) / args.backward_steps
+        # the same gradients from the chunk starting states the prefill left in
+        # its workspace (jscan_backward_saved)
+        step()
+        js.backward(x, delta, A, B, C, D, z, dy, None, dhT, workspace=bws, prefill_workspace=ws, out=grads)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.backward_steps):
+            js.backward(x, delta, A, B, C, D, z, dy, None, dhT, workspace=bws, prefill_workspace=ws, out=grads)
+        e1.record()
+        torch.cuda.synchronize()
+        saved_ms = e0.elapsed_time(e1) / args.backward_steps
         backward = {"workload": "gradients of the same prefill (dx, ddelta, dz, dA, dB, dC, dD, dh0)",
                     "ms_per_step": round(bwd_ms, 4), "channel_tokens_per_s": chtok / (bwd_ms * 1e-3),
                     "over_forward": round(bwd_ms / ms_per_step, 3),
+                    "with_saved_chunk_states_ms_per_step": round(saved_ms, 4),
                     "workspace_GiB": round(bws.numel() / 2 ** 30, 2)}
-        log(f"[bench] backward {bwd_ms:.4f} ms")
+        log(f"[bench] backward {bwd_ms:.4f} ms, from the prefill's saved chunk states {saved_ms:.4f} ms")
         del grads, bws, dy
 
     cpu = None

@@ -273,6 +273,31 @@ jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d
                             void* dx, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
                             float* dh0, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * jscan_backward for a training step that kept the workspace of its forward
+ * call: prefill_workspace is the workspace a jscan_prefill call used (the
+ * plain prefill, not the fused or trapezoidal one) with the same x, delta, A,
+ * B, h0 and sizes, on the same thread's launch plan, unchanged since.  When
+ * the plan runs in chunks, that workspace holds the state before every chunk
+ * (the forward's chunk-local pass and combine), and the backward reads them
+ * there instead of recomputing them; single-chunk plans ignore it (it may then
+ * be NULL).  The gradients equal jscan_backward's bit for bit.
+ *
+ * prefill_workspace: at least jscan_prefill_workspace_size() bytes (read
+ * only; JSCAN_ERR_NULL if NULL for a chunked plan).  workspace: NULL or at
+ * least jscan_backward_workspace_size() - jscan_prefill_workspace_size()
+ * bytes.  Otherwise as jscan_backward; nothing may overlap prefill_workspace.
+ * Breaking the contract above gives wrong gradients, not an error: the
+ * library cannot check what a workspace holds.
+ */
+jscan_status jscan_backward_saved(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                  const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* h0, const void* dy,
+                                  const float* dhT, void* dx, void* ddelta, void* dz, float* dA, float* dB,
+                                  float* dC, float* dD, float* dh0, const void* prefill_workspace,
+                                  size_t prefill_workspace_bytes, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* Static name of a status code. */
 const char* jscan_status_string(jscan_status status);
 

@@ -42,7 +42,7 @@ EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_step", "jscan
            "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
            "jscan_set_plan_override", "jscan_time_next_prefill", "jscan_prefill_fused",
            "jscan_step_batch_fused", "jscan_backward_workspace_size", "jscan_backward", "jscan_prefill_trap",
-           "jscan_step_batch_trap")
+           "jscan_step_batch_trap", "jscan_backward_saved")
 
 
 class Trap(ctypes.Structure):
@@ -122,6 +122,8 @@ def load_library(path: str = LIB_PATH):
         lib.jscan_backward_workspace_size.restype = sz
         lib.jscan_backward.argtypes = [i64, i64, i64, i64, st] + [vp] * 18 + [vp, sz, vp]
         lib.jscan_backward.restype = st
+        lib.jscan_backward_saved.argtypes = [i64, i64, i64, i64, st] + [vp] * 18 + [vp, sz, vp, sz, vp]
+        lib.jscan_backward_saved.restype = st
         _lib = lib
         return lib
 
@@ -377,11 +379,13 @@ def backward_workspace_size(batch, L, d_inner, d_state=D_STATE, io=IO_BF16) -> i
 
 
 def backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None, *, want_dh0=True, out=None, workspace=None,
-             stream=None):
+             prefill_workspace=None, stream=None):
     """Gradients of prefill for output gradients dy (like y) and dhT ([batch, d_inner, 16]
     fp32 or None).  Returns a dict: dx, ddelta, dz (like x), dA [d_inner, 16], dB, dC
     [batch, L, 16], dD [d_inner] (fp32) and dh0 ([batch, d_inner, 16] fp32, or None when
-    want_dh0 is False).  ``out`` may supply any of these tensors."""
+    want_dh0 is False).  ``out`` may supply any of these tensors.  ``prefill_workspace``:
+    the workspace a prefill call over the same inputs used (jscan_backward_saved reads the
+    chunk starting states from it instead of recomputing them)."""
     torch = _torch()
     lib = load_library()
     _dev(x, "x")
@@ -411,11 +415,16 @@ def backward(x, delta, A, B, C, D, z, dy, h0=None, dhT=None, *, want_dh0=True, o
     if workspace is not None:
         _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.jscan_backward(batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                              _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dhT), _ptr(out["dx"]),
-                              _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]),
-                              _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(workspace), ws_bytes,
-                              _stream(stream)))
+    args = (batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(h0), _ptr(dy), _ptr(dhT), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]),
+            _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]))
+    if prefill_workspace is None:
+        _check(lib.jscan_backward(*args, _ptr(workspace), ws_bytes, _stream(stream)))
+    else:
+        _dev(prefill_workspace, "prefill_workspace")
+        pws_bytes = prefill_workspace.numel() * prefill_workspace.element_size()
+        _check(lib.jscan_backward_saved(*args, _ptr(prefill_workspace), pws_bytes, _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
     return out
 
 
@@ -507,9 +516,15 @@ def _scan_fn():
     class ScanFn(torch.autograd.Function):
         @staticmethod
         def forward(ctx, x, delta, A, B, C, D, z, h0):
-            y, hT = prefill(x, delta, A, B, C, D, z, h0)
+            # The prefill's workspace is kept: it holds the chunk starting
+            # states, which the backward then does not recompute.
+            nb = workspace_size(*x.shape, io=_io_of(x))
+            ws = torch.empty(nb, dtype=torch.uint8, device=x.device) if nb else None
+            y, hT = prefill(x, delta, A, B, C, D, z, h0, workspace=ws)
             ctx.save_for_backward(x, delta, A, B, C, D, z, h0)
             ctx.has_h0 = h0 is not None
+            ctx.prefill_ws = ws
+            ctx.plan = (plan(*x.shape), nb)
             return y, hT
 
         @staticmethod
@@ -517,8 +532,13 @@ def _scan_fn():
             x, delta, A, B, C, D, z, h0 = ctx.saved_tensors
             if dy is None:
                 dy = torch.zeros_like(x)
+            # The plan is per thread and autograd may run this on another
+            # thread: the saved states are used only under the same plan.
+            saved = ctx.prefill_ws if (plan(*x.shape), workspace_size(*x.shape, io=_io_of(x))) == ctx.plan else None
             g = backward(x, delta, A, B, C, D, z, dy.contiguous(), h0 if ctx.has_h0 else None,
-                         None if dhT is None else dhT.contiguous(), want_dh0=ctx.has_h0)
+                         None if dhT is None else dhT.contiguous(), want_dh0=ctx.has_h0,
+                         prefill_workspace=saved)
+            ctx.prefill_ws = None
             return (g["dx"], g["ddelta"], g["dA"], g["dB"].to(B.dtype), g["dC"].to(C.dtype), g["dD"], g["dz"],
                     g["dh0"] if ctx.has_h0 else None)
 
@@ -528,5 +548,6 @@ def _scan_fn():
 
 def selective_scan(x, delta, A, B, C, D, z, h0=None):
     """Differentiable prefill: (y, hT) = prefill(...), with gradients for every
-    input from jscan_backward.  dB and dC are returned in B's and C's dtype."""
+    input from jscan_backward_saved (the forward's workspace is kept until the
+    backward).  dB and dC are returned in B's and C's dtype."""
     return _scan_fn().apply(x, delta, A, B, C, D, z, h0)

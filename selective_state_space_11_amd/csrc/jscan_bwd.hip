@@ -643,12 +643,14 @@ template <class T>
 jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io, const void* x, const void* delta,
                           const float* A, const void* B, const void* C, const float* D, const void* z,
                           const float* h0, const void* dy, const float* dhT, void* dx, void* ddelta, void* dz,
-                          float* dA, float* dB, float* dC, float* dD, float* dh0, char* ws, const Plan& p,
-                          hipStream_t st) {
+                          float* dA, float* dB, float* dC, float* dD, float* dh0, char* ws,
+                          const float* saved_hstart, const Plan& p, hipStream_t st) {
   const BwdLayout w = bwd_layout(batch, L, d_inner, p);
   const WsLayout fw = ws_layout(batch, L, d_inner, p);
-  float* hstart = reinterpret_cast<float*>(ws + fw.S + fw.dsum);
-  char* q = ws + w.fwd;
+  // Chunk starting states: those a prefill left in its workspace, or
+  // recomputed into the front of this workspace.
+  const float* hstart = saved_hstart ? saved_hstart : reinterpret_cast<const float*>(ws + fw.S + fw.dsum);
+  char* q = saved_hstart ? ws : ws + w.fwd;
   float* M = reinterpret_cast<float*>(q); q += w.M;
   float* dsum = reinterpret_cast<float*>(q); q += w.dsum;
   float* ck = reinterpret_cast<float*>(q); q += w.ck;
@@ -661,7 +663,9 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
   jscan_status s;
 
   if (p.chunks > 1) {
-    if ((s = forward_chunk_starts(io, batch, L, d_inner, x, delta, A, B, h0, ws, p, st)) != JSCAN_OK) return s;
+    if (!saved_hstart &&
+        (s = forward_chunk_starts(io, batch, L, d_inner, x, delta, A, B, h0, ws, p, st)) != JSCAN_OK)
+      return s;
     dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)(p.chunks - 1), (unsigned)batch);
     hipLaunchKernelGGL((k_adj_local<T>), g1, dim3(256), 0, st, static_cast<const T*>(delta), A,
                        static_cast<const T*>(C), static_cast<const T*>(z), static_cast<const T*>(dy), M, dsum, L,
@@ -687,22 +691,14 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
   return JSCAN_OK;
 }
 
-}  // namespace
-
-// ================================================================ C ABI
-extern "C" {
-
-size_t jscan_backward_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io) {
-  (void)io;
-  if (d_state != NSTATE || !sizes_ok(batch, L, d_inner)) return 0;
-  return bwd_layout(batch, L, d_inner, choose_plan(batch, L, d_inner)).total;
-}
-
-jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
-                            const void* x, const void* delta, const float* A, const void* B, const void* C,
-                            const float* D, const void* z, const float* h0, const void* dy, const float* dhT,
-                            void* dx, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
-                            float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+// jscan_backward (saved = false) and jscan_backward_saved (saved = true:
+// the chunk starting states come from the workspace of the prefill call).
+jscan_status backward_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                           const void* x, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* h0, const void* dy, const float* dhT,
+                           void* dx, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
+                           float* dh0, bool saved, const void* prefill_ws, size_t prefill_ws_bytes,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   t_last_error.clear();
   jscan_status s = check_common(d_state, io);
   if (s != JSCAN_OK) return s;
@@ -721,10 +717,21 @@ jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d
   const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
   const size_t pd = (size_t)d_inner * NSTATE * 4;
   const Plan plan = choose_plan(batch, L, d_inner);
-  const size_t need = bwd_layout(batch, L, d_inner, plan).total;
+  const BwdLayout bl = bwd_layout(batch, L, d_inner, plan);
+  // With saved chunk states the front of the workspace (the prefill's part) is not needed.
+  const bool use_saved = saved && work && plan.chunks > 1;
+  const size_t need = use_saved ? bl.total - bl.fwd : bl.total;
+  const WsLayout fl = ws_layout(batch, L, d_inner, plan);
+  if (use_saved && !prefill_ws)
+    return fail(JSCAN_ERR_NULL, "this plan runs in chunks: the prefill's workspace is required");
+  if (use_saved && !aligned16(prefill_ws))
+    return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  if (use_saved && prefill_ws_bytes < fl.total)
+    return fail(JSCAN_ERR_WORKSPACE, "prefill workspace smaller than jscan_prefill_workspace_size()");
   const Range in[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {dy, tok, "dy"}, {B, rowb, "B"},
                       {C, rowb, "C"}, {A, pd, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"},
-                      {dhT, stb, "dhT"}};
+                      {dhT, stb, "dhT"}, {use_saved ? prefill_ws : nullptr, use_saved ? fl.total : 0,
+                                          "prefill workspace"}};
   const Range out[] = {{dx, tok, "dx"}, {ddelta, tok, "ddelta"}, {dz, tok, "dz"}, {dA, pd, "dA"},
                        {dB, row4, "dB"}, {dC, row4, "dC"}, {dD, (size_t)d_inner * 4, "dD"}, {dh0, stb, "dh0"},
                        {workspace, workspace ? need : 0, "workspace"}};
@@ -732,7 +739,9 @@ jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d
       JSCAN_OK)
     return s;
   if (workspace && workspace_bytes < need)
-    return fail(JSCAN_ERR_WORKSPACE, "workspace smaller than jscan_backward_workspace_size()");
+    return fail(JSCAN_ERR_WORKSPACE, use_saved ? "workspace smaller than jscan_backward_workspace_size() - "
+                                                 "jscan_prefill_workspace_size()"
+                                               : "workspace smaller than jscan_backward_workspace_size()");
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -757,16 +766,50 @@ jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d
       return hip_fail(e, "hipMallocAsync(workspace)");
     owned = true;
   }
+  const float* saved_hstart =
+      use_saved ? reinterpret_cast<const float*>(static_cast<const char*>(prefill_ws) + fl.S + fl.dsum) : nullptr;
   s = io == JSCAN_IO_BF16
           ? run_backward<uint16_t>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz,
-                                   dA, dB, dC, dD, dh0, ws, plan, st)
+                                   dA, dB, dC, dD, dh0, ws, saved_hstart, plan, st)
           : run_backward<float>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz, dA,
-                                dB, dC, dD, dh0, ws, plan, st);
+                                dB, dC, dD, dh0, ws, saved_hstart, plan, st);
   if (owned) {
     e = hipFreeAsync(ws, st);
     if (s == JSCAN_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
   }
   return s;
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" {
+
+size_t jscan_backward_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io) {
+  (void)io;
+  if (d_state != NSTATE || !sizes_ok(batch, L, d_inner)) return 0;
+  return bwd_layout(batch, L, d_inner, choose_plan(batch, L, d_inner)).total;
+}
+
+jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                            const void* x, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const float* h0, const void* dy, const float* dhT,
+                            void* dx, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
+                            float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz, dA,
+                       dB, dC, dD, dh0, false, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+jscan_status jscan_backward_saved(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                  const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* h0, const void* dy,
+                                  const float* dhT, void* dx, void* ddelta, void* dz, float* dA, float* dB,
+                                  float* dC, float* dD, float* dh0, const void* prefill_workspace,
+                                  size_t prefill_workspace_bytes, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return backward_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz, dA,
+                       dB, dC, dD, dh0, true, prefill_workspace, prefill_workspace_bytes, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

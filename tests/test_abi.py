@@ -322,6 +322,35 @@ def test_backward_validation(lib):
     assert call_bwd(lib, bwd_args(workspace=fake(8), ws_bytes=ws)) == ALIAS   # workspace over dy
 
 
+def call_bwd_saved(lib, a):
+    keys = ("batch", "L", "d_inner", "d_state", "io", "x", "delta", "A", "B", "C", "D", "z", "h0", "dy", "dhT",
+            "dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "dh0", "pws", "pws_bytes", "workspace", "ws_bytes",
+            "stream")
+    return lib.jscan_backward_saved(*(a[k] for k in keys))
+
+
+def test_backward_saved_validation(lib):
+    """jscan_backward_saved checks the prefill workspace like any other buffer
+    (required when the plan runs in chunks) and needs a smaller workspace."""
+    try:
+        js.set_plan_override(1, 4)
+        pws = js.workspace_size(1, 64, 128)
+        full = js.backward_workspace_size(1, 64, 128)
+        assert pws > 0 and full > pws
+        sv = lambda **kw: call_bwd_saved(lib, bwd_args(**{"pws": fake(31), "pws_bytes": pws, **kw}))
+        assert sv(pws=None) == NULL                           # chunked plan: the prefill's workspace is required
+        assert sv(pws_bytes=pws - 1) == WS
+        assert sv(pws=fake(31, 4)) == ALIGN
+        assert sv(pws=fake(16)) == ALIAS                      # prefill workspace under dx
+        assert sv(workspace=fake(31, 64)) == ALIAS            # workspace over the prefill workspace
+        assert sv(workspace=fake(30), ws_bytes=full - pws - 1) == WS
+        assert sv(x=None) == NULL
+        assert sv(L=-1) == SHAPE
+        assert sv(d_state=8) == UNSUP
+    finally:
+        js.set_plan_override(0, 0)
+
+
 def test_backward_workspace_size():
     # recomputed states (~8 B per channel-token) and the dB/dC partials dominate
     L, d = 65536, 8192

@@ -147,6 +147,48 @@ def test_backward_chain_rule_across_calls():
     check_all(full, ref, bf16=True)
 
 
+def saved_vs_plain(inp, dy, dhT, chunks=None):
+    """jscan_backward_saved after a prefill that used an explicit workspace,
+    against jscan_backward on the same inputs: the same kernels on the same
+    chunk states, so every output must agree bit for bit."""
+    t = to_device(inp)
+    b, L, d = inp["x"].shape
+
+    def run():
+        pws = torch.empty(max(js.workspace_size(b, L, d), 1), dtype=torch.uint8, device="cuda")
+        js.prefill(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], workspace=pws)
+        rest = js.backward_workspace_size(b, L, d) - js.workspace_size(b, L, d)
+        ws = torch.empty(max(rest, 1), dtype=torch.uint8, device="cuda")
+        g_saved = gpu_grads(t, dy, dhT, prefill_workspace=pws, workspace=ws)
+        g_plain = gpu_grads(t, dy, dhT)
+        return g_saved, g_plain
+
+    g_saved, g_plain = with_plan(chunks, run) if chunks else run()
+    for k in g_plain:
+        assert torch.equal(g_saved[k], g_plain[k]), k
+    return g_saved
+
+
+@pytest.mark.parametrize("chunks", [0, 1, 5])
+def test_backward_saved_states_ragged(chunks):
+    """Two sequences, L 777, d_inner 200, bf16: the saved-state backward equals
+    the recomputing one bit for bit (automatic, single-chunk and 5-chunk plans)
+    and matches the oracle."""
+    print_case(f"bwd saved ragged chunks={chunks}")
+    inp, dy, dhT = problem(2, 777, 200, seed=39, io=synth.IO_BF16)
+    g = saved_vs_plain(inp, dy, dhT, chunks)
+    check_all(g, oracle_grads(inp, dy, dhT), bf16=True)
+
+
+def test_backward_saved_states_jamba_shape():
+    """Batch 2, L 4096, d_inner 8192 (the Jamba prefill shape) in the automatic
+    (chunked) plan: saved-state and recomputing backward agree bit for bit."""
+    print_case("bwd saved 2x4096x8192")
+    inp, dy, dhT = problem(2, 4096, 8192, seed=36, io=synth.IO_BF16, h0=True)
+    assert js.plan(2, 4096, 8192)[1] > 1
+    saved_vs_plain(inp, dy, dhT)
+
+
 def test_backward_jamba_prefill_every_output():
     """Batch 2, L 4096, d_inner 8192 (the Jamba prefill shape), bf16: every
     gradient of every channel and token against the oracle."""
