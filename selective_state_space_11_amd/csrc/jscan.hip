@@ -477,18 +477,33 @@ __global__ __launch_bounds__(256) void k_rms_rows(const T* __restrict__ B, const
 // token row (grid-stride over rows), the sum of squares reduced in-wave by
 // shuffles and across the four waves through LDS.  Rows whose byte size is a
 // multiple of 16 move through 16-byte vectors (8 bf16 or 4 fp32 per lane);
-// the second pass re-reads the row from cache.
+// rows of up to 256 x 4 vectors (8192 bf16 channels) stay in registers
+// between the sum and the scaling, longer ones are read again.
 template <class T>
 __global__ __launch_bounds__(256) void k_rms_dt(const T* __restrict__ delta, const float* __restrict__ w, float eps,
                                                 T* __restrict__ out, int64_t rows, int64_t d_inner) {
   constexpr int V = 16 / sizeof(T);                  // elements per 16-byte vector
+  constexpr int R = 4;                               // vectors a lane can hold
   __shared__ float part[4];
   const bool vec = d_inner % V == 0;
+  const bool held = vec && d_inner <= (int64_t)256 * V * R;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const T* src = delta + row * d_inner;
     T* dst = out + row * d_inner;
     float ss = 0.0f;
-    if (vec) {
+    uint4 buf[R];
+    if (held) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t d = ((int64_t)r * 256 + threadIdx.x) * V;
+        if (d < d_inner) {
+          buf[r] = *reinterpret_cast<const uint4*>(src + d);
+          const T* v = reinterpret_cast<const T*>(&buf[r]);
+#pragma unroll
+          for (int k = 0; k < V; ++k) ss = fmaf(widen(v[k]), widen(v[k]), ss);
+        }
+      }
+    } else if (vec) {
       for (int64_t d = (int64_t)threadIdx.x * V; d < d_inner; d += 256 * V) {
         T v[V];
         *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + d);
@@ -507,7 +522,19 @@ __global__ __launch_bounds__(256) void k_rms_dt(const T* __restrict__ delta, con
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d_inner + eps);
-    if (vec) {
+    if (held) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t d = ((int64_t)r * 256 + threadIdx.x) * V;
+        if (d < d_inner) {
+          T v[V];
+          *reinterpret_cast<uint4*>(v) = buf[r];
+#pragma unroll
+          for (int k = 0; k < V; ++k) v[k] = to_io(widen(v[k]) * inv * w[d + k], T());
+          *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(v);
+        }
+      }
+    } else if (vec) {
       for (int64_t d = (int64_t)threadIdx.x * V; d < d_inner; d += 256 * V) {
         T v[V];
         *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + d);

@@ -336,6 +336,20 @@ def test_prefill_rmsnorm_one_tensor(which, d):
     assert_state(hT, hr, "hT")
 
 
+@pytest.mark.parametrize("io,d", [(synth.IO_BF16, 2056), (synth.IO_BF16, 8200), (synth.IO_F32, 1028),
+                                  (synth.IO_F32, 4100)])
+def test_prefill_rmsnorm_row_lengths(io, d):
+    """The time step's normalisation over rows that a workgroup holds in
+    registers with a partial last group of vectors (2056 bf16, 1028 fp32) and
+    over rows too long to hold, which it reads twice (8200 bf16, 4100 fp32)."""
+    print_case(f"rmsnorm rows io={io} d={d}")
+    inp, pro = problem(1, 40, d, 4, seed=64, io=io, raw_dt=False)
+    ws, yr, hr, _ = rms_case(inp, pro, seed=64, which=(True, False, False), width=0, softplus=False)
+    y, hT, _ = gpu_rms(to_device(inp), pro, ws, width=0, softplus=False)
+    assert_y(y, yr, bf16=io == synth.IO_BF16)
+    assert_state(hT, hr, "hT")
+
+
 def test_step_rmsnorm_matches_oracle():
     """Three fused decode steps with RMSNorm, conv history and softplus."""
     print_case("rmsnorm decode")
