@@ -426,6 +426,21 @@ def main():
     scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     log(f"[bench] step {ms_per_step:.4f} ms, main scan kernel {scan_ms:.4f} ms")
 
+    # the device copy rate on this GPU (1 GiB read and 1 GiB written per copy),
+    # the practical ceiling the HBM fractions are also quoted against
+    csrc = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        cdst.copy_(csrc)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del csrc, cdst
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s")
+
     chtok = batch * L * d_inner
     value = chtok / (ms_per_step * 1e-3)
     abytes = alg_bytes_prefill(batch, L, d_inner)
@@ -456,6 +471,7 @@ def main():
               "channel_tokens_per_s": n_seq * d_inner / (us_step * 1e-6),
               "alg_GBps": round(dec_bytes / (us_step * 1e-6) / 1e9, 1),
               "hbm_frac": round(dec_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+              "frac_of_measured_copy": round(dec_bytes / (us_step * 1e-6) / 1e9 / copy_gbs, 4),
               "note": "the 128 MiB state can stay resident in the 256 MB last-level cache"}
     log(f"[bench] decode {us_step:.2f} us/step")
 
@@ -588,7 +604,9 @@ def main():
                    "batch": batch, "seq_len": L, "d_inner": d_inner, "d_state": D_STATE,
                    "plan": {"waves_per_64_channels": K, "chunks": chunks}},
         "hbm_roofline": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_step": abytes},
+                         "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_step": abytes,
+                         "measured_copy_GBps": round(copy_gbs, 1),
+                         "frac_of_measured_copy": round(hbm_gbs / copy_gbs, 4)},
         "roofline": {"bound": "alu", "kernel": "k_scan (main scan)",
                      "achieved": round(kern_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kern_tflops / VALU_PEAK_TFLOPS, 4),

@@ -600,9 +600,12 @@ __global__ __launch_bounds__(256) void k_reduce_ad(const float* __restrict__ dAp
   const int64_t n = i / d_inner;
   const int64_t d = i - n * d_inner;
   float sa = 0.0f, sd = 0.0f;
-  for (int64_t k = 0; k < slots; ++k) {
-    sa += dAp[k * per + i];
-    if (n == 0) sd += dDp[k * d_inner + d];
+  // unrolled so that several loads are in flight; the adds keep their order
+#pragma unroll 8
+  for (int64_t k = 0; k < slots; ++k) sa += dAp[k * per + i];
+  if (n == 0) {
+#pragma unroll 8
+    for (int64_t k = 0; k < slots; ++k) sd += dDp[k * d_inner + d];
   }
   dA[d * NSTATE + n] = sa;
   if (n == 0) dD[d] = sd;
