@@ -212,7 +212,13 @@ def run_all_configs(log):
         return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
 
     def timed(fn, reps):
-        fn(); torch.cuda.synchronize()
+        # untimed calls for at least 100 ms first: after the inputs are made on
+        # the host the GPU has idled, and its clocks take a while to come up
+        t_end = time.time() + 0.1
+        while True:
+            fn(); torch.cuda.synchronize()
+            if time.time() >= t_end:
+                break
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -317,7 +323,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--L", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=200)
