@@ -1,0 +1,101 @@
+"""GPU parity at the largest sizes the library accepts: d_inner = 2^24 (the
+limit of its 32-bit per-row offsets) and batch = 65535 (the grid's limit).
+
+Inputs follow the scan's seeded recipe (``synth.prefill_inputs``).  At
+d_inner = 2^24 the oracle runs on sampled channels (channels are independent
+given B and C), among them the first, the last and both sides of the 2^23
+boundary; the prefill is checked in the automatic (single-chunk) plan and in a
+forced two-chunk plan, the backward on every per-channel gradient.  The
+batch-65535 problem is small enough to compare every output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import selective_state_space_11_amd as js
+from gpu_util import assert_state, assert_y, dev_f32, dev_io, oracle_inputs, to_device
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only machines, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+DMAX = 1 << 24
+LMAX = 9            # one whole 8-token block and one token of the next
+
+
+def print_case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def widest():
+    print_case(f"generating batch 1 x L {LMAX} x d_inner {DMAX}")
+    inp = synth.prefill_inputs(1, LMAX, DMAX, seed=77, io=synth.IO_BF16, h0=True)
+    rng = np.random.default_rng(77)
+    ch = np.unique(np.concatenate([[0, 1, 63, 64, (1 << 23) - 1, 1 << 23, DMAX - 65, DMAX - 64, DMAX - 1],
+                                   rng.choice(DMAX, 23, replace=False)]))
+    return inp, ch
+
+
+def test_prefill_widest_rows(widest):
+    inp, ch = widest
+    assert js.plan(1, LMAX, DMAX)[1] == 1
+    t = to_device(inp)
+    sub = synth.channel_slice(inp, ch)
+    yr, hr = oracle.prefill(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["h0"])
+    for chunks in (0, 2):
+        print_case(f"prefill d_inner {DMAX} chunks={chunks}")
+        try:
+            if chunks:
+                js.set_plan_override(1, chunks)
+                assert js.plan(1, LMAX, DMAX)[1] == chunks
+            y, hT = js.prefill(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"])
+            torch.cuda.synchronize()
+        finally:
+            js.set_plan_override(0, 0)
+        assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+        assert_y(y[:, :, ch], yr, bf16=True)
+        assert_state(hT[:, ch], hr, "hT")
+        del y, hT
+
+
+def test_backward_widest_rows(widest):
+    inp, ch = widest
+    print_case(f"backward d_inner {DMAX}")
+    t = to_device(inp)
+    dy, dhT = synth.output_grads(1, LMAX, DMAX, seed=77, io=synth.IO_BF16)
+    g = js.backward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], dev_io(dy), t["h0"], dev_f32(dhT))
+    torch.cuda.synchronize()
+    for k in g:
+        assert torch.isfinite(g[k].float()).all(), k
+    sub = synth.channel_slice(inp, ch)
+    ref = oracle.backward(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"],
+                          synth.widen(dy[:, :, ch]), sub["h0"], dhT[:, ch].astype(np.float64))
+    for k in ("dx", "ddelta", "dz"):
+        assert_y(g[k][:, :, ch], ref[k], bf16=True, what=k)
+    assert_state(g["dA"][ch], ref["dA"], "dA")
+    assert_state(g["dD"][ch], ref["dD"], "dD")
+    assert_state(g["dh0"][:, ch], ref["dh0"], "dh0")
+
+
+def test_prefill_and_decode_most_sequences():
+    """batch 65535 (the largest accepted), L 3, d_inner 8: every output of the
+    prefill, then one decode step of every sequence from the prefill's state."""
+    batch, L, d = 65535, 3, 8
+    print_case(f"prefill and decode batch {batch}")
+    inp = synth.prefill_inputs(batch, L + 1, d, seed=78, io=synth.IO_BF16, h0=True)
+    head = {k: (v[:, :L].copy() if k in ("x", "delta", "z", "B", "C") else v) for k, v in inp.items()}
+    t = to_device(head)
+    y, hT = js.prefill(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"])
+    torch.cuda.synchronize()
+    o = oracle_inputs(inp)
+    yr, hr = oracle.prefill(*(o[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")))
+    assert_y(y, yr[:, :L], bf16=True)
+    tok = {k: dev_io(inp[k][:, L]) for k in ("x", "delta", "z", "B", "C")}
+    ys = js.step_batch(hT, tok["x"], tok["delta"], t["A"], tok["B"], tok["C"], t["D"], tok["z"])
+    torch.cuda.synchronize()
+    assert_y(ys, yr[:, L], bf16=True, what="decode y")
+    assert_state(hT, hr, "state after decode")
