@@ -193,7 +193,7 @@ def summarize_counters(pmc_dir, out_md, command, trace_db=None):
 
 
 def run_all_configs(log):
-    """Time every workload of the task once (GPU) beside the oracle on a sample.
+    """Time every workload once (GPU) beside the oracle on a sample.
 
     Prints one JSON line per workload.  Inputs come from synth (numpy, seeded);
     the seven hybrid-block layers use seeds 40..46.
@@ -353,7 +353,7 @@ def main():
         summarize_counters(args.summarize_counters, args.out, args.command, args.trace_db)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: libjscan has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
