@@ -481,6 +481,44 @@ def main():
               "note": "the 128 MiB state can stay resident in the 256 MB last-level cache"}
     log(f"[bench] decode {us_step:.2f} us/step")
 
+    # one sequence per step (8192 channels, a launch-bound kernel): 64 eager
+    # calls against the same 64 steps captured once in a HIP graph and replayed
+    st1 = st[:1].clone()
+    t1 = [v[:1].contiguous() for v in (dx, dd, dz, dB, dC)]
+    y1 = torch.empty_like(t1[0])
+
+    def steps64():
+        for _ in range(64):
+            js.step_batch(st1, t1[0], t1[1], Ad, t1[3], t1[4], Dd, t1[2], y=y1)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps64()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps64()
+    for _ in range(3):
+        steps64()
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    steps64()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / 64
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / 64
+    decode["single_sequence"] = {"workload": "decode step of one sequence x d_inner 8192",
+                                 "eager_us_per_step": round(eager_us, 3), "hip_graph_us_per_step": round(graph_us, 3)}
+    del graph
+    log(f"[bench] decode of one sequence {eager_us:.2f} us/step eager, {graph_us:.2f} us/step from a HIP graph")
+
     # the same prefill with the fused input prologue (conv width 4 + SiLU, softplus(delta + dt_bias))
     pro = synth.prologue_params(d_inner, 4, seed=2)
     cw, cb, cs, dtb = (torch.from_numpy(pro[k]).to(dev) for k in ("conv_weight", "conv_bias", "conv_state",

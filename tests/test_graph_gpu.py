@@ -1,0 +1,127 @@
+"""HIP-graph capture of libjscan calls (torch.cuda.CUDAGraph): decode steps,
+fused decode steps and a chunked prefill with a caller workspace launch only
+kernels on the caller's stream, so they can be captured once and replayed.
+
+Each graph is replayed several times from the same starting state, with eager
+library work and synchronisations between the replays, and every replay must
+equal the eager calls bit for bit (the same kernels on the same inputs).
+Inputs follow the seeded recipes of ``synth``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import selective_state_space_11_amd as js
+from gpu_util import dev_f32, dev_io, to_device
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only machines, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+REPLAYS = 3
+
+
+def print_case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def capture(fn):
+    """fn() once on a side stream (warm-up), then captured into a graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def decode_tokens(n_seq, d, T, seed):
+    toks = [synth.decode_inputs(n_seq, d, seed=seed, step=k) for k in range(T)]
+    return [{k: dev_io(v[k]) for k in ("x", "delta", "z", "B", "C")} for v in toks]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_steps_replayed(fused):
+    """Eight decode steps of 4 sequences x 256 channels (plain, or with the
+    conv(4) + SiLU and softplus prologue and its conv history in place)."""
+    print_case(f"graph decode fused={fused}")
+    n_seq, d, T = 4, 256, 8
+    A, D, _ = synth.params(d, seed=90)
+    A, D = dev_f32(A), dev_f32(D)
+    toks = decode_tokens(n_seq, d, T, seed=90)
+    pro = synth.prologue_params(d, 4, seed=90, batch=n_seq)
+    st0 = dev_f32(synth.decode_state(n_seq, d, seed=90))
+    cs0 = dev_f32(pro["conv_state"])
+    kw = dict(conv_weight=dev_f32(pro["conv_weight"]), conv_bias=dev_f32(pro["conv_bias"]),
+              dt_bias=dev_f32(pro["dt_bias"]), softplus=True)
+
+    def steps(st, cs, ys):
+        for k, t in enumerate(toks):
+            if fused:
+                js.step_batch_fused(st, t["x"], t["delta"], A, t["B"], t["C"], D, t["z"], conv_state=cs, y=ys[k],
+                                    **kw)
+            else:
+                js.step_batch(st, t["x"], t["delta"], A, t["B"], t["C"], D, t["z"], y=ys[k])
+
+    st_ref, cs_ref = st0.clone(), cs0.clone()
+    ys_ref = [torch.empty_like(toks[0]["x"]) for _ in range(T)]
+    steps(st_ref, cs_ref, ys_ref)
+    torch.cuda.synchronize()
+
+    st, cs = st0.clone(), cs0.clone()
+    ys = [torch.empty_like(toks[0]["x"]) for _ in range(T)]
+    g = capture(lambda: steps(st, cs, ys))
+    other = st0.clone()
+    for rep in range(REPLAYS):
+        st.copy_(st0)
+        cs.copy_(cs0)
+        for y in ys:
+            y.zero_()
+        js.step_batch(other, toks[rep]["x"], toks[rep]["delta"], A, toks[rep]["B"], toks[rep]["C"], D,
+                      toks[rep]["z"])           # eager library work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(T):
+            assert torch.equal(ys[k], ys_ref[k]), (rep, k)
+        assert torch.equal(st, st_ref), rep
+        if fused:
+            assert torch.equal(cs, cs_ref), rep
+
+
+def test_chunked_prefill_replayed():
+    """A prefill of 2 x 1000 tokens x 256 channels in a forced 4-chunk plan with
+    a caller workspace (chunk-local pass, combine and rescan in the graph)."""
+    print_case("graph prefill chunks=4")
+    b, L, d = 2, 1000, 256
+    inp = synth.prefill_inputs(b, L, d, seed=91, io=synth.IO_BF16, h0=True)
+    t = to_device(inp)
+    try:
+        js.set_plan_override(1, 4)
+        assert js.plan(b, L, d)[1] == 4
+        ws = torch.empty(js.workspace_size(b, L, d), dtype=torch.uint8, device="cuda")
+        y_ref, h_ref = js.prefill(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        y, hT = torch.empty_like(y_ref), torch.empty_like(h_ref)
+        g = capture(lambda: js.prefill(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], y=y,
+                                       hT=hT, workspace=ws))
+        for rep in range(REPLAYS):
+            y.zero_()
+            hT.zero_()
+            ws.zero_()
+            js.prefill(t["x"][:1], t["delta"][:1], t["A"], t["B"][:1], t["C"][:1], t["D"], t["z"][:1])
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_ref), rep
+            assert torch.equal(hT, h_ref), rep
+    finally:
+        js.set_plan_override(0, 0)
