@@ -54,8 +54,11 @@ def alg_bytes_step(n_seq, d_inner, io_bytes=2):
 
 
 def source_digest():
-    p = os.path.join(ROOT, "selective_state_space_11_amd", "csrc", "jscan.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Digest of the sources the forward kernels are compiled from."""
+    h = hashlib.sha256()
+    for f in ("jscan.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "selective_state_space_11_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel_tag):
