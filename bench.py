@@ -237,6 +237,17 @@ def run_all_configs(log):
         oracle.prefill(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["h0"])
         return inp["x"].shape[0] * inp["x"].shape[1] * n_ch / (time.time() - t0)
 
+    def cpu_bwd_rate(inp, dy, dhT, n_ch):
+        d_inner = inp["x"].shape[2]
+        chans = np.linspace(0, d_inner - 1, n_ch).astype(int)
+        sub = synth.channel_slice(inp, chans)
+        dys = synth.widen(dy[:, :, chans])
+        dhs = dhT[:, chans].astype(np.float64)
+        t0 = time.time()
+        oracle.backward(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], dys, sub["h0"],
+                        dhs)
+        return inp["x"].shape[0] * inp["x"].shape[1] * n_ch / (time.time() - t0)
+
     def emit(name, chtok, ms, abytes, cpu, extra=None):
         rec = {"workload": name, "gpu_ms": round(ms, 4), "channel_tokens_per_s": chtok / (ms * 1e-3),
                "alg_GBps": round(abytes / (ms * 1e-3) / 1e9, 1),
@@ -260,12 +271,12 @@ def run_all_configs(log):
         if L <= 65536:
             dy_np, dhT_np = synth.output_grads(batch, L, 8192, seed=seed)
             dy, dhT = dio(dy_np), dio(dhT_np)
-            del dy_np
             bws = torch.empty(js.backward_workspace_size(batch, L, 8192), dtype=torch.uint8, device=dev)
             g = js.backward(x, dl, A, B, C, D, z, dy, None, dhT, workspace=bws)
             bms = timed(lambda: js.backward(x, dl, A, B, C, D, z, dy, None, dhT, workspace=bws, out=g), 5)
-            emit("backward of " + name, batch * L * 8192, bms, alg_bytes_prefill(batch, L, 8192) * 2, None,
-                 {"over_forward": round(bms / ms, 3)})
+            emit("backward of " + name, batch * L * 8192, bms, alg_bytes_prefill(batch, L, 8192) * 2,
+                 cpu_bwd_rate(inp, dy_np, dhT_np, 64), {"over_forward": round(bms / ms, 3)})
+            del dy_np
             del g, bws, dy
         if L == 262144:
             state = torch.zeros(1, 8192, 16, device=dev)
@@ -285,9 +296,24 @@ def run_all_configs(log):
 
     # decode: 256 sequences, 1024 steps with per-step seeded inputs
     n_seq = 256
-    st = dio(synth.decode_state(n_seq, 8192, seed=3))
-    A, D, _ = synth.params(8192, seed=3)
-    A, D = dio(A), dio(D)
+    st_np = synth.decode_state(n_seq, 8192, seed=3)
+    st = dio(st_np)
+    A_np, D_np, _ = synth.params(8192, seed=3)
+    A, D = dio(A_np), dio(D_np)
+    # the oracle's decode rate on 256 of the channels over the first 16 steps
+    chans = np.linspace(0, 8191, 256).astype(int)
+    toks = []
+    for k in range(16):
+        di = synth.decode_inputs(n_seq, 8192, seed=3, step=k)
+        toks.append([synth.widen(di[n][..., chans]) if n in ("x", "delta", "z") else synth.widen(di[n])
+                     for n in ("x", "delta", "z", "B", "C")])
+    s64 = st_np[:, chans].astype(np.float64)
+    A64, D64 = A_np[chans].astype(np.float64), D_np[chans].astype(np.float64)
+    t0 = time.time()
+    for (ox, od, oz, oB, oC) in toks:
+        _, s64 = oracle.step(s64, ox, od, A64, oB, oC, D64, oz)
+    cpu_dec = n_seq * len(chans) * len(toks) / (time.time() - t0)
+    del toks, st_np
     steps = []
     for k in range(1024):
         di = synth.decode_inputs(n_seq, 8192, seed=3, step=k)
@@ -298,7 +324,7 @@ def run_all_configs(log):
         for (dx, dd, dz, dB, dC) in steps:
             js.step_batch(st, dx, dd, A, dB, dC, D, dz, y=yd)
     ms = timed(decode_run, 2)
-    emit("decode 256 sequences x 1024 steps", n_seq * 8192 * 1024, ms, 1024 * alg_bytes_step(n_seq, 8192), None,
+    emit("decode 256 sequences x 1024 steps", n_seq * 8192 * 1024, ms, 1024 * alg_bytes_step(n_seq, 8192), cpu_dec,
          {"us_per_step": round(ms * 1e3 / 1024, 2)})
     del steps
 
