@@ -148,6 +148,40 @@ def test_guard_canaries_and_determinism():
     assert torch.equal(y, y2) and torch.equal(hT, h2)
 
 
+@pytest.mark.parametrize("chunks", [1, 5])
+@pytest.mark.parametrize("case", ["A_zero", "A_positive", "z_zero", "x_zero", "C_zero"])
+def test_degenerate_parameters(case, chunks):
+    """Degenerate cases of the recurrence, two sequences of 500 tokens x 136
+    channels in bf16 with h0, against the oracle: A = 0 (no decay, the state
+    only accumulates), A > 0 (growth; A may be any finite value), z = 0 (the
+    gate is closed: y is exactly 0), x = 0 (the state only decays) and C = 0
+    (only the D skip reaches y)."""
+    print_case(f"degenerate {case} chunks={chunks}")
+    inp = synth.prefill_inputs(2, 500, 136, seed=95, io=synth.IO_BF16, h0=True)
+    zero_io = synth.to_bf16_bits(np.zeros(1))[0]
+    if case == "A_zero":
+        inp["A"] = np.zeros_like(inp["A"])
+    elif case == "A_positive":
+        inp["A"] = np.random.default_rng(95).uniform(0.0, 0.02, inp["A"].shape).astype(np.float32)
+    elif case == "z_zero":
+        inp["z"] = np.full_like(inp["z"], zero_io)
+    elif case == "x_zero":
+        inp["x"] = np.full_like(inp["x"], zero_io)
+    else:
+        inp["C"] = np.full_like(inp["C"], zero_io)
+    yr, hr = oracle_full(inp)
+    t = to_device(inp)
+    try:
+        js.set_plan_override(1, chunks)
+        y, hT = run_prefill(t)
+    finally:
+        js.set_plan_override(0, 0)
+    if case == "z_zero":
+        assert torch.count_nonzero(y) == 0
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+
+
 def test_nan_stays_in_its_channel():
     print_case("nan locality")
     inp = synth.prefill_inputs(2, 300, 256, seed=11, io=synth.IO_BF16, h0=True)
