@@ -107,6 +107,17 @@ def test_backward_short_and_empty():
     assert np.array_equal(host64(g["dh0"]), dhT.astype(np.float64))
 
 
+@pytest.mark.parametrize("chunks", [1, 5])
+def test_backward_of_zero_output_gradients(chunks):
+    """dy = 0 and no dhT: every gradient is exactly zero."""
+    print_case(f"bwd zero output gradients chunks={chunks}")
+    inp, dy, _ = problem(2, 300, 136, seed=33, io=synth.IO_BF16)
+    zero = np.full_like(dy, synth.to_bf16_bits(np.zeros(1))[0])
+    g = with_plan(chunks, lambda: gpu_grads(to_device(inp), zero, None, use_dhT=False))
+    for k, v in g.items():
+        assert torch.count_nonzero(v) == 0, k
+
+
 def test_backward_deterministic_and_workspace():
     """Two runs give identical bits; a caller-provided workspace gives the same."""
     print_case("bwd determinism")
