@@ -287,8 +287,13 @@ jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d
  * only; JSCAN_ERR_NULL if NULL for a chunked plan).  workspace: NULL or at
  * least jscan_backward_workspace_size() - jscan_prefill_workspace_size()
  * bytes.  Otherwise as jscan_backward; nothing may overlap prefill_workspace.
- * Breaking the contract above gives wrong gradients, not an error: the
- * library cannot check what a workspace holds.
+ *
+ * A chunked prefill writes a tag at the start of its workspace (sizes, plan,
+ * and which recurrence and prologue).  The backward compares it on the GPU:
+ * a workspace from a prefill of other sizes, under another plan, or from the
+ * fused or trapezoidal prefill makes every gradient NaN.  One that a plain
+ * prefill of the same sizes and plan wrote over other inputs cannot be told
+ * apart and gives wrong gradients.
  */
 jscan_status jscan_backward_saved(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
                                   const void* x, const void* delta, const float* A, const void* B, const void* C,

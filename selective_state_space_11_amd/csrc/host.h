@@ -49,13 +49,30 @@ Plan make_plan(int64_t batch, int64_t L, int64_t d_inner, int K, int64_t C_targe
 double wave_efficiency(double waves);
 
 size_t round_up(size_t v);
-// Workspace of a chunked prefill plan: chunk-local end states, delta sums,
-// chunk starting states (all state-major) and a conv-history copy.
-struct WsLayout { size_t S, dsum, hstart, hist, total; };
+// Workspace of a chunked prefill plan, in this order: a tag (first, so that
+// its place does not depend on the plan), chunk-local end states, delta sums,
+// chunk starting states (all state-major) and a conv-history copy.  The
+// fields are region sizes; the off_* functions give byte offsets.
+struct WsLayout {
+  size_t tag, S, dsum, hstart, hist, total;
+  size_t off_S() const { return tag; }
+  size_t off_dsum() const { return tag + S; }
+  size_t off_hstart() const { return tag + S + dsum; }
+  size_t off_hist() const { return tag + S + dsum + hstart; }
+};
 WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p);
 
+// The tag a chunked prefill writes at the start of its workspace: what produced
+// the chunk starting states there.  The backward that reuses them compares it
+// with its own sizes and plan on the GPU.  variant: 0 for the plain
+// recurrence, else 1 (conv) | 2 (softplus) | 4 (trapezoidal) | 8 (RMSNorm).
+constexpr int kTagWords = 8;
+constexpr int64_t kTagMagic = 0x6a7363616e746167LL;
+struct Tag { int64_t w[kTagWords]; };
+Tag make_tag(int64_t batch, int64_t L, int64_t d_inner, const Plan& p, int variant);
+
 // Launches the chunk-local pass and the combine of plan p (chunks > 1):
-// afterwards ws holds, at ws_layout's hstart offset, hstart[b][c][n][d] = the
+// afterwards ws holds, at ws_layout's off_hstart(), hstart[b][c][n][d] = the
 // state before chunk c's first token (c = 0: h0 or zero).
 jscan_status forward_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
                                   const void* delta, const float* A, const void* B, const float* h0, char* ws,

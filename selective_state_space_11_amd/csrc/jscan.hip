@@ -186,10 +186,13 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, co
                                                  const float* __restrict__ dsum, const float* __restrict__ h0,
                                                  float* __restrict__ hstart, int64_t d_inner, int n_chunks,
                                                  int seg_per_chunk, const float* __restrict__ hist,
-                                                 float* __restrict__ hist_copy, int hist_rows) {
+                                                 float* __restrict__ hist_copy, int hist_rows,
+                                                 int64_t* __restrict__ tag_out, Tag tag) {
   constexpr int G = 16;                // segments whose loads are in flight together
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t b = blockIdx.y;
+  if (tag_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kTagWords)
+    tag_out[threadIdx.x] = tag.w[threadIdx.x];
   const int64_t per_seq = d_inner * NSTATE;
   if (i >= per_seq) return;
   const int64_t n = i / d_inner;
@@ -752,9 +755,14 @@ WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
     w.dsum = round_up((size_t)batch * segs * (size_t)d_inner * sizeof(float));
     w.hstart = round_up((size_t)batch * (size_t)p.chunks * (size_t)d_inner * NSTATE * sizeof(float));
     w.hist = round_up((size_t)batch * 3 * (size_t)d_inner * sizeof(float));   // conv history copy
+    w.tag = round_up(kTagWords * sizeof(int64_t));
   }
-  w.total = w.S + w.dsum + w.hstart + w.hist;
+  w.total = w.tag + w.S + w.dsum + w.hstart + w.hist;
   return w;
+}
+
+Tag make_tag(int64_t batch, int64_t L, int64_t d_inner, const Plan& p, int variant) {
+  return Tag{{kTagMagic, batch, L, d_inner, p.chunks, p.chunk_len, p.seg_per_chunk, variant}};
 }
 
 bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner) {
@@ -795,12 +803,14 @@ template <class T, bool CONV, bool SP, bool TR>
 jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* x, const void* delta,
                          const float* A, const void* B, const void* C, const float* D, const void* z,
                          const float* h0, void* y, float* hT, char* ws, const Plan& p, const ProArgs& pa,
-                         hipStream_t st) {
+                         bool rms, hipStream_t st) {
   const WsLayout w = ws_layout(batch, L, d_inner, p);
-  float* S = reinterpret_cast<float*>(ws);
-  float* dsum = reinterpret_cast<float*>(ws + w.S);
-  float* hstart = reinterpret_cast<float*>(ws + w.S + w.dsum);
-  float* hist_copy = reinterpret_cast<float*>(ws + w.S + w.dsum + w.hstart);
+  float* S = reinterpret_cast<float*>(ws + w.off_S());
+  float* dsum = reinterpret_cast<float*>(ws + w.off_dsum());
+  float* hstart = reinterpret_cast<float*>(ws + w.off_hstart());
+  float* hist_copy = reinterpret_cast<float*>(ws + w.off_hist());
+  int64_t* tag_out = reinterpret_cast<int64_t*>(ws);
+  const int variant = (CONV ? 1 : 0) | (SP ? 2 : 0) | (TR ? 4 : 0) | (rms ? 8 : 0);
   hipError_t e;
 
   ProArgs scan_pa = pa;
@@ -814,7 +824,8 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
     const int hist_rows = CONV ? pa.width - 1 : 0;
     dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
     hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks,
-                       p.seg_per_chunk, pa.hist, hist_rows > 0 ? hist_copy : nullptr, hist_rows);
+                       p.seg_per_chunk, pa.hist, hist_rows > 0 ? hist_copy : nullptr, hist_rows, tag_out,
+                       make_tag(batch, L, d_inner, p, variant));
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
     if (hist_rows > 0) scan_pa.hist = hist_copy;
   }
@@ -835,9 +846,9 @@ jscan_status forward_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t
                                   const Plan& p, hipStream_t st) {
   if (p.chunks <= 1) return JSCAN_OK;
   const WsLayout w = ws_layout(batch, L, d_inner, p);
-  float* S = reinterpret_cast<float*>(ws);
-  float* dsum = reinterpret_cast<float*>(ws + w.S);
-  float* hstart = reinterpret_cast<float*>(ws + w.S + w.dsum);
+  float* S = reinterpret_cast<float*>(ws + w.off_S());
+  float* dsum = reinterpret_cast<float*>(ws + w.off_dsum());
+  float* hstart = reinterpret_cast<float*>(ws + w.off_hstart());
   const ProArgs none{nullptr, nullptr, nullptr, nullptr, nullptr, 1};
   const int segs = (int)p.segments();
   dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)segs, (unsigned)batch);
@@ -853,7 +864,7 @@ jscan_status forward_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
   dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
   hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks, p.seg_per_chunk,
-                     nullptr, nullptr, 0);
+                     nullptr, nullptr, 0, nullptr, Tag{});
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
   return JSCAN_OK;
 }
@@ -1105,9 +1116,9 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
     constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value;
     return io == JSCAN_IO_BF16
                ? run_prefill<uint16_t, CV, SPV, TRV>(batch, L, d_inner, x, dl, A, Bs, Cs, D, z, h0, y, hT, ws,
-                                                     plan, pa, st)
+                                                     plan, pa, has_rms(pro), st)
                : run_prefill<float, CV, SPV, TRV>(batch, L, d_inner, x, dl, A, Bs, Cs, D, z, h0, y, hT, ws,
-                                                  plan, pa, st);
+                                                  plan, pa, has_rms(pro), st);
   });
   if (owned) {
     e = hipFreeAsync(ws, st);

@@ -253,7 +253,20 @@ struct BwdArgs {
   float* ck;               // [b][chunk][block][16][d] states before each kTok-token block
   int64_t L, d_inner, chunk_len;
   int n_chunks;
+  const int64_t* tag;      // the tag of the prefill whose chunk states hinit are (saved states), or null
+  Tag expect;              // the tag a plain prefill of these sizes and plan writes
 };
+
+// False when saved chunk states come from a prefill of other sizes, another
+// plan or another variant of the recurrence.  The sweeps then start from NaN,
+// so every gradient is NaN rather than silently wrong.
+__device__ __forceinline__ bool saved_states_ok(const BwdArgs& a) {
+  if (!a.tag) return true;
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < kTagWords; ++k) ok = ok && a.tag[k] == a.expect.w[k];
+  return ok;
+}
 
 // Per-wave coordinates shared by the two sweeps.
 struct WaveTile {
@@ -329,6 +342,11 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) h[n] = hi ? hi[n] : 0.0f;
   }
+  const bool ok = saved_states_ok(a);
+  if (!ok) {
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) h[n] = __builtin_nanf("");
+  }
   const float Dd = a.D[w.d];
   const T* const rows[4] = {static_cast<const T*>(a.delta) + w.row0, static_cast<const T*>(a.x) + w.row0,
                             static_cast<const T*>(a.z) + w.row0, static_cast<const T*>(a.dy) + w.row0};
@@ -344,7 +362,7 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
   const uint32_t lb4 = (uint32_t)w.lo * 4, qoff = (uint32_t)(w.lane >> 2) * 4;
   const uint32_t nrow4 = (uint32_t)(a.d_inner * 4);
 
-  float dD = 0.0f;
+  float dD = ok ? 0.0f : __builtin_nanf("");
   Row<T, NSTATE> Bc, Bn, Cv;
   auto block = [&](int bb, const T (&v)[4][kTok]) {
     const auto rz = rsrc(dzrow + (int64_t)bb * a.d_inner);
@@ -431,6 +449,10 @@ __global__ __launch_bounds__(64, 3) void k_bwd_rev(BwdArgs a, const T* __restric
     const float* mi = a.Min + ((w.b * a.n_chunks + w.c + 1) * NSTATE) * a.d_inner + w.d;
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) mu[n] = mi[(int64_t)n * a.d_inner];
+  }
+  if (!saved_states_ok(a)) {
+#pragma unroll
+    for (int n = 0; n < NSTATE; ++n) mu[n] = __builtin_nanf("");
   }
   // LDS indexed (state or quad of states, lane), so that a wave's accesses
   // are consecutive.  dA is carried here (a register accumulator live across
@@ -647,12 +669,13 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
                           const float* A, const void* B, const void* C, const float* D, const void* z,
                           const float* h0, const void* dy, const float* dhT, void* dx, void* ddelta, void* dz,
                           float* dA, float* dB, float* dC, float* dD, float* dh0, char* ws,
-                          const float* saved_hstart, const Plan& p, hipStream_t st) {
+                          const float* saved_hstart, const int64_t* saved_tag, const Plan& p,
+                          hipStream_t st) {
   const BwdLayout w = bwd_layout(batch, L, d_inner, p);
   const WsLayout fw = ws_layout(batch, L, d_inner, p);
   // Chunk starting states: those a prefill left in its workspace, or
   // recomputed into the front of this workspace.
-  const float* hstart = saved_hstart ? saved_hstart : reinterpret_cast<const float*>(ws + fw.S + fw.dsum);
+  const float* hstart = saved_hstart ? saved_hstart : reinterpret_cast<const float*>(ws + fw.off_hstart());
   char* q = saved_hstart ? ws : ws + w.fwd;
   float* M = reinterpret_cast<float*>(q); q += w.M;
   float* dsum = reinterpret_cast<float*>(q); q += w.dsum;
@@ -679,7 +702,8 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "adjoint combine launch");
   }
   const BwdArgs args{x, delta, A, B, C, D, z, dy, p.chunks > 1 ? hstart : h0, M, dhT, dx, ddelta, dz, dBp, dCp,
-                     dAp, dDp, dh0, ck, L, d_inner, p.chunk_len, p.chunks};
+                     dAp, dDp, dh0, ck, L, d_inner, p.chunk_len, p.chunks,
+                     saved_hstart ? saved_tag : nullptr, make_tag(batch, L, d_inner, p, 0)};
   dim3 g3((unsigned)G, (unsigned)p.chunks, (unsigned)batch);
   hipLaunchKernelGGL((k_bwd_fwd<T>), g3, dim3(64), 0, st, args, static_cast<const T*>(B), static_cast<const T*>(C));
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "backward forward-sweep launch");
@@ -769,13 +793,14 @@ jscan_status backward_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
       return hip_fail(e, "hipMallocAsync(workspace)");
     owned = true;
   }
-  const float* saved_hstart =
-      use_saved ? reinterpret_cast<const float*>(static_cast<const char*>(prefill_ws) + fl.S + fl.dsum) : nullptr;
+  const char* pw = static_cast<const char*>(prefill_ws);
+  const float* saved_hstart = use_saved ? reinterpret_cast<const float*>(pw + fl.off_hstart()) : nullptr;
+  const int64_t* saved_tag = use_saved ? reinterpret_cast<const int64_t*>(pw) : nullptr;
   s = io == JSCAN_IO_BF16
           ? run_backward<uint16_t>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz,
-                                   dA, dB, dC, dD, dh0, ws, saved_hstart, plan, st)
+                                   dA, dB, dC, dD, dh0, ws, saved_hstart, saved_tag, plan, st)
           : run_backward<float>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz, dA,
-                                dB, dC, dD, dh0, ws, saved_hstart, plan, st);
+                                dB, dC, dD, dh0, ws, saved_hstart, saved_tag, plan, st);
   if (owned) {
     e = hipFreeAsync(ws, st);
     if (s == JSCAN_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");

@@ -200,6 +200,39 @@ def test_backward_saved_states_jamba_shape():
     saved_vs_plain(inp, dy, dhT)
 
 
+@pytest.mark.parametrize("case", ["sizes", "plan", "variant"])
+def test_backward_saved_states_from_elsewhere_are_nan(case):
+    """A prefill workspace that does not belong to the call is caught on the
+    GPU through the tag the prefill writes: one from a prefill over other
+    sizes (777 tokens for a 700-token backward), under another plan (5 chunks
+    against the automatic plan) or from the fused prefill (softplus) makes
+    every gradient NaN instead of silently wrong."""
+    print_case(f"bwd saved states from elsewhere: {case}")
+    b, L, d = 2, 777, 200
+    inp, dy, dhT = problem(b, L, d, seed=39, io=synth.IO_BF16)
+    t = to_device(inp)
+    Lb = 700 if case == "sizes" else L
+    assert js.plan(b, L, d)[1] > 1 and js.plan(b, Lb, d)[1] > 1
+    if case == "plan":
+        assert js.plan(b, L, d)[1] != 5
+    nbytes = max(js.workspace_size(b, L, d), js.workspace_size(b, Lb, d),
+                 with_plan(5, lambda: js.workspace_size(b, L, d)))
+    pws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args = (t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"])
+    if case == "variant":
+        js.prefill_fused(*args, dt_bias=dev_f32(synth.prologue_params(d, 4, seed=39)["dt_bias"]), softplus=True,
+                         workspace=pws)
+    elif case == "plan":
+        with_plan(5, lambda: js.prefill(*args, workspace=pws))
+    else:
+        js.prefill(*args, workspace=pws)
+    torch.cuda.synchronize()
+    sl = {k: (v[:, :Lb].contiguous() if k in ("x", "delta", "z", "B", "C") else v) for k, v in t.items()}
+    g = gpu_grads(sl, dy[:, :Lb], dhT, prefill_workspace=pws)
+    for k, v in g.items():
+        assert torch.isnan(v.float()).all(), k
+
+
 def test_backward_jamba_prefill_every_output():
     """Batch 2, L 4096, d_inner 8192 (the Jamba prefill shape), bf16: every
     gradient of every channel and token against the oracle."""
