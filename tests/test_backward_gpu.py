@@ -243,6 +243,16 @@ def test_backward_jamba_prefill_every_output():
     check_all(g, ref, bf16=True)
 
 
+def test_backward_f32_io_full_width():
+    """fp32 I/O at the full width: batch 1, L 1000, d_inner 8192, h0 and dhT,
+    the automatic (chunked) plan; every gradient."""
+    print_case("bwd f32 1x1000x8192")
+    inp, dy, dhT = problem(1, 1000, 8192, seed=97, io=synth.IO_F32)
+    assert js.plan(1, 1000, 8192)[1] > 1
+    g = gpu_grads(to_device(inp), dy, dhT)
+    check_all(g, oracle_grads(inp, dy, dhT), bf16=False)
+
+
 def test_backward_64k_sampled():
     """The 64K-token prefill (batch 1, d_inner 8192, bf16) in the automatic
     plan.  Per-channel gradients (dx, ddelta, dz, dA, dD, dh0) on 24 sampled

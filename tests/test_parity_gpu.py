@@ -378,6 +378,18 @@ def test_jamba_prefill_batch2_every_output():
     assert_state(hT, hr, "hT")
 
 
+def test_f32_io_full_width_every_output():
+    """fp32 I/O at the full width: batch 2, L 1000, d_inner 8192, h0, the
+    automatic (chunked) plan; every output."""
+    print_case("f32 I/O 2x1000x8192 (full compare)")
+    inp = synth.prefill_inputs(2, 1000, 8192, seed=96, io=synth.IO_F32, h0=True)
+    assert js.plan(2, 1000, 8192)[1] > 1
+    y, hT = run_prefill(to_device(inp))
+    yr, hr = oracle_full(inp)
+    assert_y(y, yr, bf16=False)
+    assert_state(hT, hr, "hT")
+
+
 def test_64k_context_sampled():
     """The 64K-token prefill (batch 1, d_inner 8192) in the benchmark's plan:
     sampled channels over the whole sequence against the oracle."""
