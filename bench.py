@@ -99,10 +99,12 @@ def summarize_trace(db, out_md, command):
         stats.setdefault(_short(name), []).append(dur / 1000.0)
     lines = [f"# Kernel trace: {os.path.basename(os.path.dirname(out_md)) and os.path.basename(out_md)[:-3]}", "",
              "Command (on the MI355X box, from the repository root):", "", "```", command, "```", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | total (us) |",
-             "|---|---|---|---|---|---|"]
+             "| kernel | calls | average (us) | median (us) | min (us) | max (us) | total (us) |",
+             "|---|---|---|---|---|---|---|"]
     for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | {sum(v):.1f} |")
+        med = sorted(v)[len(v) // 2]
+        lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {med:.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{sum(v):.1f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
     return stats
 
