@@ -304,3 +304,25 @@ def test_autograd_function_matches_oracle():
             assert_y(t[k].grad, ref[gname], bf16=False, what=gname)
         else:
             assert_state(t[k].grad, ref[gname], gname)
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(batch=int(rng.integers(1, 3)), L=int(rng.integers(1, 800)),
+                 d=int(rng.choice([1, 7, 64, 65, 136, 200])),
+                 io=synth.IO_BF16 if rng.random() < 0.7 else synth.IO_F32, h0=bool(rng.random() < 0.6),
+                 dhT=bool(rng.random() < 0.6), chunks=int(rng.choice([0, 1, 2, 3, 5, 9])), seed=2000 + i)
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_cases(16, 2025), ids=lambda c: "b{batch}L{L}d{d}io{io}c{chunks}".format(**c))
+def test_backward_random_shapes_and_plans(case):
+    """Seeded random sizes, I/O dtype, h0 and dhT given or not, chunk count
+    (0: the automatic plan); every gradient against the oracle."""
+    c = case
+    print_case(f"bwd random {c}")
+    inp, dy, dhT = problem(c["batch"], c["L"], c["d"], seed=c["seed"], io=c["io"], h0=c["h0"])
+    ref = oracle_grads(inp, dy, dhT, use_h0=c["h0"], use_dhT=c["dhT"])
+    run = lambda: gpu_grads(to_device(inp), dy, dhT, use_h0=c["h0"], use_dhT=c["dhT"])
+    g = with_plan(c["chunks"], run) if c["chunks"] else run()
+    check_all(g, ref, bf16=c["io"] == synth.IO_BF16)

@@ -451,3 +451,35 @@ def test_bookkeeping_bit_exact_at_256k(case):
     t = bookkeeping_inputs(1, 262144, 8192, case)
     y, hT = run_prefill(t)
     check_bookkeeping(case, t, y, hT)
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        cases.append(dict(batch=int(rng.integers(1, 4)), L=int(rng.integers(1, 1500)),
+                          d=int(rng.choice([1, 7, 64, 65, 128, 200, 257, 512])),
+                          io=synth.IO_BF16 if rng.random() < 0.7 else synth.IO_F32, h0=bool(rng.random() < 0.6),
+                          K=int(rng.choice([1, 1, 1, 2, 4, 8])), chunks=int(rng.choice([0, 1, 2, 3, 5, 8, 16, 33])),
+                          seed=1000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(40, 2024), ids=lambda c: "b{batch}L{L}d{d}io{io}K{K}c{chunks}".format(**c))
+def test_random_shapes_and_plans(case):
+    """Seeded random sizes (batch 1-3, L 1-1499, d_inner from 1 to 512), I/O
+    dtype, h0 or not, waves per group and chunk count (0: the automatic plan),
+    every output against the oracle."""
+    c = case
+    print_case(f"random {c}")
+    inp = synth.prefill_inputs(c["batch"], c["L"], c["d"], seed=c["seed"], io=c["io"], h0=c["h0"])
+    t = to_device(inp)
+    yr, hr = oracle_full(inp, use_h0=c["h0"])
+    try:
+        if c["chunks"]:
+            js.set_plan_override(c["K"], c["chunks"])
+        y, hT = run_prefill(t, h0=c["h0"])
+    finally:
+        js.set_plan_override(0, 0)
+    assert_y(y, yr, bf16=c["io"] == synth.IO_BF16)
+    assert_state(hT, hr, "hT")

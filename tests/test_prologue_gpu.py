@@ -390,3 +390,31 @@ def test_prefill_rmsnorm_jamba_shape():
     y, hT, _ = gpu_rms(to_device(inp), pro, ws, width=0)
     assert_y(y, yr, bf16=True)
     assert_state(hT, hr, "hT")
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(batch=int(rng.integers(1, 4)), L=int(rng.integers(1, 1200)),
+                 d=int(rng.choice([1, 8, 64, 65, 136, 200, 264])), width=int(rng.integers(0, 5)),
+                 softplus=bool(rng.random() < 0.7), history=bool(rng.random() < 0.7), h0=bool(rng.random() < 0.6),
+                 io=synth.IO_BF16 if rng.random() < 0.7 else synth.IO_F32,
+                 chunks=int(rng.choice([0, 1, 2, 5, 9])), seed=3000 + i) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 2026),
+                         ids=lambda c: "b{batch}L{L}d{d}w{width}sp{softplus:d}io{io}c{chunks}".format(**c))
+def test_prefill_fused_random(case):
+    """Seeded random sizes, conv width 0-4 with or without history, softplus
+    or not, h0 or not, I/O dtype and chunk count (0: automatic plan); y and hT
+    against the oracle, the written conv history bit for bit."""
+    c = case
+    print_case(f"fused random {c}")
+    inp, pro = problem(c["batch"], c["L"], c["d"], c["width"], seed=c["seed"], io=c["io"], h0=c["h0"],
+                       raw_dt=c["softplus"])
+    yr, hr, sr = oracle_fused(inp, pro, c["width"], c["softplus"], conv_state=c["history"], use_h0=c["h0"])
+    run = lambda: gpu_fused(to_device(inp), pro, c["width"], c["softplus"], conv_state=c["history"], use_h0=c["h0"])
+    y, hT, so = with_plan(1, c["chunks"], run) if c["chunks"] else run()
+    assert_y(y, yr, bf16=c["io"] == synth.IO_BF16)
+    assert_state(hT, hr, "hT")
+    if c["width"] > 1:
+        assert np.array_equal(host64(so), sr)

@@ -154,3 +154,28 @@ def test_trap_64k_sampled():
                                        B_prev=synth.widen(Bp))
     assert_y(y[:, :, ch], yr, bf16=True)
     assert_state(hT[:, ch], hr, "hT")
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(batch=int(rng.integers(1, 4)), L=int(rng.integers(1, 1200)),
+                 d=int(rng.choice([1, 8, 64, 65, 136, 200])), lam=bool(rng.random() < 0.7),
+                 prev=bool(rng.random() < 0.6), softplus=bool(rng.random() < 0.5),
+                 io=synth.IO_BF16 if rng.random() < 0.7 else synth.IO_F32,
+                 chunks=int(rng.choice([0, 1, 2, 5, 9])), seed=4000 + i) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_cases(20, 2027),
+                         ids=lambda c: "b{batch}L{L}d{d}lam{lam:d}prev{prev:d}sp{softplus:d}io{io}c{chunks}".format(**c))
+def test_trap_random(case):
+    """Seeded random sizes, lam and the token before the first given or not,
+    softplus or not, I/O dtype and chunk count (0: automatic plan); y and hT
+    against the oracle."""
+    c = case
+    print_case(f"trap random {c}")
+    inp, lam, xp, Bp, dtb = problem(c["batch"], c["L"], c["d"], seed=c["seed"], io=c["io"], softplus=c["softplus"])
+    yr, hr = oracle_trap(inp, lam, xp, Bp, dtb, c["lam"], c["prev"])
+    run = lambda: gpu_trap(to_device(inp), lam, xp, Bp, dtb, c["lam"], c["prev"])
+    y, hT = with_plan(c["chunks"], run) if c["chunks"] else run()
+    assert_y(y, yr, bf16=c["io"] == synth.IO_BF16)
+    assert_state(hT, hr, "hT")
