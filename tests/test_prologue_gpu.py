@@ -418,3 +418,46 @@ def test_prefill_fused_random(case):
     assert_state(hT, hr, "hT")
     if c["width"] > 1:
         assert np.array_equal(host64(so), sr)
+
+
+def _random_decode_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(n_seq=int(rng.integers(1, 300)), d=int(rng.choice([8, 64, 65, 136, 200, 1000])),
+                 width=int(rng.integers(0, 5)), softplus=bool(rng.random() < 0.6),
+                 io=synth.IO_BF16 if rng.random() < 0.7 else synth.IO_F32, seed=5000 + i) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_decode_cases(12, 2028),
+                         ids=lambda c: "n{n_seq}d{d}w{width}sp{softplus:d}io{io}".format(**c))
+def test_step_random(case):
+    """Seeded random sequence counts and widths, conv width 0-4, softplus or
+    not, I/O dtype: three chained decode steps (state and conv history in
+    place) against the oracle's prologue and step."""
+    c = case
+    print_case(f"decode random {c}")
+    n_seq, d, width, sp, io = c["n_seq"], c["d"], c["width"], c["softplus"], c["io"]
+    pro = synth.prologue_params(d, max(width, 1), seed=c["seed"], batch=n_seq)
+    A, D, _ = synth.params(d, seed=c["seed"])
+    st64 = synth.decode_state(n_seq, d, seed=c["seed"]).astype(np.float64)
+    cs64 = pro["conv_state"].astype(np.float64) if width > 0 else None
+    state = dev_f32(synth.decode_state(n_seq, d, seed=c["seed"]))
+    cs = dev_f32(pro["conv_state"]) if width > 0 else None
+    tA, tD = dev_f32(A), dev_f32(D)
+    for k in range(3):
+        s = synth.decode_inputs(n_seq, d, seed=c["seed"], step=k, io=io)
+        if sp:
+            s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=c["seed"] + 7 * k + 1, io=io)[:, 0, :]
+        xc, dt, cs64 = oracle.prologue(synth.widen(s["x"])[:, None, :], synth.widen(s["delta"])[:, None, :],
+                                       pro["conv_weight"] if width else None, pro["conv_bias"] if width else None,
+                                       cs64, pro["dt_bias"] if sp else None, sp)
+        yr, st64 = oracle.step(st64, xc[:, 0, :], dt[:, 0, :], A.astype(np.float64), synth.widen(s["B"]),
+                               synth.widen(s["C"]), D.astype(np.float64), synth.widen(s["z"]))
+        y = js.step_batch_fused(state, dev_io(s["x"]), dev_io(s["delta"]), tA, dev_io(s["B"]), dev_io(s["C"]), tD,
+                                dev_io(s["z"]), conv_weight=dev_f32(pro["conv_weight"]) if width else None,
+                                conv_bias=dev_f32(pro["conv_bias"]) if width else None, conv_state=cs,
+                                dt_bias=dev_f32(pro["dt_bias"]) if sp else None, softplus=sp)
+        torch.cuda.synchronize()
+        assert_y(y, yr, bf16=io == synth.IO_BF16, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+        if width > 1:
+            assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
