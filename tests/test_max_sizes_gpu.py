@@ -1,5 +1,6 @@
 """GPU parity at the largest sizes the library accepts: d_inner = 2^24 (the
-limit of its 32-bit per-row offsets) and batch = 65535 (the grid's limit).
+limit of its 32-bit per-row offsets) and batch = 65535 (the grid's limit),
+and at a context of 2^20 tokens (2^33 elements per tensor).
 
 Inputs follow the scan's seeded recipe (``synth.prefill_inputs``).  At
 d_inner = 2^24 the oracle runs on sampled channels (channels are independent
@@ -99,3 +100,37 @@ def test_prefill_and_decode_most_sequences():
     torch.cuda.synchronize()
     assert_y(ys, yr[:, L], bf16=True, what="decode y")
     assert_state(hT, hr, "state after decode")
+
+
+def test_prefill_million_tokens_bit_exact():
+    """1 x 2^20 tokens x 8192 channels (2^33 elements per tensor, byte offsets
+    past 2^34) in the automatic plan, with inputs whose fp32 arithmetic is
+    exact, built on the GPU: delta = 1 and A = -200 ln 2, so every decay
+    underflows to 0; B_t = C_t = one-hot at n*(t); x = small integer tags;
+    D = 0; z = 32 (SiLU(32) rounds to 32).  Then y = 32 x everywhere and hT
+    holds the last token's x at n*(L - 1), bit for bit."""
+    from gpu_util import n_star
+    L, d = 1 << 20, 8192
+    print_case(f"prefill bit-exact L={L} d_inner={d}")
+    bf = torch.bfloat16
+    dev = "cuda"
+    x = torch.empty(1, L, d, dtype=bf, device=dev)
+    dv = torch.arange(d, device=dev).view(1, d)
+    for t0 in range(0, L, 4096):
+        tv = torch.arange(t0, t0 + 4096, device=dev).view(-1, 1)
+        x[0, t0:t0 + 4096] = (((tv * 7 + dv * 3) % 61) + 1).to(bf)
+    delta = torch.ones(1, L, d, dtype=bf, device=dev)
+    z = torch.full((1, L, d), 32.0, dtype=bf, device=dev)
+    onehot = torch.nn.functional.one_hot(n_star(torch.arange(L, device=dev)), 16).to(bf)[None].contiguous()
+    A = torch.full((d, 16), float(np.float32(-200.0 * np.log(2.0))), device=dev)
+    D = torch.zeros(d, device=dev)
+    h0 = torch.randn(1, d, 16, device=dev)
+    assert js.plan(1, L, d)[1] > 1
+    y, hT = js.prefill(x, delta, A, onehot, onehot.clone(), D, z, h0)
+    torch.cuda.synchronize()
+    del delta, z
+    for t0 in range(0, L, 65536):
+        assert torch.equal(y[:, t0:t0 + 65536].float(), 32.0 * x[:, t0:t0 + 65536].float()), t0
+    expect = torch.zeros_like(hT)
+    expect[:, :, int(n_star(torch.tensor(L - 1)))] = x[:, L - 1, :].float()
+    assert torch.equal(hT, expect)
