@@ -1,6 +1,7 @@
 """HIP-graph capture of libjscan calls (torch.cuda.CUDAGraph): decode steps,
-fused decode steps and a chunked prefill with a caller workspace launch only
-kernels on the caller's stream, so they can be captured once and replayed.
+fused decode steps, a chunked prefill, the trapezoidal prefill and the
+backward, given caller workspaces, launch only kernels on the caller's
+stream, so they can be captured once and replayed.
 
 Each graph is replayed several times from the same starting state, with eager
 library work and synchronisations between the replays, and every replay must
@@ -123,5 +124,48 @@ def test_chunked_prefill_replayed():
             torch.cuda.synchronize()
             assert torch.equal(y, y_ref), rep
             assert torch.equal(hT, h_ref), rep
+    finally:
+        js.set_plan_override(0, 0)
+
+
+def test_backward_and_trapezoidal_prefill_replayed():
+    """The backward (chunked plan, caller workspace and outputs) and the
+    trapezoidal prefill (lam given, caller workspace) captured and replayed."""
+    print_case("graph backward and trapezoidal prefill")
+    b, L, d = 2, 600, 136
+    inp = synth.prefill_inputs(b, L, d, seed=92, io=synth.IO_BF16, h0=True)
+    dy, dhT = synth.output_grads(b, L, d, seed=92)
+    lam, xp, Bp = synth.trap_inputs(b, L, d, seed=92)
+    t = to_device(inp)
+    tdy, tdh, tl = dev_io(dy), dev_f32(dhT), dev_io(lam)
+    args = (t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    try:
+        js.set_plan_override(1, 3)
+        bws = torch.empty(js.backward_workspace_size(b, L, d), dtype=torch.uint8, device="cuda")
+        pws = torch.empty(js.workspace_size(b, L, d), dtype=torch.uint8, device="cuda")
+        g_ref = js.backward(*args, tdy, t["h0"], tdh, workspace=bws)
+        y_ref, h_ref = js.prefill_trap(*args, t["h0"], lam=tl, x_prev=dev_io(xp), B_prev=dev_io(Bp), workspace=pws)
+        torch.cuda.synchronize()
+        g = {k: torch.empty_like(v) for k, v in g_ref.items()}
+        y, hT = torch.empty_like(y_ref), torch.empty_like(h_ref)
+        txp, tBp = dev_io(xp), dev_io(Bp)
+
+        def work():
+            js.backward(*args, tdy, t["h0"], tdh, workspace=bws, out=g)
+            js.prefill_trap(*args, t["h0"], lam=tl, x_prev=txp, B_prev=tBp, y=y, hT=hT, workspace=pws)
+
+        graph = capture(work)
+        for rep in range(REPLAYS):
+            for v in list(g.values()) + [y, hT]:
+                v.zero_()
+            bws.zero_()
+            pws.zero_()
+            js.prefill(t["x"][:1], t["delta"][:1], t["A"], t["B"][:1], t["C"][:1], t["D"], t["z"][:1])
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for k in g_ref:
+                assert torch.equal(g[k], g_ref[k]), (rep, k)
+            assert torch.equal(y, y_ref) and torch.equal(hT, h_ref), rep
     finally:
         js.set_plan_override(0, 0)
