@@ -197,6 +197,81 @@ def summarize_counters(pmc_dir, out_md, command, trace_db=None):
     return per
 
 
+UBENCH_KINDS = {0: "fp32 FMA", 1: "exp2 (v_exp_f32)", 2: "1 exp2 + 4 independent FMA",
+                3: "scan token step (16 x: mul, exp2, mul, FMA, FMA)"}
+
+
+def valu_ceiling(waves_per_simd=(1, 2, 4, 8)):
+    """Measured VALU rates of this GPU (libjscan_ubench.so), per CU per shader
+    clock.  Returns a dict; the plain-FMA rate is the chip's fp32 issue peak,
+    the scan-step rate the ceiling of the scan's instruction mix."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "selective_state_space_11_amd", "libjscan_ubench.so"))
+    d = ctypes.c_double
+    lib.jscan_ubench_valu.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int] + [ctypes.POINTER(d)] * 6
+    lib.jscan_ubench_valu.restype = ctypes.c_int
+    n_cu = 256
+    iters = {0: 20000, 1: 5000, 2: 20000, 3: 5000}
+    rows = []
+    for kind in (0, 1, 2, 3):
+        for wps in (waves_per_simd if kind == 0 else (8,)):
+            waves = n_cu * 4 * wps
+            it = max(1, iters[kind] * 8 // wps)
+            out = [d() for _ in range(6)]
+            rc = lib.jscan_ubench_valu(kind, waves, it, *[ctypes.byref(o) for o in out])
+            if rc != 0:
+                raise RuntimeError(f"jscan_ubench_valu(kind {kind}) failed with {rc}")
+            sec, lane, trans, clk, wall = (o.value for o in out[:5])
+            rate = lane / sec
+            rows.append({"kind": UBENCH_KINDS[kind], "waves_per_simd": wps, "seconds": sec,
+                         "lane_instr_per_s": rate, "trans_lane_instr_per_s": trans / sec,
+                         "clock_mhz": round(clk, 1),
+                         "lane_instr_per_cu_per_clock": rate / (n_cu * clk * 1e6) if clk else None})
+    fma = max(r["lane_instr_per_s"] for r in rows if r["kind"] == UBENCH_KINDS[0])
+    exp = next(r for r in rows if r["kind"] == UBENCH_KINDS[1])["lane_instr_per_s"]
+    mix = next(r for r in rows if r["kind"] == UBENCH_KINDS[2])
+    scan = next(r for r in rows if r["kind"] == UBENCH_KINDS[3])
+    # a transcendental's cost in plain-FMA issue slots, and whether it overlaps FMAs:
+    # group = 1 exp + 4 FMA; serial cost = 4 + exp_slots, parallel = max(4, exp_slots)
+    exp_slots = fma / exp
+    group_slots = 5 * fma / mix["lane_instr_per_s"]
+    scan_instr = 5 * 16 + 3                           # per token: 16 x (mul, exp, mul, fma, fma) + 3
+    scan_slots_model = scan_instr - 16 + 16 * exp_slots
+    scan_slot_rate = scan["lane_instr_per_s"] / scan_instr * scan_slots_model / fma
+    return {"rows": rows, "fma_lane_instr_per_s": fma, "exp_slots": exp_slots,
+            "exp_plus_4fma_group_slots": group_slots, "scan_step_slots_per_chtok": scan_slots_model,
+            "scan_step_frac_of_fma_peak": scan_slot_rate,
+            "scan_step_chtok_per_s": scan["lane_instr_per_s"] / scan_instr}
+
+
+def run_valu_ceiling(out_md, command):
+    r = valu_ceiling()
+    print(json.dumps(r), flush=True)
+    if not out_md:
+        return
+    lines = ["# VALU throughput of the MI355X (gfx950) for the scan's instruction mixes", "",
+             "Command (on the MI355X box, from the repository root):", "", "```", command, "```", "",
+             "Kernels: `selective_state_space_11_amd/csrc/ubench.hip` (built by `__graft_entry__.build()`), plain "
+             "fp32 only (packed fp32 off). `rate` is VALU lane-instructions per second over one timed launch; "
+             "`per CU per clock` divides by 256 CUs and the shader clock the kernel itself read (s_memtime "
+             "over s_memrealtime).", "",
+             "| kernel | waves per SIMD | time (ms) | rate (lane-instr/s) | clock (MHz) | per CU per clock |",
+             "|---|---|---|---|---|---|"]
+    for x in r["rows"]:
+        pc = x["lane_instr_per_cu_per_clock"]
+        lines.append(f"| {x['kind']} | {x['waves_per_simd']} | {x['seconds'] * 1e3:.2f} | "
+                     f"{x['lane_instr_per_s']:.4g} | {x['clock_mhz']:.0f} | {pc:.1f} |")
+    lines += ["", f"- one v_exp_f32 costs {r['exp_slots']:.2f} plain-FMA issue slots;",
+              f"- a group of 1 exp2 + 4 independent FMAs costs {r['exp_plus_4fma_group_slots']:.2f} slots "
+              f"(4 + {r['exp_slots']:.2f} = {4 + r['exp_slots']:.2f} if they do not overlap, "
+              f"{max(4, r['exp_slots']):.2f} if they do);",
+              f"- the scan's token step (16 states) costs {r['scan_step_slots_per_chtok']:.1f} slots and runs at "
+              f"{r['scan_step_frac_of_fma_peak']:.3f} of the plain-FMA rate: "
+              f"{r['scan_step_chtok_per_s']:.4g} channel-token steps per second, the VALU ceiling of a single "
+              f"pass of the scan over its inputs."]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def run_all_configs(log):
     """Time every workload once (GPU) beside the oracle on a sample.
 
@@ -365,6 +440,9 @@ def main():
     ap.add_argument("--all-configs", action="store_true",
                     help="time every workload (batch 2 x 4K, 64K, 256K single and chained, decode x1024, "
                          "7-layer hybrid block) with the oracle on a sample; one JSON line each")
+    ap.add_argument("--valu-ceiling", action="store_true",
+                    help="only measure the VALU rates of this GPU for the scan's instruction mixes "
+                         "(libjscan_ubench.so); --out writes a summary")
     ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR", help="write the HBM traffic summary (no GPU work)")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR",
@@ -404,6 +482,10 @@ def main():
 
     if args.all_configs:
         run_all_configs(log)
+        return
+
+    if args.valu_ceiling:
+        run_valu_ceiling(args.out, args.command)
         return
 
     if args.copy_calibration:

@@ -13,6 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", f) for f in ("jscan.hip", "jscan_bwd.hip")]
 LIB = os.path.join(PKG, "libjscan.so")
+UBENCH_SRC = os.path.join(PKG, "csrc", "ubench.hip")
+UBENCH_LIB = os.path.join(PKG, "libjscan_ubench.so")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,9 +27,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *SRCS]
+def _compile(srcs, lib, verbose):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *srcs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
@@ -35,8 +37,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles libjscan.so and the VALU measurement library libjscan_ubench.so."""
+    _compile([UBENCH_SRC], UBENCH_LIB, verbose)
+    return _compile(SRCS, LIB, verbose)
 
 
 if __name__ == "__main__":

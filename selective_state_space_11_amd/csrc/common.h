@@ -14,6 +14,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kTok = 8;         // tokens per software-pipelined block
 constexpr int kCUs = 256;       // MI355X compute units
 constexpr int64_t kMinChunk = 64;           // shortest chunk worth a carry
+constexpr int kMaxChunks = 4096;            // most chunks a forced plan may ask for
 
 // ---------------------------------------------------------------- I/O types
 __device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -111,21 +112,40 @@ struct Prologue {
   }
 };
 
+// A wave-uniform address as a pointer into the constant address space: the
+// address is taken from the first lane (it is the same in every lane), and
+// loads through it are scalar (s_load into SGPRs).  Without this the
+// compiler sometimes cannot prove a row address uniform and loads the row
+// into VGPRs with a vector load, whose wait then also waits for every
+// prefetch issued before it.  The rows read this way (B and C) are inputs
+// that no kernel writes.
+template <class V, class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) V* uniform_ptr(const T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                     (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return (const __attribute__((address_space(4))) V*)(uintptr_t)u;
+}
+
+// Four dwords as a plain vector type (HIP's uint4 cannot be copied out of the
+// constant address space).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Load S consecutive floats from a wave-uniform address (scalar loads).
 template <int S>
 __device__ __forceinline__ void load_row(float (&v)[S], const float* __restrict__ p) {
   if constexpr (S % 4 == 0) {
+    const auto* q4 = uniform_ptr<u32x4>(p);
 #pragma unroll
     for (int q = 0; q < S / 4; ++q) {
-      const float4 w = reinterpret_cast<const float4*>(p)[q];
-      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+      const u32x4 w = q4[q];
+      v[4 * q] = __uint_as_float(w.x); v[4 * q + 1] = __uint_as_float(w.y);
+      v[4 * q + 2] = __uint_as_float(w.z); v[4 * q + 3] = __uint_as_float(w.w);
     }
   } else {
+    const auto* q1 = uniform_ptr<uint32_t>(p);
 #pragma unroll
-    for (int q = 0; q < S / 2; ++q) {
-      const float2 w = reinterpret_cast<const float2*>(p)[q];
-      v[2 * q] = w.x; v[2 * q + 1] = w.y;
-    }
+    for (int q = 0; q < S; ++q) v[q] = __uint_as_float(q1[q]);
   }
 }
 
@@ -144,14 +164,16 @@ template <int S> struct Row<uint16_t, S> {
   uint32_t w[S / 2];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ p) {
     if constexpr (S % 8 == 0) {
+      const auto* q4 = uniform_ptr<u32x4>(p);
 #pragma unroll
       for (int q = 0; q < S / 8; ++q) {
-        const uint4 v = reinterpret_cast<const uint4*>(p)[q];
+        const u32x4 v = q4[q];
         w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
       }
     } else {
+      const auto* q1 = uniform_ptr<uint32_t>(p);
 #pragma unroll
-      for (int q = 0; q < S / 2; ++q) w[q] = reinterpret_cast<const uint32_t*>(p)[q];
+      for (int q = 0; q < S / 2; ++q) w[q] = q1[q];
     }
   }
   __device__ __forceinline__ float operator[](int s) const {

@@ -31,51 +31,68 @@ jscan_status check_common(int64_t d_state, jscan_io io);
 jscan_status check_ranges(const Range* in, int n_in, const Range* out, int n_out, const void* same_ok = nullptr);
 bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner);
 
-// Launch plan.  The main scan runs `chunks` chunks of chunk_len tokens per
-// sequence with K waves per 64 channels.  When chunks > 1, the tokens before
-// the last chunk are cut into segments of seg_len tokens (seg_per_chunk per
-// chunk) for the chunk-local pass, so that pass fills the GPU on its own.
+// Launch plan of a prefill of `batch` sequences of L tokens.
+//
+// Forward: the main scan runs `chunks` chunks of chunk_len tokens per
+// sequence.  With chunks > 1, pass 1 scans every chunk from a zero state
+// (chunk 0 from h0), a combine folds the chunks' (decay, end state) pairs into
+// each chunk's true starting state, and pass 2 rescans each later chunk from
+// it only until the carried-in part of the state has decayed below fp32
+// resolution.
+//
+// Backward: its sweeps run one wave per (sub-chunk, 64 channels), sub-chunks
+// of sub_len tokens (subs per sequence).  Pass 1 records the chunk-local
+// state at every sub-chunk boundary it passes, so the backward can take its
+// starting states from a prefill's workspace.  With chunks == subs == 1
+// nothing is recorded and the prefill is one plain sweep.
 struct Plan {
-  int K;
-  int chunks;
-  int64_t chunk_len;
-  int seg_per_chunk;
-  int64_t seg_len;
-  int64_t segments() const { return chunks > 1 ? (int64_t)(chunks - 1) * seg_per_chunk : 0; }
+  int chunks;              // forward chunks per sequence
+  int64_t chunk_len;       // tokens per forward chunk (a multiple of kTok)
+  int subs;                // sub-chunks per sequence (the backward's chunks)
+  int64_t sub_len;         // tokens per sub-chunk (a multiple of kTok)
+  bool recorded() const { return chunks > 1 || subs > 1; }
 };
 
 Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner);
-Plan make_plan(int64_t batch, int64_t L, int64_t d_inner, int K, int64_t C_target);
 double wave_efficiency(double waves);
 
 size_t round_up(size_t v);
-// Workspace of a chunked prefill plan, in this order: a tag (first, so that
-// its place does not depend on the plan), chunk-local end states, delta sums,
-// chunk starting states (all state-major) and a conv-history copy.  The
-// fields are region sizes; the off_* functions give byte offsets.
+// Workspace of a recording prefill, in this order: a tag (first, so that its
+// place does not depend on the plan), each forward chunk's end record (its
+// chunk-local end state [b][chunks][16][d] and delta sum [b][chunks][d]), a
+// per-(chunk, channel) flag of negative time steps, the true starting states
+// of the forward chunks [b][chunks][16][d] (chunk 0: unused), and the
+// sub-chunk records (chunk-local state at the end of sub-chunk s
+// [b][subs][16][d] and the delta sum from its chunk's start [b][subs][d];
+// the last sub-chunk has none).  The fields are region sizes; the off_*
+// functions give byte offsets.
 struct WsLayout {
-  size_t tag, S, dsum, hstart, hist, total;
-  size_t off_S() const { return tag; }
-  size_t off_dsum() const { return tag + S; }
-  size_t off_hstart() const { return tag + S + dsum; }
-  size_t off_hist() const { return tag + S + dsum + hstart; }
+  size_t tag, eS, eL, neg, H, sS, sL, total;
+  size_t off_eS() const { return tag; }
+  size_t off_eL() const { return off_eS() + eS; }
+  size_t off_neg() const { return off_eL() + eL; }
+  size_t off_H() const { return off_neg() + neg; }
+  size_t off_sS() const { return off_H() + H; }
+  size_t off_sL() const { return off_sS() + sS; }
 };
 WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p);
 
-// The tag a chunked prefill writes at the start of its workspace: what produced
-// the chunk starting states there.  The backward that reuses them compares it
-// with its own sizes and plan on the GPU.  variant: 0 for the plain
-// recurrence, else 1 (conv) | 2 (softplus) | 4 (trapezoidal) | 8 (RMSNorm).
+// The tag a recording prefill writes at the start of its workspace: what
+// produced the states there.  The backward that reuses them compares it with
+// its own sizes and plan on the GPU.  variant: 0 for the plain recurrence,
+// else 1 (conv) | 2 (softplus) | 4 (trapezoidal) | 8 (RMSNorm).
 constexpr int kTagWords = 8;
 constexpr int64_t kTagMagic = 0x6a7363616e746167LL;
 struct Tag { int64_t w[kTagWords]; };
 Tag make_tag(int64_t batch, int64_t L, int64_t d_inner, const Plan& p, int variant);
 
-// Launches the chunk-local pass and the combine of plan p (chunks > 1):
-// afterwards ws holds, at ws_layout's off_hstart(), hstart[b][c][n][d] = the
-// state before chunk c's first token (c = 0: h0 or zero).
-jscan_status forward_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
-                                  const void* delta, const float* A, const void* B, const float* h0, char* ws,
-                                  const Plan& p, hipStream_t st);
+// Starting states of the sub-chunks of plan p (p.subs > 1), for the
+// backward: hstart[b][s][n][d] = the true state before sub-chunk s's first
+// token.  With `saved` (a plain prefill's workspace, as jscan_prefill leaves
+// it) they are derived from its records; otherwise a state-only pass and the
+// combine first write the records into `rec` (ws_layout(...).total bytes).
+jscan_status sub_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
+                              const void* delta, const float* A, const void* B, const float* h0, char* rec,
+                              const char* saved, float* hstart, const Plan& p, hipStream_t st);
 
 }  // namespace jscan_detail

@@ -8,26 +8,33 @@
 //
 // Work decomposition on MI355X
 // ----------------------------
-// * Lanes map to channels: a wave covers 64 consecutive channels, so each
-//   per-token load of x, delta and z is one coalesced 128-byte row segment.
-// * The 16 states of a channel are split over K waves of one workgroup
-//   (K = 1, 2, 4 or 8); wave g owns states [g*16/K, (g+1)*16/K).  The state
-//   stays in VGPRs for the whole call.  Because a wave owns the same state
-//   indices for all its lanes, the shared per-token rows B_t and C_t are
-//   wave-uniform: they are read with scalar loads into SGPRs (bf16 pairs stay
-//   packed and are widened by a scalar shift or mask) and fed to the VALU as
-//   scalar operands, with no LDS traffic and no VGPRs.
-// * With K > 1 the partial outputs sum_n C*h of the K waves are added through
-//   LDS once per block of tokens, and each wave finishes (D skip, SiLU gate,
-//   rounding, store) a 1/K share of the tokens.
-// * When batch * d_inner is too small to give every SIMD two waves (one wave
-//   per SIMD reaches only half the VALU issue rate on gfx950), the sequence
-//   is cut into chunks scanned in parallel: a first kernel scans each chunk
-//   from a zero state and keeps its end state S_c and its total delta; a
-//   second combines the (decay, offset) pairs (P_c, S_c), P_c =
-//   exp(A * sum delta), in order, seeded with h0, giving every chunk's
-//   starting state; the main kernel then rescans each chunk from its true
-//   starting state.
+// * Lanes map to channels: a wave covers 64 consecutive channels and all 16
+//   states of each, so each per-token load of x, delta and z is one coalesced
+//   128-byte row segment.  The state stays in VGPRs for the whole call.
+//   Because every lane of a wave needs the same per-token rows B_t and C_t,
+//   they are read with scalar loads into SGPRs (bf16 pairs stay packed and
+//   are widened by a scalar shift or mask) and fed to the VALU as scalar
+//   operands, with no LDS traffic and no VGPRs.
+// * The scan is bound by the fp32 VALU, not by HBM: per channel-token it
+//   moves 8 bytes but issues about 92 VALU instructions (16 decays exp2 and
+//   4 plain operations per state, plus the epilogue).  The chip therefore
+//   needs every SIMD busy, and at batch 1 the 8192 channels are only 128
+//   waves: the sequence is cut into chunks scanned in parallel.
+// * Chunked prefill, two passes and a combine:
+//   - pass 1 scans every chunk from a zero state (chunk 0 from h0), writes
+//     y, and records the chunk-local state and the delta sum at the end of
+//     each sub-chunk (the last record of a chunk is its end);
+//   - the combine folds the chunks' (decay, end state) pairs in order,
+//     h <- exp2(A' * sum delta) * h + S, giving each chunk's true starting
+//     state and the final state;
+//   - pass 2 rescans each later chunk from its true starting state while
+//     carrying the part of the state that pass 1 missed, d = exp(A * sum
+//     delta) * h_start (one multiply per state: the decays are shared), and
+//     stops as soon as that part is below fp32 resolution of the state in
+//     every lane of the wave; pass 1's outputs stand for the rest of the
+//     chunk.  The carried part only decays when A <= 0 and delta >= 0, so a
+//     wave that sees A > 0 or a chunk with a negative time step rescans its
+//     whole chunk.
 // * exp(delta*A) is computed as exp2(delta * (A*log2 e)), with A*log2 e
 //   formed once per call in registers.
 //
@@ -51,144 +58,182 @@
 
 namespace jscan_detail {
 
-// ------------------------------------------------- chunk-local end states
-// One lane per channel, all 16 states.  Segment s (of the tokens before the
-// last rescan chunk; every segment has seg_len tokens, a multiple of kTok) of
-// sequence b: S[b][s][n][d] = state after the segment when it starts from
-// zero, dsum[b][s][d] = sum of delta over the segment (accumulated in fp64).
-// The workspace is state-major ([n][d]) so every access is a coalesced row.
+enum ScanMode : int {
+  kWhole = 0,    // one chunk per sequence: from h0, writes y, hT (and the conv history)
+  kLocal = 1,    // pass 1: from zero (chunk 0 from h0), writes y and the sub-chunk records
+  kFix = 2,      // pass 2: chunks >= 1 from their true starting state until the carry has decayed
+};
+
+// A carried difference below this fraction of the lane's largest state
+// magnitude no longer changes the state in fp32.
+constexpr float kSettled = 0x1p-24f;
+
 // Waves per SIMD the main scan's register allocation is held to (the second
 // __launch_bounds__ argument, amdgpu-waves-per-eu; 1 = no bound).  A SIMD
 // lane has 512 VGPRs in granules of 8, so 4 waves allow 128.  The bf16
 // trapezoidal scan needs 129 without a bound (3 waves); held to 4 waves it
 // fits 121 without spilling VGPRs and runs its 64K prefill about 6% faster.
-// Bounds on the other variants measured no gain and spill, so they have none.
-template <class T, int K, bool CONV, bool SP, bool TR>
-constexpr int scan_waves() { return sizeof(T) == 2 && K == 1 && TR ? 4 : 1; }
+// In the chunked passes the bound spills, so they have none.
+template <class T, bool CONV, bool SP, bool TR, int MODE>
+constexpr int scan_waves() { return sizeof(T) == 2 && TR && MODE == kWhole ? 4 : 1; }
 
-template <class T, bool CONV = false, bool SP = false, bool TR = false>
-__global__ __launch_bounds__(256) void k_chunk_state(
-    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const T* __restrict__ Bm, float* __restrict__ S, float* __restrict__ dsum,
-    int64_t L, int64_t d_inner, int64_t seg_len, int n_segs, ProArgs pa) {
+__device__ __forceinline__ uint32_t raw_bits(uint16_t v) { return v; }
+__device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v); }
+
+__device__ __forceinline__ void load_a2(float (&a2)[NSTATE], const float* A, int64_t d) {
+  const float4* Ap = reinterpret_cast<const float4*>(A + d * NSTATE);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = Ap[q];
+    a2[4 * q + 0] = v.x * kLog2e; a2[4 * q + 1] = v.y * kLog2e;
+    a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
+  }
+}
+
+// A record: the lane's 16 chunk-local states (state-major, S[slot][n][d])
+// and the delta sum since the chunk start, through buffer stores (wave-uniform
+// base at channel gbase, the lane's byte offset lb4 and a row offset), which
+// cost no VGPRs for addresses.
+__device__ __forceinline__ void write_record(float* __restrict__ S, float* __restrict__ Ls,
+                                             const float (&h)[NSTATE], double dacc, int64_t slot,
+                                             int64_t d_inner, int64_t gbase, uint32_t lb4) {
+  const auto rs = rsrc(S + slot * NSTATE * d_inner + gbase);
+  const uint32_t row = (uint32_t)(d_inner * 4);
+#pragma unroll
+  for (int n = 0; n < NSTATE; ++n) buf_store(h[n], rs, lb4, (uint32_t)n * row);
+  buf_store((float)dacc, rsrc(Ls + slot * d_inner + gbase), lb4, 0);
+}
+
+// Where the records of a chunk go.  After the block ending at chunk-local
+// token `end`: the chunk's end record when the block ends the chunk, and the
+// record of sub-chunk s when the block ends at the sub-chunk boundary
+// (s + 1) * sub_len inside the sequence.
+struct Records {
+  float* eS; float* eL;        // [b][chunks][16][d], [b][chunks][d]
+  float* sS; float* sL;        // [b][subs][16][d], [b][subs][d], or null (one sub-chunk)
+  int64_t sub_len;
+  int chunks, subs;
+  __device__ __forceinline__ void after_block(int end, int nt, int64_t t0, int64_t L, int64_t b, int c,
+                                              const float (&h)[NSTATE], double dacc, int64_t d_inner,
+                                              int64_t gbase, bool real, uint32_t lb4) const {
+    const int64_t g = t0 + end;                    // global token the block ends at (exclusive)
+    if (sS && g < L && g % sub_len == 0 && real)
+      write_record(sS, sL, h, dacc, b * subs + g / sub_len - 1, d_inner, gbase, lb4);
+    if (end >= nt && real) write_record(eS, eL, h, dacc, b * chunks + c, d_inner, gbase, lb4);
+  }
+};
+
+// Issue priority by progress through the chunk.  A SIMD's arbiter issues the
+// oldest ready wave first, so among waves with the same work the first
+// dispatched finish far ahead of the last, and the SIMD then runs the last
+// stretch with fewer waves and worse latency hiding.  Lowering a wave's
+// priority (s_setprio, 3 = highest) as it passes half, three quarters and
+// nine tenths of its tokens lets the waves behind catch up, so they all
+// finish close together.
+struct ProgressPrio {
+  int t1, t2, t3;
+  __device__ __forceinline__ explicit ProgressPrio(int nt)
+      : t1(nt / 2), t2((int)((int64_t)nt * 3 / 4)), t3((int)((int64_t)nt * 9 / 10)) {}
+  __device__ __forceinline__ void set(int done) const {
+    if (done < t1) __builtin_amdgcn_s_setprio(3);
+    else if (done < t2) __builtin_amdgcn_s_setprio(2);
+    else if (done < t3) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+};
+
+// ---------------------------------------- chunk-local states (backward only)
+// The state half of pass 1 for the plain recurrence, for a backward that has
+// to recompute the records: one lane per channel, all 16 states, chunk c of
+// sequence b from zero (chunk 0 from h0).  Its arithmetic is pass 1's,
+// operation for operation, so both write identical records.
+template <class T>
+__global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ x, const T* __restrict__ delta,
+                                                     const float* __restrict__ A, const T* __restrict__ Bm,
+                                                     const float* __restrict__ h0, Records rec, int64_t L,
+                                                     int64_t d_inner, int64_t chunk_len) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t gbase = ((int64_t)blockIdx.x * 4 + wave) * 64;
   if (gbase >= d_inner) return;                       // whole wave past the end
-  const int seg = blockIdx.y;
+  const int c = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
   const int64_t d = gbase + lo;
 
   float a2[NSTATE], h[NSTATE];
-  const float4* Ap = reinterpret_cast<const float4*>(A + d * NSTATE);
+  load_a2(a2, A, d);
+  const float* hi = c == 0 && h0 ? h0 + (b * d_inner + d) * NSTATE : nullptr;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float4 v = Ap[q];
-    a2[4 * q + 0] = v.x * kLog2e; a2[4 * q + 1] = v.y * kLog2e;
-    a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
-  }
-#pragma unroll
-  for (int n = 0; n < NSTATE; ++n) h[n] = 0.0f;
+  for (int n = 0; n < NSTATE; ++n) h[n] = hi ? hi[n] : 0.0f;
   double dacc = 0.0;
 
-  const int64_t t0 = (int64_t)seg * seg_len;
-  const int nt = (int)seg_len;
+  const int64_t t0 = (int64_t)c * chunk_len;
+  const int nt = (int)std::min<int64_t>(chunk_len, L - t0);
   const T* xrow = x + (b * L + t0) * d_inner + gbase;
   const T* drow = delta + (b * L + t0) * d_inner + gbase;
   const T* brow = Bm + (b * L + t0) * NSTATE;
-  const uint32_t lb = (uint32_t)lo * sizeof(T);      // lane byte offset within a row
+  const uint32_t lb = (uint32_t)lo * sizeof(T);
   const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
-  Prologue<CONV, SP> pro;
-  pro.init(pa, d);
-  pro.start(pa, pa.hist, x, b, L, d_inner, t0, d);
-  // Trapezoidal form: the scan runs on the shifted state g (see trap_seed);
-  // segment 0 starts from g_{-1} - h0 = w_0 B_prev, the combine adds h0.
-  const T* lrow = TR && pa.lam ? static_cast<const T*>(pa.lam) + (b * L + t0) * d_inner + gbase : drow;
-  const float lam_add = TR && !pa.lam ? 0.5f : 0.0f;      // a missing lam reads 0 through the empty resource
-  if constexpr (TR) {
-    if (t0 == 0) trap_seed(h, pa, pro, delta, b, L, d_inner, d, 0);
-  }
+  const int last = (nt - 1) / kTok * kTok;
+  const ProgressPrio prio(nt);
 
-  // Loads of token block bb (always kTok whole tokens: segments are multiples),
-  // and with TR delta and lam of the token after the block (a segment never
-  // ends the sequence, so that token exists).
-  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&ll)[kTok], T& dn, T& ln) {
+  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok]) {
     const int64_t o = (int64_t)bb * d_inner;
-    const auto rd = rsrc(drow + o), rx = rsrc(xrow + o);
-    const auto rl = TR && pa.lam ? rsrc(lrow + o) : rsrc(drow, 0);
+    const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), r0 = rsrc(drow, 0);
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-      buf_load(dd[j], rd, lb, j * rowb);
-      buf_load(xx[j], rx, lb, j * rowb);
-      if constexpr (TR) buf_load(ll[j], rl, lb, j * rowb);
-    }
-    if constexpr (TR) {
-      buf_load(dn, rd, lb, kTok * rowb);
-      buf_load(ln, rl, lb, kTok * rowb);
+      const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
+      buf_load(dd[j], bb + j < nt ? rd : r0, lb, so);
+      buf_load(xx[j], rx, lb, so);
     }
   };
   Row<T, NSTATE> Bc, Bn;
-  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&ll)[kTok], const T& dn,
-                      const T& ln) {
-    float dtv[kTok + 1], lv[kTok + 1];             // TR: delta and lam of the block's tokens and the next
-    if constexpr (TR) {
-#pragma unroll
-      for (int j = 0; j < kTok; ++j) { dtv[j] = pro.dt(widen(dd[j])); lv[j] = widen(ll[j]) + lam_add; }
-      dtv[kTok] = pro.dt(widen(dn));
-      lv[kTok] = widen(ln) + lam_add;
-    }
+  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok]) {
+    float bsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
-      const float dt = TR ? dtv[j] : pro.dt(widen(dd[j]));
-      const float xv = pro.xin(widen(xx[j]));
-      float dx = dt * xv;
-      if constexpr (TR) dx = fmaf(dtv[j + 1] * (1.0f - lv[j + 1]), xv, dx * lv[j]);
-      dacc += (double)dt;
+      const float dt = widen(dd[j]);
+      const float dx = dt * widen(xx[j]);
+      bsum += dt;
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
       Bc = Bn;
       __builtin_amdgcn_sched_barrier(0);
     }
+    dacc += (double)bsum;
+    rec.after_block(bb + kTok, nt, t0, L, b, c, h, dacc, d_inner, gbase, lo == lane, (uint32_t)lo * 4);
   };
-  // Two register sets in turn: block i+1 is in flight while block i computes.
-  T dA[kTok], xA[kTok], lA[kTok], dB[kTok], xB[kTok], lB[kTok], dnA, lnA, dnB, lnB;
-  load_block(0, dA, xA, lA, dnA, lnA);
+  T dA[kTok], xA[kTok], dB[kTok], xB[kTok];
+  load_block(0, dA, xA);
   Bc.load(brow);
   __builtin_amdgcn_s_waitcnt(0);
   for (int base = 0; base < nt; base += 2 * kTok) {
-    load_block(std::min(base + kTok, nt - kTok), dB, xB, lB, dnB, lnB);
-    do_block(base, dA, xA, lA, dnA, lnA);
+    prio.set(base);
+    load_block(std::min(base + kTok, last), dB, xB);
+    do_block(base, dA, xA);
     if (base + kTok >= nt) break;
-    load_block(std::min(base + 2 * kTok, nt - kTok), dA, xA, lA, dnA, lnA);
-    do_block(base + kTok, dB, xB, lB, dnB, lnB);
-  }
-  if (lo == lane) {
-    const int64_t slot = b * n_segs + seg;
-#pragma unroll
-    for (int n = 0; n < NSTATE; ++n) S[(slot * NSTATE + n) * d_inner + d] = h[n];
-    dsum[slot * d_inner + d] = (float)dacc;
+    load_block(std::min(base + 2 * kTok, last), dA, xA);
+    do_block(base + kTok, dB, xB);
   }
 }
 
 // ------------------------------------------------------------ carry combine
-// One lane per (b, n, d), d fastest.  Folds the segments' (P, S) pairs in
-// sequence order, h <- P * h + S with P = exp2(A' * dsum), seeded with h0,
-// and records the state each rescan chunk starts from (every seg_per_chunk
-// segments) in hstart[b][c][n][d].
-//
-// With a convolution prologue it also copies the conv history before the
-// sequence into the workspace (hist_copy), so the rescan's first chunk never
-// reads the caller's history buffer, which the last chunk may overwrite in
-// place.
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, const float* __restrict__ S,
-                                                 const float* __restrict__ dsum, const float* __restrict__ h0,
-                                                 float* __restrict__ hstart, int64_t d_inner, int n_chunks,
-                                                 int seg_per_chunk, const float* __restrict__ hist,
-                                                 float* __restrict__ hist_copy, int hist_rows,
+// One lane per (b, n, d), d fastest.  Folds the forward chunks' (P, S) pairs
+// in sequence order, h <- P * h + S with P = exp2(A' * delta sum) and S the
+// chunk's end record, starting from chunk 0's (which began at h0);
+// H[b][c][n][d] = the state before chunk c, and the state after the last
+// chunk is hT.  Also writes the conv history after the sequence (the last
+// width - 1 raw x, or history values for a short sequence) and the
+// workspace tag.
+template <class T>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, const float* __restrict__ eS,
+                                                 const float* __restrict__ eL, float* __restrict__ H,
+                                                 float* __restrict__ hT, int64_t d_inner, int chunks,
+                                                 const T* __restrict__ x, int64_t L, ProArgs pa,
                                                  int64_t* __restrict__ tag_out, Tag tag) {
-  constexpr int G = 16;                // segments whose loads are in flight together
+  constexpr int G = 16;                // chunks whose loads are in flight together
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t b = blockIdx.y;
   if (tag_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kTagWords)
@@ -197,49 +242,90 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, co
   if (i >= per_seq) return;
   const int64_t n = i / d_inner;
   const int64_t d = i - n * d_inner;
-  const int n_segs = (n_chunks - 1) * seg_per_chunk;
-  if (hist_copy && n < hist_rows) {
-    const int64_t o = (b * hist_rows + n) * d_inner + d;
-    hist_copy[o] = hist ? hist[o] : 0.0f;
-  }
   const float a2 = A[d * NSTATE + n] * kLog2e;
-  const float* Sp = S + (b * n_segs) * per_seq + i;
-  const float* Dp = dsum + (b * n_segs) * d_inner + d;
-  float* Hp = hstart + (b * n_chunks) * per_seq + i;
-  float h = h0 ? h0[(b * d_inner + d) * NSTATE + n] : 0.0f;
-  Hp[0] = h;
-  for (int s0 = 0; s0 < n_segs; s0 += G) {
-    float sv[G], dv[G];
+  const float* Sp = eS + (b * chunks) * per_seq + i;
+  const float* Lp = eL + (b * chunks) * d_inner + d;
+  float* Hp = H + (b * chunks) * per_seq + i;
+  float h = Sp[0];
+  for (int c0 = 1; c0 < chunks; c0 += G) {
+    float sv[G], lv[G];
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const int sg = std::min(s0 + k, n_segs - 1);
-      sv[k] = Sp[(int64_t)sg * per_seq];
-      dv[k] = Dp[(int64_t)sg * d_inner];
+      const int c = std::min(c0 + k, chunks - 1);
+      sv[k] = Sp[(int64_t)c * per_seq];
+      lv[k] = Lp[(int64_t)c * d_inner];
     }
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const int sg = s0 + k;
-      if (sg < n_segs) {
-        h = fmaf(fast_exp2(a2 * dv[k]), h, sv[k]);
-        if ((sg + 1) % seg_per_chunk == 0) Hp[(int64_t)((sg + 1) / seg_per_chunk) * per_seq] = h;
+      if (c0 + k < chunks) {
+        Hp[(int64_t)(c0 + k) * per_seq] = h;
+        h = fmaf(fast_exp2(a2 * lv[k]), h, sv[k]);
       }
+    }
+  }
+  if (hT) hT[(b * d_inner + d) * NSTATE + n] = h;
+  // Conv history after the sequence, by the lane of state 0 of each channel,
+  // slot by slot: with an in-place history (hist_out == hist) slot j is read
+  // from slot j + L >= j, before that slot is written.
+  if (pa.hist_out && n == 0) {
+    for (int j = 0; j < pa.width - 1; ++j) {
+      const int64_t pos = L - (pa.width - 1) + j;
+      const int64_t k = (pa.width - 1) + pos;
+      const float v = pos >= 0 ? widen(x[(b * L + pos) * d_inner + d])
+                               : (pa.hist && k >= 0 ? pa.hist[(b * (pa.width - 1) + k) * d_inner + d] : 0.0f);
+      pa.hist_out[(b * (pa.width - 1) + j) * d_inner + d] = v;
     }
   }
 }
 
+// Starting states of the sub-chunks (for the backward), one lane per
+// (b, s, n, d): sub-chunk 0 starts at h0 (or zero); sub-chunk s >= 1 starts
+// at the boundary g = s * sub_len, inside forward chunk c = (g - 1) /
+// chunk_len, where the true state is P * H[c] + S from the boundary's record
+// (for c = 0 the record itself, which began at h0).
+__global__ __launch_bounds__(256) void k_substarts(const float* __restrict__ A, const float* __restrict__ sS,
+                                                   const float* __restrict__ sL, const float* __restrict__ H,
+                                                   const float* __restrict__ h0, float* __restrict__ hs,
+                                                   int64_t d_inner, int chunks, int subs, int64_t chunk_len,
+                                                   int64_t sub_len) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int s = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int64_t per_seq = d_inner * NSTATE;
+  if (i >= per_seq) return;
+  const int64_t n = i / d_inner;
+  const int64_t d = i - n * d_inner;
+  float v;
+  if (s == 0) {
+    v = h0 ? h0[(b * d_inner + d) * NSTATE + n] : 0.0f;
+  } else {
+    const int64_t j = s - 1;
+    const int64_t c = (s * sub_len - 1) / chunk_len;
+    const float S = sS[((b * subs + j) * NSTATE + n) * d_inner + d];
+    if (c == 0) {
+      v = S;
+    } else {
+      const float a2 = A[d * NSTATE + n] * kLog2e;
+      v = fmaf(fast_exp2(a2 * sL[(b * subs + j) * d_inner + d]), H[((b * chunks + c) * NSTATE + n) * d_inner + d], S);
+    }
+  }
+  hs[((b * subs + s) * NSTATE + n) * d_inner + d] = v;
+}
+
 // ----------------------------------------------------------------- main scan
-struct ScanArgs {
-  const void* x; const void* delta; const float* A; const void* B; const void* C; const float* D;
-  const void* z; const float* hinit;   // h0 (single chunk) or hstart (chunked), may be null
-  void* y; float* hT;
+// Extra arguments of the main scan (pointers into the workspace).
+struct ScanAux {
+  const float* h0;        // [b][d][n] (kWhole, and chunk 0 in kLocal), may be null
+  float* hT;              // kWhole
+  Records rec;            // kLocal: chunk-end and sub-chunk records
+  int32_t* neg;           // kLocal writes, kFix reads: a negative time step in [b][chunk][d]
+  const float* H;         // kFix: chunk starting states [b][chunk][n][d]
   int64_t L, d_inner, chunk_len;
-  int n_chunks;
-  ProArgs pa;
+  int chunks;
 };
 
-// Grid: (ceil(d_inner / 64), chunks, batch); block: K waves.  Wave g of a
-// block owns states [g*16/K, (g+1)*16/K) of the block's 64 channels for the
-// block's chunk of tokens.
+// Grid: (ceil(d_inner / 64), chunks (kFix: chunks - 1), batch); one wave per
+// block, owning all 16 states of its 64 channels for the block's chunk.
 //
 // Tokens go in blocks of kTok, the next block's loads issued before the
 // current block is computed.  A chunk's last block may be partial: its
@@ -248,53 +334,48 @@ struct ScanArgs {
 // 0 * x * B = 0 for finite x and B) and their output equals the last token's,
 // which they store again to the same address.  Every block therefore runs the
 // same branch-free code.
-template <class T, int K, bool CONV = false, bool SP = false, bool TR = false>
-__global__ __launch_bounds__(64 * K, (scan_waves<T, K, CONV, SP, TR>())) void k_scan(
+template <class T, bool CONV, bool SP, bool TR, int MODE>
+__global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_scan(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dw, const T* __restrict__ z,
-    const float* __restrict__ hinit, T* __restrict__ y, float* __restrict__ hT,
-    int64_t L, int64_t d_inner, int64_t chunk_len, int n_chunks, ProArgs pa) {
-  static_assert(K == 1 || !(CONV || SP || TR), "the input prologue and the trapezoidal form run with one wave "
-                                              "per 64 channels");
+    T* __restrict__ y, ScanAux aux, ProArgs pa) {
   static_assert(!(CONV && TR), "the trapezoidal form takes no outer convolution");
-  constexpr int S = NSTATE / K;
-  constexpr int F = kTok / K;          // tokens of a block finished by each wave
-  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x;
+  const int64_t L = aux.L, d_inner = aux.d_inner;
   const int64_t gbase = (int64_t)blockIdx.x * 64;
-  const int c = blockIdx.y;
+  const int c = MODE == kFix ? (int)blockIdx.y + 1 : (int)blockIdx.y;
   const int64_t b = blockIdx.z;
   const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
   const int64_t d = gbase + lo;
-  const int n0 = g * S;
 
-  float a2[S], h[S];
+  float a2[NSTATE], h[NSTATE], dd[MODE == kFix ? NSTATE : 1];
+  load_a2(a2, A, d);
+  bool can_exit = true;
+  if constexpr (MODE == kFix) {
+    const float* hi = aux.H + ((b * aux.chunks + c) * NSTATE) * d_inner + d;
 #pragma unroll
-  for (int s = 0; s < S; ++s) a2[s] = A[d * NSTATE + n0 + s] * kLog2e;
-  // Start state: hstart[b][c][n][d] (state-major) for chunked plans, else
-  // h0[b][d][n] or zero.
-  if (n_chunks > 1) {
-    const float* hi = hinit + ((b * n_chunks + c) * NSTATE + n0) * d_inner + d;
-#pragma unroll
-    for (int s = 0; s < S; ++s) h[s] = hi[(int64_t)s * d_inner];
+    for (int n = 0; n < NSTATE; ++n) {
+      h[n] = hi[(int64_t)n * d_inner];
+      dd[n] = h[n];
+      can_exit = can_exit && a2[n] <= 0.0f;
+    }
+    can_exit = can_exit && aux.neg[(b * aux.chunks + c) * d_inner + d] == 0;
   } else {
-    const float* hi = hinit ? hinit + (b * d_inner + d) * NSTATE + n0 : nullptr;
+    const float* hi = (MODE == kWhole || c == 0) && aux.h0 ? aux.h0 + (b * d_inner + d) * NSTATE : nullptr;
 #pragma unroll
-    for (int s = 0; s < S; ++s) h[s] = hi ? hi[s] : 0.0f;
+    for (int n = 0; n < NSTATE; ++n) h[n] = hi ? hi[n] : 0.0f;
   }
   const float Dd = Dw[d];
 
-  const int64_t t0 = (int64_t)c * chunk_len;
-  const int nt = (int)std::min<int64_t>(chunk_len, L - t0);   // >= 1 for every chunk
+  const int64_t t0 = (int64_t)c * aux.chunk_len;
+  const int nt = (int)std::min<int64_t>(aux.chunk_len, L - t0);   // >= 1 for every chunk
   const int64_t row0 = (b * L + t0) * d_inner + gbase;
   const T* xrow = x + row0;
   const T* drow = delta + row0;
   const T* zrow = z + row0;
   T* yrow = y + row0;
-  const T* brow = Bm + (b * L + t0) * NSTATE + n0;
-  const T* crow = Cm + (b * L + t0) * NSTATE + n0;
-
-  __shared__ float red[K > 1 ? 2 : 1][K > 1 ? K : 1][kTok][64];
+  const T* brow = Bm + (b * L + t0) * NSTATE;
+  const T* crow = Cm + (b * L + t0) * NSTATE;
 
   const uint32_t lb = (uint32_t)lo * sizeof(T);      // lane byte offset within a row
   const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
@@ -305,8 +386,8 @@ __global__ __launch_bounds__(64 * K, (scan_waves<T, K, CONV, SP, TR>())) void k_
   // chunk 0 starts from h0 + w_0 B_prev, later chunks from the combine's g.
   const T* lrow = TR && pa.lam ? static_cast<const T*>(pa.lam) + row0 : drow;
   const float lam_add = TR && !pa.lam ? 0.5f : 0.0f;      // a missing lam reads 0 through the empty resource
-  if constexpr (TR) {
-    if (c == 0) trap_seed(h, pa, pro, delta, b, L, d_inner, d, n0);
+  if constexpr (TR && MODE != kFix) {
+    if (c == 0) trap_seed(h, pa, pro, delta, b, L, d_inner, d, 0);
   }
 
   // Loads of token block bb.  Rows past the chunk's end are clamped onto its
@@ -314,17 +395,17 @@ __global__ __launch_bounds__(64 * K, (scan_waves<T, K, CONV, SP, TR>())) void k_
   // TR also: delta and lam of the token after the block (0 past the
   // sequence's end), and for the block's C_t . B_t products lane l's pair of
   // states 2 (l & 7) + {0, 1} of token bb + (l >> 3), B and C.
-  auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&ll)[kTok], T (&xff)[F],
-                        T (&zff)[F], T& dn, T& ln, Pair<T>& pb, Pair<T>& pc) {
+  auto load_block = [&](int bb, T (&dq)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&ll)[kTok], T& dn, T& ln,
+                        Pair<T>& pb, Pair<T>& pc) {
     const int64_t o = (int64_t)bb * d_inner;
     const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), r0 = rsrc(drow, 0);
     const auto rl = TR && pa.lam ? rsrc(lrow + o) : r0;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
-      buf_load(dd[j], bb + j < nt ? rd : r0, lb, so);
+      buf_load(dq[j], bb + j < nt ? rd : r0, lb, so);
       buf_load(xx[j], rx, lb, so);
-      if constexpr (K == 1) buf_load(zz[j], rz, lb, so);
+      buf_load(zz[j], rz, lb, so);
       if constexpr (TR) buf_load(ll[j], rl, lb, so);
     }
     if constexpr (TR) {
@@ -336,32 +417,24 @@ __global__ __launch_bounds__(64 * K, (scan_waves<T, K, CONV, SP, TR>())) void k_
       pb.load(rsrc(brow + (int64_t)bb * NSTATE), vo);
       pc.load(rsrc(crow + (int64_t)bb * NSTATE), vo);
     }
-    if constexpr (K > 1) {
-#pragma unroll
-      for (int i = 0; i < F; ++i) {
-        const uint32_t so = (uint32_t)(std::min(bb + i * K + g, nt - 1) - bb) * rowb;
-        buf_load(xff[i], rx, lb, so); buf_load(zff[i], rz, lb, so);
-      }
-    }
   };
 
   // B of the next token is prefetched a token ahead; C is needed only after
   // the token's state updates, so it is loaded at the token's start.
-  Row<T, S> Bc, Bn, Cv;
-  int buf = 0;
+  Row<T, NSTATE> Bc, Bn, Cv;
+  double dacc = 0.0;                 // kLocal: delta sum since the chunk start
+  uint32_t negbits = 0;              // kLocal: OR of the raw time steps (sign bit)
   // y of token bb + j (padding tokens map onto the last token's address and
-  // store the identical value again).
-  // With a convolution, a padding token's input differs (its history has
-  // shifted), so only real tokens store.
+  // store the identical value again).  With a convolution, a padding token's
+  // input differs (its history has shifted), so only real tokens store.
   auto finish = [&](__amdgpu_buffer_rsrc_t ry, int bb, int j, float acc, float xv, float zv) {
     const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
     if (!CONV || bb + j < nt) buf_store(to_io(fmaf(Dd, xv, acc) * silu(zv), T()), ry, lb, so);
   };
-  auto do_block = [&](int bb, const T (&dd)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
-                      const T (&ll)[kTok], const T (&xff)[F], const T (&zff)[F], const T& dn, const T& ln,
-                      const Pair<T>& pb, const Pair<T>& pc) {
+  // Returns true (kFix) once the carried part has settled in every lane.
+  auto do_block = [&](int bb, const T (&dq)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
+                      const T (&ll)[kTok], const T& dn, const T& ln, const Pair<T>& pb, const Pair<T>& pc) {
     const auto ry = rsrc(yrow + (int64_t)bb * d_inner);
-    float part[kTok];
     // TR: delta and lam of the block's tokens and of the one after it (a
     // padding token's or a missing one's delta is 0), and C_t . B_t summed
     // over the 8 lanes of each token (lane 8 j holds token j's).
@@ -369,7 +442,7 @@ __global__ __launch_bounds__(64 * K, (scan_waves<T, K, CONV, SP, TR>())) void k_
     if constexpr (TR) {
 #pragma unroll
       for (int j = 0; j < kTok; ++j) {
-        dtv[j] = bb + j < nt ? pro.dt(widen(dd[j])) : 0.0f;
+        dtv[j] = bb + j < nt ? pro.dt(widen(dq[j])) : 0.0f;
         lv[j] = widen(ll[j]) + lam_add;
       }
       dtv[kTok] = t0 + bb + kTok < L ? pro.dt(widen(dn)) : 0.0f;
@@ -379,80 +452,99 @@ __global__ __launch_bounds__(64 * K, (scan_waves<T, K, CONV, SP, TR>())) void k_
       cbl += dpp_mov<0x4E>(cbl);        // lane ^ 2
       cbl += dpp_mov<0x141>(cbl);       // lane ^ 7 within 8 lanes
     }
+    float bsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
       // A padding token's delta reads 0; softplus would turn that into a
       // positive step, so it is forced back to 0 (a wave-uniform select).
-      const float dt = TR ? dtv[j] : SP ? (bb + j < nt ? pro.dt(widen(dd[j])) : 0.0f) : widen(dd[j]);
+      const float dt = TR ? dtv[j] : SP ? (bb + j < nt ? pro.dt(widen(dq[j])) : 0.0f) : widen(dq[j]);
       const float xv = pro.xin(widen(xx[j]));
       float dx = dt * xv, wn = 0.0f;
       if constexpr (TR) {
         wn = dtv[j + 1] * (1.0f - lv[j + 1]) * xv;        // w_{t+1}
         dx = fmaf(dx, lv[j], wn);                          // dt lam x + w_{t+1}
       }
+      if constexpr (MODE == kLocal) {
+        bsum += dt;
+        if constexpr (!SP) negbits |= raw_bits(dq[j]);
+      }
+      if constexpr (MODE == kFix) {
 #pragma unroll
-      for (int s = 0; s < S; ++s) h[s] = fmaf(fast_exp2(dt * a2[s]), h[s], dx * Bc[s]);
+        for (int n = 0; n < NSTATE; ++n) {
+          const float e = fast_exp2(dt * a2[n]);
+          h[n] = fmaf(e, h[n], dx * Bc[n]);
+          dd[n] *= e;
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
+      }
       float acc = 0.0f;
 #pragma unroll
-      for (int s = 0; s < S; ++s) acc = fmaf(Cv[s], h[s], acc);
+      for (int n = 0; n < NSTATE; ++n) acc = fmaf(Cv[n], h[n], acc);
       if constexpr (TR) acc = fmaf(-wn, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbl), 8 * j)), acc);
-      if constexpr (K == 1) finish(ry, bb, j, acc, xv, widen(zz[j]));
-      else part[j] = acc;
+      finish(ry, bb, j, acc, xv, widen(zz[j]));
       Bc = Bn;
       // Keep each token's scalar B/C loads in its own token: hoisting them
       // across tokens would hold several rows in SGPRs at once and spill.
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (K > 1) {
-      // Partial sums through LDS, double-buffered so one barrier per block
-      // suffices: a wave overwrites buffer p only after the barrier of the
-      // following block, which every wave reaches after its reads of p.
-#pragma unroll
-      for (int j = 0; j < kTok; ++j) red[buf][g][j][lane] = part[j];
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < F; ++i) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int w = 0; w < K; ++w) acc += red[buf][w][i * K + g][lane];
-        finish(ry, bb, i * K + g, acc, widen(xff[i]), widen(zff[i]));
-      }
-      buf ^= 1;
+    if constexpr (MODE == kLocal) {
+      dacc += (double)bsum;
+      aux.rec.after_block(bb + kTok, nt, t0, L, b, c, h, dacc, d_inner, gbase, lo == lane, (uint32_t)lo * 4);
     }
+    if constexpr (MODE == kFix) {
+      float dm = 0.0f, hm = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) {
+        dm = fmaxf(dm, fabsf(dd[n]));
+        hm = fmaxf(hm, fabsf(h[n]));
+      }
+      const bool settled = can_exit && dm <= hm * kSettled;    // false for NaN
+      return __builtin_amdgcn_ballot_w64(!settled) == 0;
+    }
+    return false;
   };
 
   // Two register sets in turn: block i+1 is in flight while block i computes.
-  T dA[kTok], xA[kTok], zA[kTok], lA[kTok], fxA[F], fzA[F], dnA, lnA;
-  T dB[kTok], xB[kTok], zB[kTok], lB[kTok], fxB[F], fzB[F], dnB, lnB;
+  T dA[kTok], xA[kTok], zA[kTok], lA[kTok], dnA, lnA;
+  T dB[kTok], xB[kTok], zB[kTok], lB[kTok], dnB, lnB;
   Pair<T> pbA, pcA, pbB, pcB;
-  load_block(0, dA, xA, zA, lA, fxA, fzA, dnA, lnA, pbA, pcA);
+  load_block(0, dA, xA, zA, lA, dnA, lnA, pbA, pcA);
   Bc.load(brow);
   __builtin_amdgcn_s_waitcnt(0);
   // Prefetches past the chunk's end are clamped to its last block (valid rows,
   // values unused), so every row offset below stays non-negative.
   const int last = (nt - 1) / kTok * kTok;
+  const ProgressPrio prio(nt);
   for (int base = 0; base < nt; base += 2 * kTok) {
-    load_block(std::min(base + kTok, last), dB, xB, zB, lB, fxB, fzB, dnB, lnB, pbB, pcB);
-    do_block(base, dA, xA, zA, lA, fxA, fzA, dnA, lnA, pbA, pcA);
+    if constexpr (MODE != kFix) prio.set(base);
+    load_block(std::min(base + kTok, last), dB, xB, zB, lB, dnB, lnB, pbB, pcB);
+    if (do_block(base, dA, xA, zA, lA, dnA, lnA, pbA, pcA)) break;
     if (base + kTok >= nt) break;
-    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, lA, fxA, fzA, dnA, lnA, pbA, pcA);
-    do_block(base + kTok, dB, xB, zB, lB, fxB, fzB, dnB, lnB, pbB, pcB);
+    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, lA, dnA, lnA, pbA, pcA);
+    if (do_block(base + kTok, dB, xB, zB, lB, dnB, lnB, pbB, pcB)) break;
   }
-  if (hT && c == n_chunks - 1 && lo == lane) {
-    float* ho = hT + (b * d_inner + d) * NSTATE + n0;
+  if constexpr (MODE == kLocal) {
+    constexpr uint32_t sign = sizeof(T) == 2 ? 0x8000u : 0x80000000u;
+    if (lo == lane) aux.neg[(b * aux.chunks + c) * d_inner + d] = (negbits & sign) ? 1 : 0;
+  }
+  if constexpr (MODE == kWhole) {
+    if (aux.hT && lo == lane) {
+      float* ho = aux.hT + (b * d_inner + d) * NSTATE;
 #pragma unroll
-    for (int s = 0; s < S; ++s) ho[s] = h[s];
-  }
-  // Conv history after the sequence: its last width-1 raw x (read back from
-  // x, or from the history before it when the sequence is shorter).  With
-  // chunks > 1 every read here comes from x, so an in-place history is safe.
-  if constexpr (CONV) {
-    if (pa.hist_out && c == n_chunks - 1 && lo == lane) {
-      for (int j = 0; j < pa.width - 1; ++j) {
-        const float v = pro.before(pa, pa.hist, x, b, L, d_inner, L - (pa.width - 1) + j, d);
-        pa.hist_out[(b * (pa.width - 1) + j) * d_inner + d] = v;
+      for (int n = 0; n < NSTATE; ++n) ho[n] = h[n];
+    }
+    // Conv history after the sequence: its last width-1 raw x (read back from
+    // x, or from the history before it when the sequence is shorter).
+    if constexpr (CONV) {
+      if (pa.hist_out && lo == lane) {
+        for (int j = 0; j < pa.width - 1; ++j) {
+          const float v = pro.before(pa, pa.hist, x, b, L, d_inner, L - (pa.width - 1) + j, d);
+          pa.hist_out[(b * (pa.width - 1) + j) * d_inner + d] = v;
+        }
       }
     }
   }
@@ -655,7 +747,6 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
 thread_local std::string t_last_error;
 thread_local hipEvent_t t_ev_before = nullptr;
 thread_local hipEvent_t t_ev_after = nullptr;
-thread_local int t_force_K = 0;
 thread_local int t_force_chunks = 0;
 
 jscan_status fail(jscan_status s, const std::string& msg) {
@@ -675,7 +766,6 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
-
 bool overlap(const Range& a, const Range& b) {
   if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
   const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
@@ -684,12 +774,11 @@ bool overlap(const Range& a, const Range& b) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-
-// Relative throughput of the scan loops with `waves` waves launched on the
-// 1024 SIMDs, measured on MI355X with the one-wave-per-64-channels kernels
-// (main scan at batch 1 and batch 8, d_inner 8192): one wave per SIMD issues
-// at most every other cycle, a few more hide the load and exp latencies, and
-// many more even out the tail across CUs.
+// Relative throughput of the backward's sweeps with `waves` waves launched on
+// the 1024 SIMDs, measured on MI355X with the one-wave-per-64-channels
+// kernels: one wave per SIMD issues at most every other cycle, a few more
+// hide the load and exp latencies, and many more even out the tail across
+// CUs.
 double wave_efficiency(double waves) {
   static const double lw[] = {10, 11, 12, 13, 14, 15};
   static const double ef[] = {0.37, 0.53, 0.68, 0.91, 0.96, 1.0};
@@ -700,69 +789,125 @@ double wave_efficiency(double waves) {
   return 1.0;
 }
 
-Plan make_plan(int64_t batch, int64_t L, int64_t d_inner, int K, int64_t C_target) {
-  Plan p{K, 1, std::max<int64_t>(L, 1), 1, std::max<int64_t>(L, 1)};
-  const int64_t groups = batch * ((d_inner + 63) / 64);
-  if (L <= 0 || C_target <= 1 || groups <= 0) return p;
-  // segments per chunk: about 32 chunk-local waves per SIMD (rounded down: the
-  // combine's work grows with the segment count), >= 64 tokens each
-  const int64_t want = (32 * 4 * kCUs) / (groups * (C_target - 1));
-  int64_t F = std::max<int64_t>(1, std::min<int64_t>(want, (L / C_target) / kMinChunk));
-  int64_t seg = (L + C_target * F - 1) / (C_target * F);
-  seg = (seg + kTok - 1) / kTok * kTok;                    // whole token blocks
-  int64_t chunk_len = seg * F;
-  int64_t C = (L + chunk_len - 1) / chunk_len;
-  if (C <= 1) return p;
-  while ((C - 1) * F > 65535) { F = (F + 1) / 2; seg *= 2; chunk_len = seg * F; C = (L + chunk_len - 1) / chunk_len; }
-  if (C <= 1) return p;
-  return Plan{K, (int)C, chunk_len, (int)F, seg};
+// Throughput of one SIMD running the forward scan with k resident waves,
+// relative to four (measured on MI355X at batch 1 x 64K and batch 8 x 16K
+// with the progress priority): one wave issues well under half the time, two
+// reach about three quarters.  A SIMD holds at most four of these one-wave
+// workgroups (a compute unit takes at most 16 workgroups), so a launch runs in
+// rounds of 4096 waves.
+constexpr int kResidentWaves = 4 * 4 * kCUs;
+double simd_throughput(int k) {
+  static const double t[] = {0.0, 0.45, 0.75, 0.92, 1.0};
+  return t[std::min(std::max(k, 0), 4)];
 }
 
-// Pick the plan.  Estimated time per channel-token: the rescan's VALU issue
-// slots (about 150: 16 x (mul, exp at quarter rate, mul, fma, fma) plus the
-// epilogue) over the efficiency its wave count reaches, plus the chunk-local
-// pass (about 115 slots) on the (C-1)/C of the tokens that need a carry, over
-// its own efficiency.  Measured on MI355X, splitting a channel's states over
-// K > 1 waves never beat one wave per 64 channels with more chunks (the
-// per-token work the K waves repeat and their barriers cost more than the
-// extra chunk-local work), so the automatic plan keeps K = 1.
-Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner) {
-  if (t_force_K > 0 && t_force_chunks > 0)
-    return make_plan(batch, L, d_inner, t_force_K, std::min<int64_t>(t_force_chunks, std::max<int64_t>(L, 1)));
-  const int64_t groups = batch * ((d_inner + 63) / 64);
-  if (L <= 0 || groups <= 0) return make_plan(batch, L, d_inner, 1, 1);
-  Plan best = make_plan(batch, L, d_inner, 1, 1);
-  double best_cost = 1e300;
-  for (int64_t C = 1; C <= 4096; C *= 2) {
-    if (C > 1 && L / C < kMinChunk) break;
-    const Plan p = make_plan(batch, L, d_inner, 1, C);
-    double cost = 150.0 / wave_efficiency((double)groups * p.chunks);
-    if (p.chunks > 1)
-      cost += 115.0 * (double)(p.chunks - 1) / p.chunks / wave_efficiency((double)groups * p.segments());
-    if (cost < best_cost * 0.999) { best = p; best_cost = cost; }
+// Time of a scan launch with `waves` waves of `tokens` tokens each, in units
+// of a token step of one wave at full occupancy; a wave's setup (parameters,
+// starting state, the first block's loads) costs about kWaveSetup steps.
+constexpr double kWaveSetup = 24.0;
+double scan_time(double waves, double tokens) {
+  if (waves <= 0 || tokens <= 0) return 0.0;
+  tokens += kWaveSetup;
+  const double rounds = std::floor(waves / kResidentWaves);
+  const double rest = waves - rounds * kResidentWaves;
+  double t = rounds * 4.0 * tokens;                       // full rounds: 4 waves per SIMD
+  if (rest > 0) {
+    const int k = (int)std::ceil(rest / (4.0 * kCUs));    // waves per SIMD in the last round
+    t += k * tokens / simd_throughput(k);
   }
-  return best;
+  return t;
 }
 
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Pieces of about L / n tokens: a multiple of kTok, n' = ceil(L / len) of them.
+void split(int64_t L, int64_t n, int64_t* len, int* count) {
+  const int64_t Lp = std::max<int64_t>(L, 1);
+  if (L <= 0 || n <= 1) { *len = Lp; *count = 1; return; }
+  int64_t l = (L + n - 1) / n;
+  l = (l + kTok - 1) / kTok * kTok;
+  *len = l;
+  *count = (int)((L + l - 1) / l);
+}
+
+// Sub-chunk count: the granularity of the backward's sweeps, from their cost
+// per channel-token (about 150 issue slots over the efficiency of their wave
+// count, plus a chunk-local adjoint pass of about 115 on the (C-1)/C of the
+// tokens that need a carry, run on segments that fill about 32 waves per
+// SIMD).
+int64_t choose_subs(int64_t batch, int64_t L, int64_t d_inner) {
+  const int64_t groups = batch * ((d_inner + 63) / 64);
+  if (L <= 0 || groups <= 0) return 1;
+  int64_t best = 1;
+  double best_cost = 1e300;
+  for (int64_t C = 1; C <= 4096; C *= 2) {
+    if (C > 1 && L / C < kMinChunk) break;
+    int64_t len;
+    int subs;
+    split(L, C, &len, &subs);
+    const int64_t want = (32 * 4 * kCUs) / (groups * std::max(1, subs - 1));
+    const int64_t F = std::max<int64_t>(1, std::min<int64_t>(want, len / kMinChunk));
+    double cost = 150.0 / wave_efficiency((double)groups * subs);
+    if (subs > 1) cost += 115.0 * (double)(subs - 1) / subs / wave_efficiency((double)groups * (subs - 1) * F);
+    if (cost < best_cost * 0.999) { best = subs; best_cost = cost; }
+  }
+  return best;
+}
+
+// Forward chunk count from the estimated time of pass 1 (every token, at the
+// occupancy its wave count reaches) and pass 2 (about kFixTokens tokens of
+// every chunk but the first: the carried-in state decays below fp32
+// resolution within about 100 tokens at the configurations' decay rates, and
+// a pass-2 token costs about 1.2 pass-1 tokens), plus a small fixed cost per
+// launch (about 8 token steps).  At batch 1 x 64K this picks 32 chunks: one round of four waves per
+// SIMD.
+Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner) {
+  Plan p{1, std::max<int64_t>(L, 1), 1, std::max<int64_t>(L, 1)};
+  if (t_force_chunks > 0) {
+    split(L, std::min<int64_t>(t_force_chunks, std::max<int64_t>(L, 1)), &p.chunk_len, &p.chunks);
+    p.sub_len = p.chunk_len;
+    p.subs = p.chunks;
+    return p;
+  }
+  const int64_t groups = batch * ((d_inner + 63) / 64);
+  if (L <= 0 || groups <= 0) return p;
+  split(L, choose_subs(batch, L, d_inner), &p.sub_len, &p.subs);
+  constexpr double kFixTokens = 128.0, kLaunch = 8.0;
+  double best = 1e300;
+  for (int64_t C = 1; C <= 4096; C = C < 8 ? C + 1 : C * 2) {
+    if (C > 1 && L / C < kMinChunk) break;
+    int64_t len;
+    int chunks;
+    split(L, C, &len, &chunks);
+    double t = scan_time((double)groups * chunks, (double)len);
+    if (chunks > 1)
+      t += 1.2 * scan_time((double)groups * (chunks - 1), std::min<double>((double)len, kFixTokens)) + 2 * kLaunch;
+    if (t < best * 0.999) { best = t; p.chunks = chunks; p.chunk_len = len; }
+  }
+  return p;
+}
 
 WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
+  (void)L;
   WsLayout w{};
-  if (p.chunks > 1) {
-    const size_t segs = (size_t)p.segments();
-    w.S = round_up((size_t)batch * segs * (size_t)d_inner * NSTATE * sizeof(float));
-    w.dsum = round_up((size_t)batch * segs * (size_t)d_inner * sizeof(float));
-    w.hstart = round_up((size_t)batch * (size_t)p.chunks * (size_t)d_inner * NSTATE * sizeof(float));
-    w.hist = round_up((size_t)batch * 3 * (size_t)d_inner * sizeof(float));   // conv history copy
+  if (p.recorded()) {
+    const size_t B = (size_t)batch, Dn = (size_t)d_inner, C = (size_t)p.chunks;
     w.tag = round_up(kTagWords * sizeof(int64_t));
+    w.eS = round_up(B * C * NSTATE * Dn * sizeof(float));
+    w.eL = round_up(B * C * Dn * sizeof(float));
+    w.neg = round_up(B * C * Dn * sizeof(int32_t));
+    w.H = round_up(B * C * NSTATE * Dn * sizeof(float));
+    if (p.subs > 1) {
+      w.sS = round_up(B * (size_t)p.subs * NSTATE * Dn * sizeof(float));
+      w.sL = round_up(B * (size_t)p.subs * Dn * sizeof(float));
+    }
   }
-  w.total = w.tag + w.S + w.dsum + w.hstart + w.hist;
+  w.total = w.tag + w.eS + w.eL + w.neg + w.H + w.sS + w.sL;
   return w;
 }
 
 Tag make_tag(int64_t batch, int64_t L, int64_t d_inner, const Plan& p, int variant) {
-  return Tag{{kTagMagic, batch, L, d_inner, p.chunks, p.chunk_len, p.seg_per_chunk, variant}};
+  return Tag{{kTagMagic, batch, L, d_inner, p.chunks, p.chunk_len, p.sub_len, variant}};
 }
 
 bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner) {
@@ -775,28 +920,21 @@ bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner) {
   return L <= INT32_MAX && batch <= 65535 && d_inner <= (1 << 24);
 }
 
-template <class T, int K, bool CONV, bool SP, bool TR>
-hipError_t launch_scan(const ScanArgs& a, int64_t batch, hipStream_t st) {
-  dim3 grid((unsigned)((a.d_inner + 63) / 64), (unsigned)a.n_chunks, (unsigned)batch);
-  hipLaunchKernelGGL((k_scan<T, K, CONV, SP, TR>), grid, dim3(64 * K), 0, st, static_cast<const T*>(a.x),
-                     static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
-                     a.D, static_cast<const T*>(a.z), a.hinit,
-                     static_cast<T*>(a.y), a.hT, a.L, a.d_inner, a.chunk_len, a.n_chunks, a.pa);
+template <class T, bool CONV, bool SP, bool TR, int MODE>
+hipError_t launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, void* y, const ScanAux& aux, const ProArgs& pa,
+                       unsigned chunks, int64_t batch, hipStream_t st) {
+  dim3 grid((unsigned)((aux.d_inner + 63) / 64), chunks, (unsigned)batch);
+  hipLaunchKernelGGL((k_scan<T, CONV, SP, TR, MODE>), grid, dim3(64), 0, st, static_cast<const T*>(x),
+                     static_cast<const T*>(delta), A, static_cast<const T*>(B), static_cast<const T*>(C), D,
+                     static_cast<const T*>(z), static_cast<T*>(y), aux, pa);
   return hipGetLastError();
 }
 
-template <class T, bool CONV, bool SP, bool TR>
-hipError_t launch_scan_k(int K, const ScanArgs& a, int64_t batch, hipStream_t st) {
-  if constexpr (CONV || SP || TR) {
-    return launch_scan<T, 1, CONV, SP, TR>(a, batch, st);     // these run with K = 1
-  } else {
-    switch (K) {
-      case 1: return launch_scan<T, 1, false, false, false>(a, batch, st);
-      case 2: return launch_scan<T, 2, false, false, false>(a, batch, st);
-      case 4: return launch_scan<T, 4, false, false, false>(a, batch, st);
-      default: return launch_scan<T, 8, false, false, false>(a, batch, st);
-    }
-  }
+Records records_in(char* ws, const WsLayout& w, const Plan& p) {
+  return Records{reinterpret_cast<float*>(ws + w.off_eS()), reinterpret_cast<float*>(ws + w.off_eL()),
+                 p.subs > 1 ? reinterpret_cast<float*>(ws + w.off_sS()) : nullptr,
+                 p.subs > 1 ? reinterpret_cast<float*>(ws + w.off_sL()) : nullptr, p.sub_len, p.chunks, p.subs};
 }
 
 template <class T, bool CONV, bool SP, bool TR>
@@ -805,68 +943,76 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
                          const float* h0, void* y, float* hT, char* ws, const Plan& p, const ProArgs& pa,
                          bool rms, hipStream_t st) {
   const WsLayout w = ws_layout(batch, L, d_inner, p);
-  float* S = reinterpret_cast<float*>(ws + w.off_S());
-  float* dsum = reinterpret_cast<float*>(ws + w.off_dsum());
-  float* hstart = reinterpret_cast<float*>(ws + w.off_hstart());
-  float* hist_copy = reinterpret_cast<float*>(ws + w.off_hist());
-  int64_t* tag_out = reinterpret_cast<int64_t*>(ws);
-  const int variant = (CONV ? 1 : 0) | (SP ? 2 : 0) | (TR ? 4 : 0) | (rms ? 8 : 0);
-  hipError_t e;
-
-  ProArgs scan_pa = pa;
-  if (p.chunks > 1) {
-    const int segs = (int)p.segments();
-    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)segs, (unsigned)batch);
-    hipLaunchKernelGGL((k_chunk_state<T, CONV, SP, TR>), g1, dim3(256), 0, st, static_cast<const T*>(x),
-                       static_cast<const T*>(delta), A, static_cast<const T*>(B), S, dsum, L, d_inner, p.seg_len,
-                       segs, pa);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
-    const int hist_rows = CONV ? pa.width - 1 : 0;
-    dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
-    hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks,
-                       p.seg_per_chunk, pa.hist, hist_rows > 0 ? hist_copy : nullptr, hist_rows, tag_out,
-                       make_tag(batch, L, d_inner, p, variant));
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
-    if (hist_rows > 0) scan_pa.hist = hist_copy;
-  }
-  ScanArgs a{x, delta, A, B, C, D, z, p.chunks > 1 ? hstart : h0, y, hT, L, d_inner, p.chunk_len, p.chunks,
-             scan_pa};
+  ScanAux aux{h0, hT, Records{}, nullptr, nullptr, L, d_inner, p.chunk_len, p.chunks};
   hipEvent_t eb = t_ev_before, ea = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
+  hipError_t e;
   if (eb && ea && (e = hipEventRecord(eb, st)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = launch_scan_k<T, CONV, SP, TR>(p.K, a, batch, st)) != hipSuccess) return hip_fail(e, "scan launch");
+  if (!p.recorded()) {
+    if ((e = launch_scan<T, CONV, SP, TR, kWhole>(x, delta, A, B, C, D, z, y, aux, pa, 1, batch, st)) !=
+        hipSuccess)
+      return hip_fail(e, "scan launch");
+    if (eb && ea && (e = hipEventRecord(ea, st)) != hipSuccess) return hip_fail(e, "event record");
+    return JSCAN_OK;
+  }
+  aux.rec = records_in(ws, w, p);
+  aux.neg = reinterpret_cast<int32_t*>(ws + w.off_neg());
+  float* H = reinterpret_cast<float*>(ws + w.off_H());
+  aux.H = H;
+  if ((e = launch_scan<T, CONV, SP, TR, kLocal>(x, delta, A, B, C, D, z, y, aux, pa, (unsigned)p.chunks, batch,
+                                                st)) != hipSuccess)
+    return hip_fail(e, "scan launch");
   if (eb && ea && (e = hipEventRecord(ea, st)) != hipSuccess) return hip_fail(e, "event record");
+  const int variant = (CONV ? 1 : 0) | (SP ? 2 : 0) | (TR ? 4 : 0) | (rms ? 8 : 0);
+  dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
+  hipLaunchKernelGGL((k_combine<T>), g2, dim3(256), 0, st, A, aux.rec.eS, aux.rec.eL, H, hT, d_inner, p.chunks,
+                     static_cast<const T*>(x), L, CONV ? pa : ProArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 1},
+                     reinterpret_cast<int64_t*>(ws), make_tag(batch, L, d_inner, p, variant));
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
+  if (p.chunks > 1 &&
+      (e = launch_scan<T, CONV, SP, TR, kFix>(x, delta, A, B, C, D, z, y, aux, pa, (unsigned)(p.chunks - 1), batch,
+                                              st)) != hipSuccess)
+    return hip_fail(e, "scan launch");
   return JSCAN_OK;
 }
 
-// Chunk starting states of a chunked plan (the chunk-local pass and the
-// combine, without a prologue), for callers other than the prefill.
-jscan_status forward_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
-                                  const void* delta, const float* A, const void* B, const float* h0, char* ws,
-                                  const Plan& p, hipStream_t st) {
-  if (p.chunks <= 1) return JSCAN_OK;
+template <class T>
+jscan_status sub_starts_t(int64_t batch, int64_t L, int64_t d_inner, const void* x, const void* delta,
+                          const float* A, const void* B, const float* h0, char* rec, const char* saved,
+                          float* hstart, const Plan& p, hipStream_t st) {
   const WsLayout w = ws_layout(batch, L, d_inner, p);
-  float* S = reinterpret_cast<float*>(ws + w.off_S());
-  float* dsum = reinterpret_cast<float*>(ws + w.off_dsum());
-  float* hstart = reinterpret_cast<float*>(ws + w.off_hstart());
-  const ProArgs none{nullptr, nullptr, nullptr, nullptr, nullptr, 1};
-  const int segs = (int)p.segments();
-  dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)segs, (unsigned)batch);
-  if (io == JSCAN_IO_BF16)
-    hipLaunchKernelGGL((k_chunk_state<uint16_t>), g1, dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(delta), A, static_cast<const uint16_t*>(B), S, dsum, L,
-                       d_inner, p.seg_len, segs, none);
-  else
-    hipLaunchKernelGGL((k_chunk_state<float>), g1, dim3(256), 0, st, static_cast<const float*>(x),
-                       static_cast<const float*>(delta), A, static_cast<const float*>(B), S, dsum, L, d_inner,
-                       p.seg_len, segs, none);
   hipError_t e;
-  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
-  dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
-  hipLaunchKernelGGL(k_combine, g2, dim3(256), 0, st, A, S, dsum, h0, hstart, d_inner, p.chunks, p.seg_per_chunk,
-                     nullptr, nullptr, 0, nullptr, Tag{});
-  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
+  const char* base = saved ? saved : rec;
+  if (!saved) {
+    const Records r = records_in(rec, w, p);
+    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)p.chunks, (unsigned)batch);
+    hipLaunchKernelGGL((k_chunk_state<T>), g1, dim3(256), 0, st, static_cast<const T*>(x),
+                       static_cast<const T*>(delta), A, static_cast<const T*>(B), h0, r, L, d_inner, p.chunk_len);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
+    if (p.chunks > 1) {
+      dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
+      hipLaunchKernelGGL((k_combine<T>), g2, dim3(256), 0, st, A, r.eS, r.eL, reinterpret_cast<float*>(rec + w.off_H()),
+                         nullptr, d_inner, p.chunks, static_cast<const T*>(x), L,
+                         ProArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 1}, nullptr, Tag{});
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
+    }
+  }
+  dim3 g3((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)p.subs, (unsigned)batch);
+  hipLaunchKernelGGL(k_substarts, g3, dim3(256), 0, st, A, reinterpret_cast<const float*>(base + w.off_sS()),
+                     reinterpret_cast<const float*>(base + w.off_sL()),
+                     reinterpret_cast<const float*>(base + w.off_H()), h0, hstart, d_inner, p.chunks, p.subs,
+                     p.chunk_len, p.sub_len);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "sub-chunk starts launch");
   return JSCAN_OK;
+}
+
+jscan_status sub_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
+                              const void* delta, const float* A, const void* B, const float* h0, char* rec,
+                              const char* saved, float* hstart, const Plan& p, hipStream_t st) {
+  if (p.subs <= 1) return JSCAN_OK;
+  return io == JSCAN_IO_BF16
+             ? sub_starts_t<uint16_t>(batch, L, d_inner, x, delta, A, B, h0, rec, saved, hstart, p, st)
+             : sub_starts_t<float>(batch, L, d_inner, x, delta, A, B, h0, rec, saved, hstart, p, st);
 }
 
 // Calls f(integral_constant<bool, CONV>, integral_constant<bool, SP>,
@@ -1049,7 +1195,7 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
   const size_t tok = (size_t)batch * (size_t)L * (size_t)d_inner * es;
   const size_t rowb = (size_t)batch * (size_t)L * NSTATE * es;
   const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
-  Plan plan = choose_plan(batch, L, d_inner);
+  const Plan plan = choose_plan(batch, L, d_inner);
   const size_t need = ws_layout(batch, L, d_inner, plan).total;
   Range in[20] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
                   {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"}};
@@ -1096,7 +1242,6 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
     return JSCAN_OK;
   }
   const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
-  if (conv || sp || tr) plan.K = 1;                        // these run with one wave per group
   const void *dl = delta, *Bs = B, *Cs = C;
   void* rms_scratch = nullptr;
   if ((s = apply_rms(pro, io, batch, L, d_inner, &dl, &Bs, &Cs, &rms_scratch, st)) != JSCAN_OK) {
@@ -1219,13 +1364,11 @@ void jscan_time_next_prefill(void* before, void* after) {
 
 jscan_status jscan_set_plan_override(int waves_per_group, int chunks) {
   if (waves_per_group == 0 && chunks == 0) {
-    t_force_K = t_force_chunks = 0;
+    t_force_chunks = 0;
     return JSCAN_OK;
   }
-  if ((waves_per_group != 1 && waves_per_group != 2 && waves_per_group != 4 && waves_per_group != 8) ||
-      chunks < 1 || chunks > 65535)
-    return fail(JSCAN_ERR_UNSUPPORTED, "waves_per_group must be 1, 2, 4 or 8 and chunks in [1, 65535]");
-  t_force_K = waves_per_group;
+  if (waves_per_group != 1 || chunks < 1 || chunks > kMaxChunks)
+    return fail(JSCAN_ERR_UNSUPPORTED, "waves_per_group must be 1 and chunks in [1, 4096]");
   t_force_chunks = chunks;
   return JSCAN_OK;
 }
@@ -1235,7 +1378,7 @@ jscan_status jscan_prefill_plan(int64_t batch, int64_t L, int64_t d_inner, int64
   if (d_state != NSTATE) return fail(JSCAN_ERR_UNSUPPORTED, "d_state must be 16");
   if (!sizes_ok(batch, L, d_inner)) return fail(JSCAN_ERR_SHAPE, "invalid sizes");
   const Plan p = choose_plan(batch, L, d_inner);
-  if (waves_per_group) *waves_per_group = p.K;
+  if (waves_per_group) *waves_per_group = 1;
   if (chunks) *chunks = p.chunks;
   return JSCAN_OK;
 }

@@ -640,18 +640,23 @@ __global__ __launch_bounds__(256) void k_copy_or_zero(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ host
+// Backward workspace: the sub-chunk starting states (the backward's chunks
+// are the plan's sub-chunks), then the records a prefill would have left
+// (written here only when they are recomputed), then the adjoint carries,
+// state checkpoints and partial sums.
 struct BwdLayout {
-  size_t fwd, M, dsum, ck, dBp, dCp, dAp, dDp, total;
+  size_t hs, fwd, M, dsum, ck, dBp, dCp, dAp, dDp, total;
 };
 
 BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   BwdLayout w{};
   if (batch <= 0 || L <= 0 || d_inner <= 0) return w;
-  const size_t B = (size_t)batch, C = (size_t)p.chunks, Dn = (size_t)d_inner;
+  const size_t B = (size_t)batch, C = (size_t)p.subs, Dn = (size_t)d_inner;
   const size_t G = (size_t)((d_inner + 63) / 64);
-  const size_t blocks = (size_t)((p.chunk_len + kTok - 1) / kTok);
+  const size_t blocks = (size_t)((p.sub_len + kTok - 1) / kTok);
   w.fwd = ws_layout(batch, L, d_inner, p).total;
-  if (p.chunks > 1) {
+  if (p.subs > 1) {
+    w.hs = round_up(B * C * NSTATE * Dn * 4);
     w.M = round_up(B * C * NSTATE * Dn * 4);
     w.dsum = round_up(B * C * Dn * 4);
   }
@@ -660,7 +665,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   w.dCp = w.dBp;
   w.dAp = round_up(B * C * NSTATE * Dn * 4);
   w.dDp = round_up(B * C * Dn * 4);
-  w.total = w.fwd + w.M + w.dsum + w.ck + w.dBp + w.dCp + w.dAp + w.dDp;
+  w.total = w.hs + w.fwd + w.M + w.dsum + w.ck + w.dBp + w.dCp + w.dAp + w.dDp;
   return w;
 }
 
@@ -669,14 +674,14 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
                           const float* A, const void* B, const void* C, const float* D, const void* z,
                           const float* h0, const void* dy, const float* dhT, void* dx, void* ddelta, void* dz,
                           float* dA, float* dB, float* dC, float* dD, float* dh0, char* ws,
-                          const float* saved_hstart, const int64_t* saved_tag, const Plan& p,
-                          hipStream_t st) {
+                          const char* saved, const Plan& p, hipStream_t st) {
   const BwdLayout w = bwd_layout(batch, L, d_inner, p);
-  const WsLayout fw = ws_layout(batch, L, d_inner, p);
-  // Chunk starting states: those a prefill left in its workspace, or
-  // recomputed into the front of this workspace.
-  const float* hstart = saved_hstart ? saved_hstart : reinterpret_cast<const float*>(ws + fw.off_hstart());
-  char* q = saved_hstart ? ws : ws + w.fwd;
+  // The sub-chunk starting states, derived from the records a prefill left
+  // in its workspace (`saved`) or from records recomputed into this one.
+  char* q = ws;
+  float* hstart = reinterpret_cast<float*>(q); q += w.hs;
+  char* rec = saved ? nullptr : q;
+  if (!saved) q += w.fwd;
   float* M = reinterpret_cast<float*>(q); q += w.M;
   float* dsum = reinterpret_cast<float*>(q); q += w.dsum;
   float* ck = reinterpret_cast<float*>(q); q += w.ck;
@@ -685,26 +690,26 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
   float* dAp = reinterpret_cast<float*>(q); q += w.dAp;
   float* dDp = reinterpret_cast<float*>(q);
   const int G = (int)((d_inner + 63) / 64);
+  const int chunks = p.subs;
   hipError_t e;
   jscan_status s;
 
-  if (p.chunks > 1) {
-    if (!saved_hstart &&
-        (s = forward_chunk_starts(io, batch, L, d_inner, x, delta, A, B, h0, ws, p, st)) != JSCAN_OK)
+  if (chunks > 1) {
+    if ((s = sub_chunk_starts(io, batch, L, d_inner, x, delta, A, B, h0, rec, saved, hstart, p, st)) != JSCAN_OK)
       return s;
-    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)(p.chunks - 1), (unsigned)batch);
+    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)(chunks - 1), (unsigned)batch);
     hipLaunchKernelGGL((k_adj_local<T>), g1, dim3(256), 0, st, static_cast<const T*>(delta), A,
                        static_cast<const T*>(C), static_cast<const T*>(z), static_cast<const T*>(dy), M, dsum, L,
-                       d_inner, p.chunk_len, p.chunks);
+                       d_inner, p.sub_len, chunks);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "adjoint chunk launch");
     dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
-    hipLaunchKernelGGL(k_adj_combine, g2, dim3(256), 0, st, A, dsum, dhT, M, d_inner, p.chunks);
+    hipLaunchKernelGGL(k_adj_combine, g2, dim3(256), 0, st, A, dsum, dhT, M, d_inner, chunks);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "adjoint combine launch");
   }
-  const BwdArgs args{x, delta, A, B, C, D, z, dy, p.chunks > 1 ? hstart : h0, M, dhT, dx, ddelta, dz, dBp, dCp,
-                     dAp, dDp, dh0, ck, L, d_inner, p.chunk_len, p.chunks,
-                     saved_hstart ? saved_tag : nullptr, make_tag(batch, L, d_inner, p, 0)};
-  dim3 g3((unsigned)G, (unsigned)p.chunks, (unsigned)batch);
+  const BwdArgs args{x, delta, A, B, C, D, z, dy, chunks > 1 ? hstart : h0, M, dhT, dx, ddelta, dz, dBp, dCp,
+                     dAp, dDp, dh0, ck, L, d_inner, p.sub_len, chunks,
+                     saved ? reinterpret_cast<const int64_t*>(saved) : nullptr, make_tag(batch, L, d_inner, p, 0)};
+  dim3 g3((unsigned)G, (unsigned)chunks, (unsigned)batch);
   hipLaunchKernelGGL((k_bwd_fwd<T>), g3, dim3(64), 0, st, args, static_cast<const T*>(B), static_cast<const T*>(C));
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "backward forward-sweep launch");
   hipLaunchKernelGGL((k_bwd_rev<T>), g3, dim3(64), 0, st, args, static_cast<const T*>(B), static_cast<const T*>(C));
@@ -713,7 +718,7 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
   hipLaunchKernelGGL(k_reduce_bc, g4, dim3(256), 0, st, dBp, dCp, dB, dC, L, G);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dB/dC reduce launch");
   hipLaunchKernelGGL(k_reduce_ad, dim3((unsigned)((d_inner * NSTATE + 255) / 256)), dim3(256), 0, st, dAp, dDp, dA,
-                     dD, d_inner, batch * (int64_t)p.chunks);
+                     dD, d_inner, batch * (int64_t)chunks);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dA/dD reduce launch");
   return JSCAN_OK;
 }
@@ -746,7 +751,7 @@ jscan_status backward_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
   const Plan plan = choose_plan(batch, L, d_inner);
   const BwdLayout bl = bwd_layout(batch, L, d_inner, plan);
   // With saved chunk states the front of the workspace (the prefill's part) is not needed.
-  const bool use_saved = saved && work && plan.chunks > 1;
+  const bool use_saved = saved && work && plan.subs > 1;
   const size_t need = use_saved ? bl.total - bl.fwd : bl.total;
   const WsLayout fl = ws_layout(batch, L, d_inner, plan);
   if (use_saved && !prefill_ws)
@@ -793,14 +798,12 @@ jscan_status backward_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
       return hip_fail(e, "hipMallocAsync(workspace)");
     owned = true;
   }
-  const char* pw = static_cast<const char*>(prefill_ws);
-  const float* saved_hstart = use_saved ? reinterpret_cast<const float*>(pw + fl.off_hstart()) : nullptr;
-  const int64_t* saved_tag = use_saved ? reinterpret_cast<const int64_t*>(pw) : nullptr;
+  const char* pw = use_saved ? static_cast<const char*>(prefill_ws) : nullptr;
   s = io == JSCAN_IO_BF16
           ? run_backward<uint16_t>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz,
-                                   dA, dB, dC, dD, dh0, ws, saved_hstart, saved_tag, plan, st)
+                                   dA, dB, dC, dD, dh0, ws, pw, plan, st)
           : run_backward<float>(batch, L, d_inner, io, x, delta, A, B, C, D, z, h0, dy, dhT, dx, ddelta, dz, dA,
-                                dB, dC, dD, dh0, ws, saved_hstart, saved_tag, plan, st);
+                                dB, dC, dD, dh0, ws, pw, plan, st);
   if (owned) {
     e = hipFreeAsync(ws, st);
     if (s == JSCAN_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");

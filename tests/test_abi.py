@@ -128,12 +128,14 @@ def test_prefill_workspace_too_small(lib):
 
 
 def test_workspace_size_formula(lib):
-    # single-pass plans need no workspace; chunked plans hold per-segment end
-    # states (16 fp32 per channel) and per-chunk start states
+    # single-pass plans need no workspace; chunked plans hold the sub-chunk
+    # records (16 fp32 states and a delta sum per channel) and per-chunk start
+    # states
     K, chunks = js.plan(1, 65536, 8192)
-    assert chunks > 1
-    assert js.workspace_size(1, 65536, 8192) >= chunks * 8192 * 16 * 4
-    assert js.workspace_size(16, 4096, 8192) == 0 or js.plan(16, 4096, 8192)[1] > 1
+    assert K == 1 and chunks > 1
+    assert js.workspace_size(1, 65536, 8192) >= 2 * chunks * 8192 * 16 * 4
+    # a chunked forward always records; a one-chunk forward records only for the backward's sub-chunks
+    assert js.plan(16, 4096, 8192)[1] == 1 or js.workspace_size(16, 4096, 8192) > 0
     assert js.workspace_size(1, 64, 128, 15) == 0
     assert js.workspace_size(-1, 64, 128) == 0
     assert js.workspace_size(0, 0, 0) == 0
@@ -146,22 +148,23 @@ def test_automatic_plan_fills_mi355x():
     # at least two waves per SIMD and a workgroup per CU for the Jamba shapes
     for batch, L in ((1, 65536), (1, 262144), (2, 4096), (8, 16384), (16, 4096)):
         K, chunks = js.plan(batch, L, 8192)
-        assert K in (1, 2, 4, 8)
+        assert K == 1
         groups = batch * 8192 // 64
-        assert groups * K * chunks >= 2048
+        assert groups * chunks >= 2048
         assert groups * chunks >= 256
     assert js.plan(1, 65536, 8192)[1] > 1            # batch 1 needs chunks
 
 
 def test_plan_override_round_trip():
     try:
-        js.set_plan_override(4, 3)
-        assert js.plan(1, 300, 64) == (4, 3)
-        js.set_plan_override(2, 1000)                 # chunks are whole 8-token blocks
-        assert js.plan(1, 10, 64) == (2, 2)
-        assert js.plan(1, 4096, 64) == (2, 512)
-        with pytest.raises(js.JscanError):
-            js.set_plan_override(3, 1)
+        js.set_plan_override(1, 3)
+        assert js.plan(1, 300, 64) == (1, 3)
+        js.set_plan_override(1, 1000)                 # chunks are whole 8-token blocks
+        assert js.plan(1, 10, 64) == (1, 2)
+        assert js.plan(1, 4096, 64) == (1, 512)
+        for bad in ((2, 4), (4, 1), (3, 1), (1, 0), (1, 4097)):
+            with pytest.raises(js.JscanError):
+                js.set_plan_override(*bad)
     finally:
         js.set_plan_override(0, 0)
 

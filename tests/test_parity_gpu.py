@@ -45,15 +45,16 @@ def print_case(msg):
 
 
 # ------------------------------------------------------------ small, every output
-@pytest.mark.parametrize("K,chunks", [(1, 1), (2, 1), (4, 1), (8, 1), (1, 3), (2, 5), (4, 2), (8, 7)])
-def test_tiny_f32_all_plans(K, chunks):
-    """Tiny fp32 prefill (batch 1, L 256, d_inner 64, h0 = 0) in every kernel variant."""
-    print_case(f"tiny f32 K={K} chunks={chunks}")
+@pytest.mark.parametrize("chunks", [1, 2, 3, 5, 7, 11, 32])
+def test_tiny_f32_all_plans(chunks):
+    """Tiny fp32 prefill (batch 1, L 256, d_inner 64, h0 = 0) in one sweep and
+    in chunked plans (pass 1, combine, pass 2)."""
+    print_case(f"tiny f32 chunks={chunks}")
     inp = synth.prefill_inputs(1, 256, 64, seed=0, io=synth.IO_F32)
     t = to_device(inp)
     yr, hr = oracle_full(inp)
     try:
-        js.set_plan_override(K, chunks)
+        js.set_plan_override(1, chunks)
         y, hT = run_prefill(t)
     finally:
         js.set_plan_override(0, 0)
@@ -61,16 +62,16 @@ def test_tiny_f32_all_plans(K, chunks):
     assert_state(hT, hr, "hT")
 
 
-@pytest.mark.parametrize("K,chunks", [(1, 1), (2, 4), (4, 1), (8, 3), (1, 9)])
-def test_ragged_bf16_with_h0(K, chunks):
+@pytest.mark.parametrize("chunks", [1, 2, 4, 9, 16])
+def test_ragged_bf16_with_h0(chunks):
     """Ragged sizes: L not a multiple of the token block or the chunk, d_inner
     not a multiple of 64, non-zero h0, two sequences."""
-    print_case(f"ragged bf16 K={K} chunks={chunks}")
+    print_case(f"ragged bf16 chunks={chunks}")
     inp = synth.prefill_inputs(2, 777, 200, seed=5, io=synth.IO_BF16, h0=True)
     t = to_device(inp)
     yr, hr = oracle_full(inp)
     try:
-        js.set_plan_override(K, chunks)
+        js.set_plan_override(1, chunks)
         y, hT = run_prefill(t)
     finally:
         js.set_plan_override(0, 0)
@@ -293,14 +294,14 @@ def bookkeeping_inputs(batch, L, d_inner, case):
                 B=onehot, C=onehot.clone(), D=D, z=z, h0=torch.randn(batch, d_inner, 16, device=DEV))
 
 
-@pytest.mark.parametrize("K,chunks", [(1, 1), (8, 1), (2, 6), (1, 17)])
+@pytest.mark.parametrize("chunks", [1, 2, 6, 17])
 @pytest.mark.parametrize("case", ["hold", "read", "pass"])
-def test_bookkeeping_bit_exact(case, K, chunks):
-    print_case(f"bookkeeping {case} K={K} chunks={chunks}")
+def test_bookkeeping_bit_exact(case, chunks):
+    print_case(f"bookkeeping {case} chunks={chunks}")
     batch, L, d_inner = 3, 1111, 320
     t = bookkeeping_inputs(batch, L, d_inner, case)
     try:
-        js.set_plan_override(K, chunks)
+        js.set_plan_override(1, chunks)
         y, hT = run_prefill(t)
     finally:
         js.set_plan_override(0, 0)
@@ -460,15 +461,15 @@ def _random_cases(n, seed):
         cases.append(dict(batch=int(rng.integers(1, 4)), L=int(rng.integers(1, 1500)),
                           d=int(rng.choice([1, 7, 64, 65, 128, 200, 257, 512])),
                           io=synth.IO_BF16 if rng.random() < 0.7 else synth.IO_F32, h0=bool(rng.random() < 0.6),
-                          K=int(rng.choice([1, 1, 1, 2, 4, 8])), chunks=int(rng.choice([0, 1, 2, 3, 5, 8, 16, 33])),
+                          chunks=int(rng.choice([0, 1, 2, 3, 5, 8, 16, 33])),
                           seed=1000 + i))
     return cases
 
 
-@pytest.mark.parametrize("case", _random_cases(40, 2024), ids=lambda c: "b{batch}L{L}d{d}io{io}K{K}c{chunks}".format(**c))
+@pytest.mark.parametrize("case", _random_cases(40, 2024), ids=lambda c: "b{batch}L{L}d{d}io{io}c{chunks}".format(**c))
 def test_random_shapes_and_plans(case):
     """Seeded random sizes (batch 1-3, L 1-1499, d_inner from 1 to 512), I/O
-    dtype, h0 or not, waves per group and chunk count (0: the automatic plan),
+    dtype, h0 or not and chunk count (0: the automatic plan),
     every output against the oracle."""
     c = case
     print_case(f"random {c}")
@@ -477,7 +478,7 @@ def test_random_shapes_and_plans(case):
     yr, hr = oracle_full(inp, use_h0=c["h0"])
     try:
         if c["chunks"]:
-            js.set_plan_override(c["K"], c["chunks"])
+            js.set_plan_override(1, c["chunks"])
         y, hT = run_prefill(t, h0=c["h0"])
     finally:
         js.set_plan_override(0, 0)

@@ -116,14 +116,14 @@ def test_prefill_fused_in_place_conv_state(chunks):
     assert np.array_equal(host64(so), sr)
 
 
-def test_prefill_fused_override_of_waves_is_ignored():
-    """A plan override with several waves per group still runs the fused path
-    with one (and gives the same result as the automatic plan's K)."""
-    print_case("fused with K=4 override")
+def test_prefill_fused_many_short_chunks():
+    """Chunks of 8 tokens (every chunk but the first rescanned from its true
+    start by pass 2, the conv history of each chunk read from x)."""
+    print_case("fused with 38 chunks of 8 tokens")
     inp, pro = problem(1, 300, 96, 4, seed=14, io=synth.IO_BF16)
     t = to_device(inp)
     yr, hr, sr = oracle_fused(inp, pro, 4, True)
-    y, hT, so = with_plan(4, 3, lambda: gpu_fused(t, pro, 4, True))
+    y, hT, so = with_plan(1, 38, lambda: gpu_fused(t, pro, 4, True))
     assert_y(y, yr, bf16=True)
     assert_state(hT, hr, "hT")
     assert np.array_equal(host64(so), sr)
