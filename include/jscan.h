@@ -99,6 +99,31 @@ jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
                            void* stream);
 
 /*
+ * jscan_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as jscan_prefill without a workspace; the
+ * chunked plan's records (per sequence, forward chunk and channel: 16 fp32
+ * end states, a delta sum, a flag and 16 fp32 starting states, 136 bytes,
+ * plus a 256-byte tag, each region rounded up to 256 bytes) live in a scratch
+ * array of 64 MiB that the library holds on each GPU it runs on until the
+ * process ends: batch * chunks * d_inner up to about 493 000 (at batch 1 and
+ * d_inner 8192, plans of up to 60 chunks; the automatic plan there takes 32;
+ * a one-chunk plan needs no records at all).  A larger problem returns
+ * JSCAN_ERR_WORKSPACE before any GPU work, and jscan_last_error names the
+ * bytes it needs.
+ * The call allocates nothing (no hipMalloc, no stream-ordered allocation);
+ * its first call on a device looks up the array's device address.  Every
+ * call on one GPU shares the array: calls that overlap in time on one GPU
+ * (on different streams) race and give wrong results.  Nothing in the array
+ * needs to start at zero.  A prefill workspace written here cannot be passed
+ * to jscan_backward_saved (it holds no sub-chunk records).
+ */
+jscan_status jscan_prefill_noalloc(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                   const void* x, const void* delta, const float* A, const void* B,
+                                   const void* C, const float* D, const void* z, const float* h0, void* y,
+                                   float* hT, void* stream);
+
+/*
  * Decode step for one sequence: one token, state updated in place.
  *
  *   state : [d_inner][d_state] fp32, read and overwritten with the new state

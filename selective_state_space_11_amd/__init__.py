@@ -9,6 +9,8 @@ raises ``JscanUnavailable`` -- there is no fallback implementation.
 Entry points mirror the C ABI in ``include/jscan.h``:
 
 * ``prefill(x, delta, A, B, C, D, z, h0=None)`` -> ``(y, hT)``
+* ``prefill_noalloc(x, delta, A, B, C, D, z, h0=None, y=..., hT=...)``: the
+  same through jscan_prefill_noalloc (no allocation anywhere)
 * ``step(state, x, delta, A, B, C, D, z)`` -> ``y`` (state updated in place)
 * ``step_batch(state, x, delta, A, B, C, D, z)`` -> ``y`` (states updated in place)
 * ``prefill_fused`` / ``step_batch_fused``: the same with the layer's input
@@ -38,7 +40,7 @@ STATUS_NAMES = {0: "JSCAN_OK", 1: "JSCAN_ERR_NULL", 2: "JSCAN_ERR_SHAPE", 3: "JS
                 4: "JSCAN_ERR_ALIGN", 5: "JSCAN_ERR_ALIAS", 6: "JSCAN_ERR_WORKSPACE", 7: "JSCAN_ERR_HIP"}
 IO_F32, IO_BF16 = 0, 1
 
-EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_step", "jscan_step_batch",
+EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_prefill_noalloc", "jscan_step", "jscan_step_batch",
            "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
            "jscan_set_plan_override", "jscan_time_next_prefill", "jscan_prefill_fused",
            "jscan_step_batch_fused", "jscan_backward_workspace_size", "jscan_backward", "jscan_prefill_trap",
@@ -91,6 +93,8 @@ def load_library(path: str = LIB_PATH):
         lib.jscan_prefill_workspace_size.restype = sz
         lib.jscan_prefill.argtypes = [i64, i64, i64, i64, st, vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, vp, sz, vp]
         lib.jscan_prefill.restype = st
+        lib.jscan_prefill_noalloc.argtypes = [i64, i64, i64, i64, st, vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, vp]
+        lib.jscan_prefill_noalloc.restype = st
         lib.jscan_step.argtypes = [i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, vp]
         lib.jscan_step.restype = st
         lib.jscan_step_batch.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, vp]
@@ -227,6 +231,30 @@ def prefill(x, delta, A, B, C, D, z, h0=None, *, y=None, hT=None, want_state=Tru
     _check(lib.jscan_prefill(batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
                              _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), _ptr(workspace),
                              ws_bytes, _stream(stream)))
+    return y, hT
+
+
+def prefill_noalloc(x, delta, A, B, C, D, z, h0=None, *, y, hT=None, stream=None):
+    """jscan_prefill_noalloc: the prefill with its chunk records in the
+    library's own per-GPU scratch array, for callers that cannot allocate.
+    The caller passes every output buffer (y, and hT or None); nothing is
+    allocated here either."""
+    torch = _torch()
+    lib = load_library()
+    _dev(x, "x")
+    batch, L, d_inner = x.shape
+    io = _io_of(x)
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(z, "z", x.dtype, x.shape)
+    _dev(B, "B", x.dtype, (batch, L, D_STATE))
+    _dev(C, "C", x.dtype, (batch, L, D_STATE))
+    _dev(A, "A", torch.float32, (d_inner, D_STATE))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, D_STATE))
+    _dev(y, "y", x.dtype, x.shape)
+    _dev(hT, "hT", torch.float32, (batch, d_inner, D_STATE))
+    _check(lib.jscan_prefill_noalloc(batch, L, d_inner, D_STATE, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream)))
     return y, hT
 
 

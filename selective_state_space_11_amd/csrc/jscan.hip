@@ -48,6 +48,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1176,11 +1177,40 @@ jscan_status check_trap(const jscan_trap* tr, bool rms, int64_t nseq, int64_t L,
   return JSCAN_OK;
 }
 
+// ------------------------------------------------ allocation-free prefill
+// jscan_prefill_noalloc keeps its chunk records in this array instead of a
+// caller workspace: one copy per GPU, alive until the process ends.  Host code
+// never passes `scratch` itself to a kernel (on the host the name is only a
+// stand-in); it passes the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+jscan_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(JSCAN_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return JSCAN_OK;
+}
+
 jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
                           const void* x, const void* delta, const float* A, const void* B, const void* C,
                           const float* D, const void* z, const float* h0, void* y, float* hT,
                           const jscan_prologue* pro, const jscan_trap* trap, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, bool noalloc = false) {
   t_last_error.clear();
   jscan_status s = check_common(d_state, io);
   if (s != JSCAN_OK) return s;
@@ -1195,8 +1225,15 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
   const size_t tok = (size_t)batch * (size_t)L * (size_t)d_inner * es;
   const size_t rowb = (size_t)batch * (size_t)L * NSTATE * es;
   const size_t stb = (size_t)batch * (size_t)d_inner * NSTATE * 4;
-  const Plan plan = choose_plan(batch, L, d_inner);
+  Plan plan = choose_plan(batch, L, d_inner);
+  if (noalloc) {                 // no sub-chunk records for a backward: the forward's chunks only
+    plan.subs = 1;
+    plan.sub_len = std::max<int64_t>(L, 1);
+  }
   const size_t need = ws_layout(batch, L, d_inner, plan).total;
+  if (noalloc && need > kScratchBytes)
+    return fail(JSCAN_ERR_WORKSPACE, "jscan_prefill_noalloc: this problem needs " + std::to_string(need) +
+                                         " bytes of scratch, more than its " + std::to_string(kScratchBytes));
   Range in[20] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
                   {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"}};
   Range out[4] = {{y, tok, "y"}, {hT, stb, "hT"}, {workspace, workspace ? need : 0, "workspace"}};
@@ -1242,6 +1279,7 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
     return JSCAN_OK;
   }
   const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
+  if (noalloc && need > 0 && (s = scratch_address(&workspace)) != JSCAN_OK) return s;
   const void *dl = delta, *Bs = B, *Cs = C;
   void* rms_scratch = nullptr;
   if ((s = apply_rms(pro, io, batch, L, d_inner, &dl, &Bs, &Cs, &rms_scratch, st)) != JSCAN_OK) {
@@ -1397,6 +1435,14 @@ jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
                            void* stream) {
   return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, nullptr, nullptr,
                       workspace, workspace_bytes, stream);
+}
+
+jscan_status jscan_prefill_noalloc(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,
+                                   const void* x, const void* delta, const float* A, const void* B,
+                                   const void* C, const float* D, const void* z, const float* h0, void* y,
+                                   float* hT, void* stream) {
+  return prefill_impl(batch, L, d_inner, d_state, io, x, delta, A, B, C, D, z, h0, y, hT, nullptr, nullptr,
+                      nullptr, 0, stream, true);
 }
 
 jscan_status jscan_prefill_fused(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,

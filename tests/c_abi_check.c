@@ -22,6 +22,7 @@ int main(void) {
   typedef void (*fn)(void);
   const fn entry[] = {
       (fn)&jscan_prefill_workspace_size, (fn)&jscan_prefill,          (fn)&jscan_step,
+      (fn)&jscan_prefill_noalloc,
       (fn)&jscan_step_batch,             (fn)&jscan_prefill_fused,    (fn)&jscan_step_batch_fused,
       (fn)&jscan_prefill_trap,           (fn)&jscan_step_batch_trap,  (fn)&jscan_backward_workspace_size,
       (fn)&jscan_backward,               (fn)&jscan_backward_saved,   (fn)&jscan_status_string,

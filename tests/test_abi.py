@@ -120,6 +120,39 @@ def test_prefill_aliasing(lib):
     assert "overlaps" in lib.jscan_last_error().decode()
 
 
+def call_noalloc(lib, a):
+    return lib.jscan_prefill_noalloc(a["batch"], a["L"], a["d_inner"], a["d_state"], a["io"], a["x"],
+                                     a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["y"],
+                                     a["hT"], a["stream"])
+
+
+def test_noalloc_validates_like_prefill(lib):
+    """jscan_prefill_noalloc rejects what jscan_prefill rejects, before any HIP call."""
+    assert call_noalloc(lib, prefill_args(x=None)) == NULL
+    assert call_noalloc(lib, prefill_args(L=-1)) == SHAPE
+    assert call_noalloc(lib, prefill_args(d_state=8)) == UNSUP
+    assert call_noalloc(lib, prefill_args(y=fake(0))) == ALIAS
+    assert call_noalloc(lib, prefill_args(batch=0)) == OK
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """The scratch holds 64 MiB of chunk records: 136 bytes per (sequence,
+    chunk, channel).  Batch 8 x 16K at 1024 chunks needs far more; the
+    automatic plan at batch 1 x 64K (32 chunks) fits."""
+    try:
+        js.set_plan_override(1, 1024)
+        assert call_noalloc(lib, prefill_args(batch=8, L=16384, d_inner=8192)) == WS
+        msg = lib.jscan_last_error().decode()
+        assert "needs" in msg and str(64 << 20) in msg
+        js.set_plan_override(1, 60)
+        assert 60 * 8192 * 136 <= (64 << 20)
+        js.set_plan_override(1, 61)
+        assert call_noalloc(lib, prefill_args(batch=1, L=65536, d_inner=8192)) == WS
+    finally:
+        js.set_plan_override(0, 0)
+    assert js.plan(1, 65536, 8192)[1] * 8192 * 136 + 5 * 256 <= (64 << 20)
+
+
 def test_prefill_workspace_too_small(lib):
     L, d = 65536, 8192
     ws = js.workspace_size(1, L, d)
