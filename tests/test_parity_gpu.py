@@ -183,6 +183,50 @@ def test_degenerate_parameters(case, chunks):
     assert_state(hT, hr, "hT")
 
 
+def _decay_case(case, inp):
+    """Inputs under which the carried-in part of a chunk's starting state
+    does not decay below fp32 resolution within the chunk, so pass 2 must
+    rescan whole chunks: very slow decay, no decay, growth, and chunks with
+    negative time steps (whose decay factor exceeds 1 there)."""
+    rng = np.random.default_rng({"slow": 81, "zero": 82, "grow": 83, "negdt": 84}[case])
+    d_inner = inp["A"].shape[0]
+    if case == "slow":          # A in [-0.02, -0.005], delta scaled to ~0.01
+        inp["A"] = -rng.uniform(0.005, 0.02, size=(d_inner, 16)).astype(np.float32)
+        inp["delta"] = synth.to_bf16_bits(synth.widen(inp["delta"]) * 0.05)
+    elif case == "zero":
+        inp["A"] = np.zeros((d_inner, 16), np.float32)
+    elif case == "grow":        # A in [0, 0.01]: growth up to exp(0.01 * sum delta)
+        inp["A"] = rng.uniform(0.0, 0.01, size=(d_inner, 16)).astype(np.float32)
+    else:                       # a band of delta = -0.02 in the middle of every 300 tokens
+        dl = synth.widen(inp["delta"])
+        L = dl.shape[1]
+        for t0 in range(150, L, 300):
+            dl[:, t0:t0 + 20, :] = -0.02
+        inp["delta"] = synth.to_bf16_bits(dl)
+    return inp
+
+
+@pytest.mark.parametrize("chunks", [0, 9])
+@pytest.mark.parametrize("case", ["slow", "zero", "grow", "negdt"])
+def test_carry_that_does_not_settle(case, chunks):
+    """Pass 2 falls back to rescanning whole chunks when the carried-in state
+    cannot settle: every output against the oracle (batch 2 x 3000 x 200,
+    bf16, h0), in the automatic plan (0) and a forced 9-chunk plan."""
+    print_case(f"unsettled carry {case} chunks={chunks}")
+    inp = _decay_case(case, synth.prefill_inputs(2, 3000, 200, seed=80, io=synth.IO_BF16, h0=True))
+    t = to_device(inp)
+    yr, hr = oracle_full(inp)
+    try:
+        if chunks:
+            js.set_plan_override(1, chunks)
+        assert js.plan(2, 3000, 200)[1] > 1
+        y, hT = run_prefill(t)
+    finally:
+        js.set_plan_override(0, 0)
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+
+
 def test_nan_stays_in_its_channel():
     print_case("nan locality")
     inp = synth.prefill_inputs(2, 300, 256, seed=11, io=synth.IO_BF16, h0=True)
@@ -201,6 +245,44 @@ def test_nan_stays_in_its_channel():
 
 
 # ------------------------------------------------------------- decode step
+def test_decode_1024_steps_sampled():
+    """The decode workload as written: 256 sequences x 8192 channels, 1024
+    chained step_batch calls with each step's own seeded inputs, state in
+    place.  The oracle follows 64 sampled channels of all 256 sequences
+    through every step; y is compared at every 64th step and the state after
+    the last."""
+    import concurrent.futures as cf
+    n_seq, d_inner, steps = 256, 8192, 1024
+    chans = sampled_channels(d_inner, k=64, seed=3)
+    ci = torch.as_tensor(chans, device=DEV)
+    state_np = synth.decode_state(n_seq, d_inner, seed=3)
+    A, D, _ = synth.params(d_inner, seed=3)
+    state = dev_f32(state_np)
+    ref = state_np[:, chans].astype(np.float64)
+    A64, D64 = A[chans].astype(np.float64), D[chans].astype(np.float64)
+    Ad, Dd = dev_f32(A), dev_f32(D)
+    y = torch.empty(n_seq, d_inner, dtype=torch.bfloat16, device=DEV)
+    gen = lambda k: synth.decode_inputs(n_seq, d_inner, seed=3, step=k)
+    with cf.ThreadPoolExecutor(16) as ex:
+        ahead = 24
+        futs = {k: ex.submit(gen, k) for k in range(min(ahead, steps))}
+        for k in range(steps):
+            inp = futs.pop(k).result()
+            if k + ahead < steps:
+                futs[k + ahead] = ex.submit(gen, k + ahead)
+            t = {n: dev_io(inp[n]) for n in ("x", "delta", "z", "B", "C")}
+            js.step_batch(state, t["x"], t["delta"], Ad, t["B"], t["C"], Dd, t["z"], y=y)
+            sub = {n: synth.widen(inp[n][:, chans]) for n in ("x", "delta", "z")}
+            yr, ref = oracle.step(ref, sub["x"], sub["delta"], A64, synth.widen(inp["B"]), synth.widen(inp["C"]),
+                                  D64, sub["z"])
+            if k % 64 == 63 or k == 0:
+                print_case(f"decode step {k} of {steps}")
+                torch.cuda.synchronize()
+                assert_y(y.index_select(1, ci), yr, bf16=True, what=f"y at step {k} (sampled channels)")
+    torch.cuda.synchronize()
+    assert_state(state.index_select(1, ci), ref, "state after 1024 steps (sampled channels)")
+
+
 def test_decode_step_batch_matches_oracle_steps():
     """256 sequences x 8192 channels (128 MiB fp32 state), several steps, every
     output and the whole state after each step against the oracle's step."""
@@ -436,13 +518,17 @@ def test_long_context_256k_single_vs_chunked_calls():
     assert_state(state, host64(hT), "hT chunked vs single")
 
 
-def test_hybrid_block_layer_sampled():
-    """One of the seven Mamba layers of a 1:7 block: batch 8, L 16384."""
-    print_case("hybrid block layer sampled")
-    inp = synth.prefill_inputs(8, 16384, 8192, seed=40, io=synth.IO_BF16)
+@pytest.mark.parametrize("layer", range(7))
+def test_hybrid_block_layer_sampled(layer):
+    """The seven Mamba layers of a 1:7 block, each an independent call with
+    its own A, D and inputs (seeds 40..46): batch 8, L 16384, d_inner 8192,
+    in the automatic plan, 16 sampled channels of every sequence over every
+    token against the oracle."""
+    print_case(f"hybrid block layer {layer} sampled")
+    inp = synth.prefill_inputs(8, 16384, 8192, seed=40 + layer, io=synth.IO_BF16, threads=16)
     t = to_device(inp)
     y, hT = run_prefill(t, h0=False)
-    check_sampled(inp, y, hT, sampled_channels(8192, k=16, seed=40))
+    check_sampled(inp, y, hT, sampled_channels(8192, k=16, seed=40 + layer))
 
 
 @pytest.mark.parametrize("case", ["pass"])
