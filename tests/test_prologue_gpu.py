@@ -286,9 +286,8 @@ def rms_case(inp, pro, seed, which=(True, True, True), width=4, softplus=True):
     w_dt, w_B, w_C = synth.rms_weights(inp["x"].shape[2], seed=seed)
     ws = tuple(w if k else None for w, k in zip((w_dt, w_B, w_C), which))
     o = oracle_inputs(inp)
-    # the normalised values are stored in the I/O dtype before the scan reads them
-    rnd = "bf16" if inp["x"].dtype == np.uint16 else "f32"
-    dn, Bn, Cn = oracle.rmsnorm_inputs(o["delta"], o["B"], o["C"], *ws, eps=EPS, round_to=rnd)
+    # the plain definition in fp64: nothing is rounded between the normalisation and the scan
+    dn, Bn, Cn = oracle.rmsnorm_inputs(o["delta"], o["B"], o["C"], *ws, eps=EPS)
     xc, dt, st = oracle.prologue(o["x"], dn, pro["conv_weight"] if width else None,
                                  pro["conv_bias"] if width else None, pro["conv_state"] if width else None,
                                  pro["dt_bias"] if softplus else None, softplus)
@@ -366,8 +365,7 @@ def test_step_rmsnorm_matches_oracle():
         s = synth.decode_inputs(n_seq, d, seed=62, step=k)
         s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=200 + k)[:, 0, :]
         dn, Bn, Cn = oracle.rmsnorm_inputs(synth.widen(s["delta"])[:, None, :], synth.widen(s["B"])[:, None, :],
-                                           synth.widen(s["C"])[:, None, :], w_dt, w_B, w_C, eps=EPS,
-                                           round_to="bf16")
+                                           synth.widen(s["C"])[:, None, :], w_dt, w_B, w_C, eps=EPS)
         xc, dt, cs64 = oracle.prologue(synth.widen(s["x"])[:, None, :], dn, pro["conv_weight"], pro["conv_bias"],
                                        cs64, pro["dt_bias"], True)
         yr, st64 = oracle.step(st64, xc[:, 0], dt[:, 0], A.astype(np.float64), Bn[:, 0], Cn[:, 0],
