@@ -103,8 +103,9 @@ jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
  * HIP graph capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments and results as jscan_prefill without a workspace; the
  * chunked plan's records (per sequence, forward chunk and channel: 16 fp32
- * end states, a delta sum, a flag and 16 fp32 starting states, 136 bytes,
- * plus a 256-byte tag, each region rounded up to 256 bytes) live in a scratch
+ * end states, a delta sum, a flag and 16 fp32 starting states, 136 bytes;
+ * per sequence, chunk and 64-channel group a 4-byte token index; a 256-byte
+ * tag; each region rounded up to 256 bytes) live in a scratch
  * array of 64 MiB that the library holds on each GPU it runs on until the
  * process ends: batch * chunks * d_inner up to about 493 000 (at batch 1 and
  * d_inner 8192, plans of up to 60 chunks; the automatic plan there takes 32;

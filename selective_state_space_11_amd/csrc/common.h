@@ -60,6 +60,15 @@ struct ProArgs {
   const void* lam = nullptr;
   const void* x_prev = nullptr;
   const void* B_prev = nullptr;
+  // RMSNorm of the inputs, prepared per token by k_rms_prep in fp32: the
+  // inverse root-mean-square of the time step over its channels [nseq][L]
+  // (1 when the time step is not normalised), the time step's weight per
+  // channel [d_inner] (null: 1), and the normalised B and C rows
+  // [nseq][L][16].  The scan reads delta * w[d] * s[t] and these rows.
+  const float* rms_s = nullptr;
+  const float* rms_w = nullptr;
+  const float* rms_B = nullptr;
+  const float* rms_C = nullptr;
 };
 
 template <bool CONV, bool SP>

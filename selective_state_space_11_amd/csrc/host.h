@@ -57,21 +57,27 @@ Plan choose_plan(int64_t batch, int64_t L, int64_t d_inner);
 double wave_efficiency(double waves);
 
 size_t round_up(size_t v);
+// Workgroups of 256 for a grid-stride pass over n elements (capped).
+unsigned copy_grid(int64_t n);
+// Bytes of the RMSNorm region of a prefill workspace for `rows` token rows.
+size_t rms_bytes(int64_t rows);
 // Workspace of a recording prefill, in this order: a tag (first, so that its
 // place does not depend on the plan), each forward chunk's end record (its
 // chunk-local end state [b][chunks][16][d] and delta sum [b][chunks][d]), a
-// per-(chunk, channel) flag of negative time steps, the true starting states
+// per-(chunk, channel) flag of negative time steps, per (chunk, 64-channel
+// group) the first token pass 1 wrote y for, the true starting states
 // of the forward chunks [b][chunks][16][d] (chunk 0: unused), and the
 // sub-chunk records (chunk-local state at the end of sub-chunk s
 // [b][subs][16][d] and the delta sum from its chunk's start [b][subs][d];
 // the last sub-chunk has none).  The fields are region sizes; the off_*
 // functions give byte offsets.
 struct WsLayout {
-  size_t tag, eS, eL, neg, H, sS, sL, total;
+  size_t tag, eS, eL, neg, from, H, sS, sL, total;
   size_t off_eS() const { return tag; }
   size_t off_eL() const { return off_eS() + eS; }
   size_t off_neg() const { return off_eL() + eL; }
-  size_t off_H() const { return off_neg() + neg; }
+  size_t off_from() const { return off_neg() + neg; }
+  size_t off_H() const { return off_from() + from; }
   size_t off_sS() const { return off_H() + H; }
   size_t off_sL() const { return off_sS() + sS; }
 };

@@ -74,12 +74,11 @@ constexpr float kSettled = 0x1p-24f;
 // lane has 512 VGPRs in granules of 8, so 4 waves allow 128.  The bf16
 // trapezoidal scan needs 129 without a bound (3 waves); held to 4 waves it
 // fits 121 without spilling VGPRs and runs its 64K prefill about 6% faster.
-// In the chunked passes the bound spills, so they have none.
-template <class T, bool CONV, bool SP, bool TR, int MODE>
+template <class T, bool CONV, bool SP, bool TR, bool RMS, int MODE>
 constexpr int scan_waves() { return sizeof(T) == 2 && TR && MODE == kWhole ? 4 : 1; }
 
-__device__ __forceinline__ uint32_t raw_bits(uint16_t v) { return v; }
-__device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v); }
+// One float from a wave-uniform address, as a scalar load.
+__device__ __forceinline__ float load_uniform(const float* p) { return __uint_as_float(*uniform_ptr<uint32_t>(p)); }
 
 __device__ __forceinline__ void load_a2(float (&a2)[NSTATE], const float* A, int64_t d) {
   const float4* Ap = reinterpret_cast<const float4*>(A + d * NSTATE);
@@ -320,9 +319,10 @@ struct ScanAux {
   float* hT;              // kWhole
   Records rec;            // kLocal: chunk-end and sub-chunk records
   int32_t* neg;           // kLocal writes, kFix reads: a negative time step in [b][chunk][d]
+  int32_t* from;          // kLocal writes, kFix reads: first token pass 1 wrote y for, [b][chunk][group]
   const float* H;         // kFix: chunk starting states [b][chunk][n][d]
   int64_t L, d_inner, chunk_len;
-  int chunks;
+  int chunks, groups;
 };
 
 // Grid: (ceil(d_inner / 64), chunks (kFix: chunks - 1), batch); one wave per
@@ -335,12 +335,14 @@ struct ScanAux {
 // 0 * x * B = 0 for finite x and B) and their output equals the last token's,
 // which they store again to the same address.  Every block therefore runs the
 // same branch-free code.
-template <class T, bool CONV, bool SP, bool TR, int MODE>
-__global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_scan(
+template <class T, bool CONV, bool SP, bool TR, bool RMS, int MODE>
+__global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) void k_scan(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dw, const T* __restrict__ z,
     T* __restrict__ y, ScanAux aux, ProArgs pa) {
   static_assert(!(CONV && TR), "the trapezoidal form takes no outer convolution");
+  static_assert(!(RMS && TR), "the trapezoidal form takes no RMSNorm");
+  using RT = std::conditional_t<RMS, float, T>;     // B and C rows: fp32 after RMSNorm
   const int lane = threadIdx.x;
   const int64_t L = aux.L, d_inner = aux.d_inner;
   const int64_t gbase = (int64_t)blockIdx.x * 64;
@@ -349,15 +351,28 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
   const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
   const int64_t d = gbase + lo;
 
-  float a2[NSTATE], h[NSTATE], dd[MODE == kFix ? NSTATE : 1];
+  float a2[NSTATE], h[NSTATE], hs[MODE == kFix ? NSTATE : 1];
   load_a2(a2, A, d);
   bool can_exit = true;
+  // kLocal: chunk 0 (from the true h0) writes all its y; a later chunk starts
+  // writing y at the block after which sum delta >= settle_sum in every lane
+  bool emit = MODE != kLocal || blockIdx.y == 0;
+  int emit_from = 0;
+  double settle_sum = 0.0;
+  if constexpr (MODE == kLocal) {
+    float a2max = a2[0];
+#pragma unroll
+    for (int n = 1; n < NSTATE; ++n) a2max = fmaxf(a2max, a2[n]);
+    settle_sum = a2max < 0.0f ? 24.0 / -(double)a2max : __builtin_inf();
+  }
+  // kFix: the first token from which pass 1 wrote y for this wave's channels
+  const int fix_from = MODE == kFix ? aux.from[(b * aux.chunks + (int64_t)blockIdx.y + 1) * aux.groups + blockIdx.x] : 0;
   if constexpr (MODE == kFix) {
     const float* hi = aux.H + ((b * aux.chunks + c) * NSTATE) * d_inner + d;
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) {
       h[n] = hi[(int64_t)n * d_inner];
-      dd[n] = h[n];
+      hs[n] = h[n];
       can_exit = can_exit && a2[n] <= 0.0f;
     }
     can_exit = can_exit && aux.neg[(b * aux.chunks + c) * d_inner + d] == 0;
@@ -375,8 +390,24 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
   const T* drow = delta + row0;
   const T* zrow = z + row0;
   T* yrow = y + row0;
-  const T* brow = Bm + (b * L + t0) * NSTATE;
-  const T* crow = Cm + (b * L + t0) * NSTATE;
+  const RT* brow;
+  const RT* crow;
+  if constexpr (RMS) {
+    brow = pa.rms_B + (b * L + t0) * NSTATE;
+    crow = pa.rms_C + (b * L + t0) * NSTATE;
+  } else {
+    brow = Bm + (b * L + t0) * NSTATE;
+    crow = Cm + (b * L + t0) * NSTATE;
+  }
+  // RMSNorm: delta * w[d] * s[t], s read a token ahead like the B row
+  const float* srow = RMS ? pa.rms_s + b * L + t0 : nullptr;
+  const float wdt = RMS && pa.rms_w ? pa.rms_w[d] : 1.0f;
+  float s_cur = 1.0f, s_next = 1.0f;
+  auto raw_dt = [&](T v) {
+    float r = widen(v);
+    if constexpr (RMS) r = r * wdt * s_cur;
+    return r;
+  };
 
   const uint32_t lb = (uint32_t)lo * sizeof(T);      // lane byte offset within a row
   const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
@@ -397,7 +428,7 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
   // sequence's end), and for the block's C_t . B_t products lane l's pair of
   // states 2 (l & 7) + {0, 1} of token bb + (l >> 3), B and C.
   auto load_block = [&](int bb, T (&dq)[kTok], T (&xx)[kTok], T (&zz)[kTok], T (&ll)[kTok], T& dn, T& ln,
-                        Pair<T>& pb, Pair<T>& pc) {
+                        Pair<T>& pb, Pair<T>& pc) __attribute__((always_inline)) {
     const int64_t o = (int64_t)bb * d_inner;
     const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), r0 = rsrc(drow, 0);
     const auto rl = TR && pa.lam ? rsrc(lrow + o) : r0;
@@ -422,9 +453,10 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
 
   // B of the next token is prefetched a token ahead; C is needed only after
   // the token's state updates, so it is loaded at the token's start.
-  Row<T, NSTATE> Bc, Bn, Cv;
+  Row<RT, NSTATE> Bc, Bn, Cv;
   double dacc = 0.0;                 // kLocal: delta sum since the chunk start
-  uint32_t negbits = 0;              // kLocal: OR of the raw time steps (sign bit)
+  float fsum = 0.0f;                 // kFix: delta sum since the chunk start
+  uint32_t negbits = 0;              // kLocal: OR of the time steps' bits (sign bit)
   // y of token bb + j (padding tokens map onto the last token's address and
   // store the identical value again).  With a convolution, a padding token's
   // input differs (its history has shifted), so only real tokens store.
@@ -433,8 +465,13 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
     if (!CONV || bb + j < nt) buf_store(to_io(fmaf(Dd, xv, acc) * silu(zv), T()), ry, lb, so);
   };
   // Returns true (kFix) once the carried part has settled in every lane.
-  auto do_block = [&](int bb, const T (&dq)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
-                      const T (&ll)[kTok], const T& dn, const T& ln, const Pair<T>& pb, const Pair<T>& pc) {
+  // EMIT: the block computes and stores y; without it (pass 1 before the
+  // predicted settle point of a chunk c >= 1, whose y pass 2 writes) only the
+  // state is advanced.
+  auto do_block = [&](auto emit_tag, int bb, const T (&dq)[kTok], const T (&xx)[kTok], const T (&zz)[kTok],
+                      const T (&ll)[kTok], const T& dn, const T& ln, const Pair<T>& pb, const Pair<T>& pc)
+                      __attribute__((always_inline)) {
+    constexpr bool EMIT = decltype(emit_tag)::value;
     const auto ry = rsrc(yrow + (int64_t)bb * d_inner);
     // TR: delta and lam of the block's tokens and of the one after it (a
     // padding token's or a missing one's delta is 0), and C_t . B_t summed
@@ -448,46 +485,42 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
       }
       dtv[kTok] = t0 + bb + kTok < L ? pro.dt(widen(dn)) : 0.0f;
       lv[kTok] = widen(ln) + lam_add;
-      cbl = pb.dot(pc);
-      cbl += dpp_mov<0xB1>(cbl);        // lane ^ 1
-      cbl += dpp_mov<0x4E>(cbl);        // lane ^ 2
-      cbl += dpp_mov<0x141>(cbl);       // lane ^ 7 within 8 lanes
+      if constexpr (EMIT) {
+        cbl = pb.dot(pc);
+        cbl += dpp_mov<0xB1>(cbl);        // lane ^ 1
+        cbl += dpp_mov<0x4E>(cbl);        // lane ^ 2
+        cbl += dpp_mov<0x141>(cbl);       // lane ^ 7 within 8 lanes
+      }
     }
     float bsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-      Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
+      if constexpr (EMIT) Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
       Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
+      if constexpr (RMS) s_next = load_uniform(srow + std::min(bb + j + 1, nt - 1));
       // A padding token's delta reads 0; softplus would turn that into a
       // positive step, so it is forced back to 0 (a wave-uniform select).
-      const float dt = TR ? dtv[j] : SP ? (bb + j < nt ? pro.dt(widen(dq[j])) : 0.0f) : widen(dq[j]);
+      const float dt = TR ? dtv[j] : SP ? (bb + j < nt ? pro.dt(raw_dt(dq[j])) : 0.0f) : raw_dt(dq[j]);
       const float xv = pro.xin(widen(xx[j]));
       float dx = dt * xv, wn = 0.0f;
       if constexpr (TR) {
         wn = dtv[j + 1] * (1.0f - lv[j + 1]) * xv;        // w_{t+1}
         dx = fmaf(dx, lv[j], wn);                          // dt lam x + w_{t+1}
       }
-      if constexpr (MODE == kLocal) {
-        bsum += dt;
-        if constexpr (!SP) negbits |= raw_bits(dq[j]);
+      if constexpr (MODE != kWhole) bsum += dt;
+      if constexpr (MODE == kLocal && !SP) negbits |= __float_as_uint(dt);
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
+      if constexpr (EMIT) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NSTATE; ++n) acc = fmaf(Cv[n], h[n], acc);
+        if constexpr (TR)
+          acc = fmaf(-wn, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbl), 8 * j)), acc);
+        finish(ry, bb, j, acc, xv, widen(zz[j]));
       }
-      if constexpr (MODE == kFix) {
-#pragma unroll
-        for (int n = 0; n < NSTATE; ++n) {
-          const float e = fast_exp2(dt * a2[n]);
-          h[n] = fmaf(e, h[n], dx * Bc[n]);
-          dd[n] *= e;
-        }
-      } else {
-#pragma unroll
-        for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
-      }
-      float acc = 0.0f;
-#pragma unroll
-      for (int n = 0; n < NSTATE; ++n) acc = fmaf(Cv[n], h[n], acc);
-      if constexpr (TR) acc = fmaf(-wn, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbl), 8 * j)), acc);
-      finish(ry, bb, j, acc, xv, widen(zz[j]));
       Bc = Bn;
+      if constexpr (RMS) s_cur = s_next;
       // Keep each token's scalar B/C loads in its own token: hoisting them
       // across tokens would hold several rows in SGPRs at once and spill.
       __builtin_amdgcn_sched_barrier(0);
@@ -497,17 +530,22 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
       aux.rec.after_block(bb + kTok, nt, t0, L, b, c, h, dacc, d_inner, gbase, lo == lane, (uint32_t)lo * 4);
     }
     if constexpr (MODE == kFix) {
+      fsum += bsum;
+      // The part of the state pass 1 missed: exp(A * sum delta) * h_start,
+      // sum delta since the chunk start (exp2 of very negative arguments is 0).
       float dm = 0.0f, hm = 0.0f;
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) {
-        dm = fmaxf(dm, fabsf(dd[n]));
+        dm = fmaxf(dm, fast_exp2(a2[n] * fsum) * fabsf(hs[n]));
         hm = fmaxf(hm, fabsf(h[n]));
       }
-      const bool settled = can_exit && dm <= hm * kSettled;    // false for NaN
+      // never before the point from which pass 1 wrote y
+      const bool settled = can_exit && bb + kTok >= fix_from && dm <= hm * kSettled;    // false for NaN
       return __builtin_amdgcn_ballot_w64(!settled) == 0;
     }
     return false;
   };
+
 
   // Two register sets in turn: block i+1 is in flight while block i computes.
   T dA[kTok], xA[kTok], zA[kTok], lA[kTok], dnA, lnA;
@@ -515,22 +553,54 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
   Pair<T> pbA, pcA, pbB, pcB;
   load_block(0, dA, xA, zA, lA, dnA, lnA, pbA, pcA);
   Bc.load(brow);
+  if constexpr (RMS) s_cur = load_uniform(srow);
   __builtin_amdgcn_s_waitcnt(0);
   // Prefetches past the chunk's end are clamped to its last block (valid rows,
   // values unused), so every row offset below stays non-negative.
   const int last = (nt - 1) / kTok * kTok;
   const ProgressPrio prio(nt);
-  for (int base = 0; base < nt; base += 2 * kTok) {
-    if constexpr (MODE != kFix) prio.set(base);
-    load_block(std::min(base + kTok, last), dB, xB, zB, lB, dnB, lnB, pbB, pcB);
-    if (do_block(base, dA, xA, zA, lA, dnA, lnA, pbA, pcA)) break;
-    if (base + kTok >= nt) break;
-    load_block(std::min(base + 2 * kTok, last), dA, xA, zA, lA, dnA, lnA, pbA, pcA);
-    if (do_block(base + kTok, dB, xB, zB, lB, dnB, lnB, pbB, pcB)) break;
+  // Pairs of blocks, one register set each, the next block's loads in
+  // flight while a block computes.  Returns true when the chunk is done (or
+  // pass 2 may stop after this pair), false when a state-only pass reaches
+  // the point from which it must write y; `base` is then the next pair's
+  // first token.
+  int base = 0;
+  auto pairs = [&](auto emit_tag) __attribute__((always_inline)) {
+    constexpr bool EMIT = decltype(emit_tag)::value;
+    for (; base < nt; base += 2 * kTok) {
+      if constexpr (MODE != kFix) prio.set(base);
+      load_block(std::min(base + kTok, last), dB, xB, zB, lB, dnB, lnB, pbB, pcB);
+      const bool settled = do_block(emit_tag, base, dA, xA, zA, lA, dnA, lnA, pbA, pcA);
+      if (base + kTok >= nt) return true;
+      load_block(std::min(base + 2 * kTok, last), dA, xA, zA, lA, dnA, lnA, pbA, pcA);
+      // pass 2 leaves at a pair's end (one exit per iteration keeps the
+      // register allocation of the two blocks apart)
+      if (do_block(emit_tag, base + kTok, dB, xB, zB, lB, dnB, lnB, pbB, pcB) || settled) return true;
+      if constexpr (!EMIT) {
+        // The carried-in part of the state has decayed by exp(A * sum delta)
+        // since the chunk start, at most exp2(a2max * sum delta) for the
+        // slowest state: once that is below 2^-24 in every lane, pass 2 can
+        // stop here, so y from the next pair on is this pass's to write.
+        if (__builtin_amdgcn_ballot_w64(!(dacc >= settle_sum)) == 0) {
+          base += 2 * kTok;
+          return false;
+        }
+      }
+    }
+    return true;
+  };
+  if constexpr (MODE == kLocal) {
+    if (!emit && !pairs(std::false_type{})) {
+      emit = true;
+      emit_from = base;
+    }
+    if (emit && base < nt) pairs(std::true_type{});
+  } else {
+    pairs(std::true_type{});
   }
   if constexpr (MODE == kLocal) {
-    constexpr uint32_t sign = sizeof(T) == 2 ? 0x8000u : 0x80000000u;
-    if (lo == lane) aux.neg[(b * aux.chunks + c) * d_inner + d] = (negbits & sign) ? 1 : 0;
+    if (lo == lane) aux.neg[(b * aux.chunks + c) * d_inner + d] = (negbits & 0x80000000u) ? 1 : 0;
+    if (lane == 0) aux.from[(b * aux.chunks + c) * aux.groups + blockIdx.x] = emit ? emit_from : nt;
   }
   if constexpr (MODE == kWhole) {
     if (aux.hT && lo == lane) {
@@ -552,112 +622,71 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, MODE>())) void k_s
 }
 
 // ------------------------------------------------------------ input RMSNorm
-// RMSNorm before the scan, v / sqrt(mean v^2 + eps) * w, fp32 inside and the
-// result rounded to the I/O dtype.  Rows of B and C: one thread per (token,
-// tensor), all 16 entries; a null weight copies the row unchanged.
+// RMSNorm of the scan's inputs, v / sqrt(mean v^2 + eps) * w per token, over
+// the d_inner channels of the time step and over the 16 entries of each B and
+// C row.  This pre-pass writes, in fp32 (nothing is rounded to the I/O
+// dtype): s[row] = the time step's inverse root-mean-square (1 without a
+// weight), and the normalised B and C rows (a null weight copies the row).
+// The scan then reads delta * w[d] * s[t] and the fp32 rows.  One workgroup
+// per token row (grid-stride over rows); the time step's sum of squares is
+// reduced in-wave by shuffles and across the four waves through LDS, reading
+// 16-byte vectors when a row's size allows.
 template <class T>
-__global__ __launch_bounds__(256) void k_rms_rows(const T* __restrict__ B, const T* __restrict__ C,
-                                                  const float* __restrict__ wB, const float* __restrict__ wC,
-                                                  float eps, T* __restrict__ Bo, T* __restrict__ Co,
-                                                  int64_t rows) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * rows; i += (int64_t)gridDim.x * 256) {
-    const bool isC = i >= rows;
-    const int64_t r = isC ? i - rows : i;
-    const T* src = (isC ? C : B) + r * NSTATE;
-    T* dst = (isC ? Co : Bo) + r * NSTATE;
-    const float* w = isC ? wC : wB;
-    float v[NSTATE], ss = 0.0f;
-#pragma unroll
-    for (int n = 0; n < NSTATE; ++n) {
-      v[n] = widen(src[n]);
-      ss = fmaf(v[n], v[n], ss);
-    }
-    const float inv = w ? 1.0f / sqrtf(ss * (1.0f / NSTATE) + eps) : 1.0f;
-#pragma unroll
-    for (int n = 0; n < NSTATE; ++n) store_io(dst + n, w ? v[n] * inv * w[n] : v[n]);
-  }
-}
-
-// The time step over the d_inner channels of each token: one workgroup per
-// token row (grid-stride over rows), the sum of squares reduced in-wave by
-// shuffles and across the four waves through LDS.  Rows whose byte size is a
-// multiple of 16 move through 16-byte vectors (8 bf16 or 4 fp32 per lane);
-// rows of up to 256 x 4 vectors (8192 bf16 channels) stay in registers
-// between the sum and the scaling, longer ones are read again.
-template <class T>
-__global__ __launch_bounds__(256) void k_rms_dt(const T* __restrict__ delta, const float* __restrict__ w, float eps,
-                                                T* __restrict__ out, int64_t rows, int64_t d_inner) {
+__global__ __launch_bounds__(256) void k_rms_prep(const T* __restrict__ delta, const T* __restrict__ B,
+                                                  const T* __restrict__ C, const float* __restrict__ w_dt,
+                                                  const float* __restrict__ w_B, const float* __restrict__ w_C,
+                                                  float eps, int64_t rows, int64_t d_inner, float* __restrict__ s_out,
+                                                  float* __restrict__ B_out, float* __restrict__ C_out) {
   constexpr int V = 16 / sizeof(T);                  // elements per 16-byte vector
-  constexpr int R = 4;                               // vectors a lane can hold
   __shared__ float part[4];
   const bool vec = d_inner % V == 0;
-  const bool held = vec && d_inner <= (int64_t)256 * V * R;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    const T* src = delta + row * d_inner;
-    T* dst = out + row * d_inner;
-    float ss = 0.0f;
-    uint4 buf[R];
-    if (held) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int64_t d = ((int64_t)r * 256 + threadIdx.x) * V;
-        if (d < d_inner) {
-          buf[r] = *reinterpret_cast<const uint4*>(src + d);
-          const T* v = reinterpret_cast<const T*>(&buf[r]);
+    if (w_dt) {
+      const T* src = delta + row * d_inner;
+      float ss = 0.0f;
+      if (vec) {
+        for (int64_t d = (int64_t)threadIdx.x * V; d < d_inner; d += 256 * V) {
+          T v[V];
+          *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + d);
 #pragma unroll
           for (int k = 0; k < V; ++k) ss = fmaf(widen(v[k]), widen(v[k]), ss);
         }
-      }
-    } else if (vec) {
-      for (int64_t d = (int64_t)threadIdx.x * V; d < d_inner; d += 256 * V) {
-        T v[V];
-        *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + d);
-#pragma unroll
-        for (int k = 0; k < V; ++k) ss = fmaf(widen(v[k]), widen(v[k]), ss);
-      }
-    } else {
-      for (int64_t d = threadIdx.x; d < d_inner; d += 256) {
-        const float v = widen(src[d]);
-        ss = fmaf(v, v, ss);
-      }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-    __syncthreads();                                 // part[] of the previous row is consumed
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d_inner + eps);
-    if (held) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int64_t d = ((int64_t)r * 256 + threadIdx.x) * V;
-        if (d < d_inner) {
-          T v[V];
-          *reinterpret_cast<uint4*>(v) = buf[r];
-#pragma unroll
-          for (int k = 0; k < V; ++k) v[k] = to_io(widen(v[k]) * inv * w[d + k], T());
-          *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(v);
+      } else {
+        for (int64_t d = threadIdx.x; d < d_inner; d += 256) {
+          const float v = widen(src[d]);
+          ss = fmaf(v, v, ss);
         }
       }
-    } else if (vec) {
-      for (int64_t d = (int64_t)threadIdx.x * V; d < d_inner; d += 256 * V) {
-        T v[V];
-        *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + d);
 #pragma unroll
-        for (int k = 0; k < V; ++k) v[k] = to_io(widen(v[k]) * inv * w[d + k], T());
-        *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(v);
-      }
-    } else {
-      for (int64_t d = threadIdx.x; d < d_inner; d += 256) store_io(dst + d, widen(src[d]) * inv * w[d]);
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      __syncthreads();                               // part[] of the previous row is consumed
+      if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+      __syncthreads();
+      if (threadIdx.x == 0)
+        s_out[row] = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d_inner + eps);
+    } else if (threadIdx.x == 0) {
+      s_out[row] = 1.0f;
+    }
+    // B row on lanes 0-15, C row on lanes 16-31: one entry per lane
+    if (threadIdx.x < 2 * NSTATE) {
+      const int k = threadIdx.x / NSTATE, n = threadIdx.x % NSTATE;
+      const float* w = k ? w_C : w_B;
+      const float v = widen((k ? C : B)[row * NSTATE + n]);
+      float q = v * v;
+#pragma unroll
+      for (int m = NSTATE / 2; m >= 1; m >>= 1) q += __shfl_xor(q, m, NSTATE);
+      const float out = w ? v * (1.0f / sqrtf(q / (float)NSTATE + eps)) * w[n] : v;
+      (k ? C_out : B_out)[row * NSTATE + n] = out;
     }
   }
 }
 
-// Copy (or zero) the state for an empty sequence: hT = h0, or 0 when h0 is null.
+// Copy (or zero) the state for an empty sequence: hT = h0, or 0 when h0 is
+// null.  Grid-stride, so any size fits a capped grid.
 __global__ __launch_bounds__(256) void k_copy_state(const float* __restrict__ src, float* __restrict__ dst,
                                                     int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) dst[i] = src ? src[i] : 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = src ? src[i] : 0.0f;
 }
 
 // --------------------------------------------------------------- decode step
@@ -669,7 +698,7 @@ __global__ __launch_bounds__(256) void k_copy_state(const float* __restrict__ sr
 // (pa.hist[s][j][d], width-1 raw x) is read first and the shifted history,
 // ending with this token's x, written by the quad's first lane (in place
 // allowed).
-template <class T, bool CONV = false, bool SP = false, bool TR = false>
+template <class T, bool CONV = false, bool SP = false, bool TR = false, bool RMS = false>
 __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T* __restrict__ x,
                                               const T* __restrict__ delta, const float* __restrict__ A,
                                               const T* __restrict__ B, const T* __restrict__ C,
@@ -701,9 +730,21 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
     pro.h3 = hw == 3 ? hist[0] : 0.f;
   }
   const float xv = pro.xin(xraw);
-  const float dt = pro.dt(widen(delta[sd]));
-  const T* Bs = B + s * NSTATE + 4 * q;
-  const T* Cs = C + s * NSTATE + 4 * q;
+  // RMSNorm (prepared by k_rms_prep, one row per sequence): delta * w[d] *
+  // s[seq], and the normalised fp32 B and C rows
+  using RT = std::conditional_t<RMS, float, T>;
+  float dtr = widen(delta[sd]);
+  const RT* Bs;
+  const RT* Cs;
+  if constexpr (RMS) {
+    dtr = dtr * (pa.rms_w ? pa.rms_w[d] : 1.0f) * pa.rms_s[s];
+    Bs = pa.rms_B + s * NSTATE + 4 * q;
+    Cs = pa.rms_C + s * NSTATE + 4 * q;
+  } else {
+    Bs = B + s * NSTATE + 4 * q;
+    Cs = C + s * NSTATE + 4 * q;
+  }
+  const float dt = pro.dt(dtr);
   float dx = dt * xv;
   if constexpr (TR) {
     // h = a (h + w B_prev) + v B with w = dt (1 - lam) x_prev, v = dt lam x
@@ -821,6 +862,13 @@ double scan_time(double waves, double tokens) {
 
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Workgroups of 256 for a grid-stride pass over n elements (capped).
+unsigned copy_grid(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1 << 20)); }
+
+// The decode step runs four lanes per (sequence, channel) in a
+// one-dimensional grid, which holds at most 2^32 work-items.
+constexpr int64_t kMaxStepChannels = ((int64_t)1 << 30) - 64;
+
 // Pieces of about L / n tokens: a multiple of kTok, n' = ceil(L / len) of them.
 void split(int64_t L, int64_t n, int64_t* len, int* count) {
   const int64_t Lp = std::max<int64_t>(L, 1);
@@ -897,13 +945,14 @@ WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
     w.eS = round_up(B * C * NSTATE * Dn * sizeof(float));
     w.eL = round_up(B * C * Dn * sizeof(float));
     w.neg = round_up(B * C * Dn * sizeof(int32_t));
+    w.from = round_up(B * C * (size_t)((d_inner + 63) / 64) * sizeof(int32_t));
     w.H = round_up(B * C * NSTATE * Dn * sizeof(float));
     if (p.subs > 1) {
       w.sS = round_up(B * (size_t)p.subs * NSTATE * Dn * sizeof(float));
       w.sL = round_up(B * (size_t)p.subs * Dn * sizeof(float));
     }
   }
-  w.total = w.tag + w.eS + w.eL + w.neg + w.H + w.sS + w.sL;
+  w.total = w.tag + w.eS + w.eL + w.neg + w.from + w.H + w.sS + w.sL;
   return w;
 }
 
@@ -921,12 +970,12 @@ bool sizes_ok(int64_t batch, int64_t L, int64_t d_inner) {
   return L <= INT32_MAX && batch <= 65535 && d_inner <= (1 << 24);
 }
 
-template <class T, bool CONV, bool SP, bool TR, int MODE>
+template <class T, bool CONV, bool SP, bool TR, bool RMS, int MODE>
 hipError_t launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C,
                        const float* D, const void* z, void* y, const ScanAux& aux, const ProArgs& pa,
                        unsigned chunks, int64_t batch, hipStream_t st) {
   dim3 grid((unsigned)((aux.d_inner + 63) / 64), chunks, (unsigned)batch);
-  hipLaunchKernelGGL((k_scan<T, CONV, SP, TR, MODE>), grid, dim3(64), 0, st, static_cast<const T*>(x),
+  hipLaunchKernelGGL((k_scan<T, CONV, SP, TR, RMS, MODE>), grid, dim3(64), 0, st, static_cast<const T*>(x),
                      static_cast<const T*>(delta), A, static_cast<const T*>(B), static_cast<const T*>(C), D,
                      static_cast<const T*>(z), static_cast<T*>(y), aux, pa);
   return hipGetLastError();
@@ -938,19 +987,20 @@ Records records_in(char* ws, const WsLayout& w, const Plan& p) {
                  p.subs > 1 ? reinterpret_cast<float*>(ws + w.off_sL()) : nullptr, p.sub_len, p.chunks, p.subs};
 }
 
-template <class T, bool CONV, bool SP, bool TR>
+template <class T, bool CONV, bool SP, bool TR, bool RMS>
 jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* x, const void* delta,
                          const float* A, const void* B, const void* C, const float* D, const void* z,
                          const float* h0, void* y, float* hT, char* ws, const Plan& p, const ProArgs& pa,
-                         bool rms, hipStream_t st) {
+                         hipStream_t st) {
   const WsLayout w = ws_layout(batch, L, d_inner, p);
-  ScanAux aux{h0, hT, Records{}, nullptr, nullptr, L, d_inner, p.chunk_len, p.chunks};
+  ScanAux aux{h0, hT, Records{}, nullptr, nullptr, nullptr, L, d_inner, p.chunk_len, p.chunks,
+              (int)((d_inner + 63) / 64)};
   hipEvent_t eb = t_ev_before, ea = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
   hipError_t e;
   if (eb && ea && (e = hipEventRecord(eb, st)) != hipSuccess) return hip_fail(e, "event record");
   if (!p.recorded()) {
-    if ((e = launch_scan<T, CONV, SP, TR, kWhole>(x, delta, A, B, C, D, z, y, aux, pa, 1, batch, st)) !=
+    if ((e = launch_scan<T, CONV, SP, TR, RMS, kWhole>(x, delta, A, B, C, D, z, y, aux, pa, 1, batch, st)) !=
         hipSuccess)
       return hip_fail(e, "scan launch");
     if (eb && ea && (e = hipEventRecord(ea, st)) != hipSuccess) return hip_fail(e, "event record");
@@ -958,20 +1008,21 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
   }
   aux.rec = records_in(ws, w, p);
   aux.neg = reinterpret_cast<int32_t*>(ws + w.off_neg());
+  aux.from = reinterpret_cast<int32_t*>(ws + w.off_from());
   float* H = reinterpret_cast<float*>(ws + w.off_H());
   aux.H = H;
-  if ((e = launch_scan<T, CONV, SP, TR, kLocal>(x, delta, A, B, C, D, z, y, aux, pa, (unsigned)p.chunks, batch,
+  if ((e = launch_scan<T, CONV, SP, TR, RMS, kLocal>(x, delta, A, B, C, D, z, y, aux, pa, (unsigned)p.chunks, batch,
                                                 st)) != hipSuccess)
     return hip_fail(e, "scan launch");
   if (eb && ea && (e = hipEventRecord(ea, st)) != hipSuccess) return hip_fail(e, "event record");
-  const int variant = (CONV ? 1 : 0) | (SP ? 2 : 0) | (TR ? 4 : 0) | (rms ? 8 : 0);
+  const int variant = (CONV ? 1 : 0) | (SP ? 2 : 0) | (TR ? 4 : 0) | (RMS ? 8 : 0);
   dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
   hipLaunchKernelGGL((k_combine<T>), g2, dim3(256), 0, st, A, aux.rec.eS, aux.rec.eL, H, hT, d_inner, p.chunks,
                      static_cast<const T*>(x), L, CONV ? pa : ProArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 1},
                      reinterpret_cast<int64_t*>(ws), make_tag(batch, L, d_inner, p, variant));
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
   if (p.chunks > 1 &&
-      (e = launch_scan<T, CONV, SP, TR, kFix>(x, delta, A, B, C, D, z, y, aux, pa, (unsigned)(p.chunks - 1), batch,
+      (e = launch_scan<T, CONV, SP, TR, RMS, kFix>(x, delta, A, B, C, D, z, y, aux, pa, (unsigned)(p.chunks - 1), batch,
                                               st)) != hipSuccess)
     return hip_fail(e, "scan launch");
   return JSCAN_OK;
@@ -1017,17 +1068,21 @@ jscan_status sub_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_i
 }
 
 // Calls f(integral_constant<bool, CONV>, integral_constant<bool, SP>,
-// integral_constant<bool, TR>) for the supported combinations (the
-// trapezoidal form takes no convolution; callers reject that pair first).
+// integral_constant<bool, TR>, integral_constant<bool, RMS>) for the
+// supported combinations (the trapezoidal form takes no convolution and no
+// RMSNorm; callers reject those pairs first).
 template <class F>
-auto with_flags(bool conv, bool sp, bool tr, F&& f) {
+auto with_flags(bool conv, bool sp, bool tr, bool rms, F&& f) {
   using Y = std::true_type;
   using N = std::false_type;
-  if (tr) return sp ? f(N{}, Y{}, Y{}) : f(N{}, N{}, Y{});
-  if (conv && sp) return f(Y{}, Y{}, N{});
-  if (conv) return f(Y{}, N{}, N{});
-  if (sp) return f(N{}, Y{}, N{});
-  return f(N{}, N{}, N{});
+  if (tr) return sp ? f(N{}, Y{}, Y{}, N{}) : f(N{}, N{}, Y{}, N{});
+  auto pick = [&](auto r) {
+    if (conv && sp) return f(Y{}, Y{}, N{}, r);
+    if (conv) return f(Y{}, N{}, N{}, r);
+    if (sp) return f(N{}, Y{}, N{}, r);
+    return f(N{}, N{}, N{}, r);
+  };
+  return rms ? pick(Y{}) : pick(N{});
 }
 
 jscan_status check_common(int64_t d_state, jscan_io io) {
@@ -1051,12 +1106,12 @@ jscan_status check_ranges(const Range* in, int n_in, const Range* out, int n_out
   return JSCAN_OK;
 }
 
-template <class T, bool CONV, bool SP, bool TR>
+template <class T, bool CONV, bool SP, bool TR, bool RMS>
 jscan_status run_step(int64_t n_seq, int64_t d_inner, float* state, const void* x, const void* delta,
                       const float* A, const void* B, const void* C, const float* D, const void* z,
                       void* y, const ProArgs& pa, hipStream_t st) {
   const int64_t total = n_seq * d_inner * 4;
-  hipLaunchKernelGGL((k_step<T, CONV, SP, TR>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, state,
+  hipLaunchKernelGGL((k_step<T, CONV, SP, TR, RMS>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, state,
                      static_cast<const T*>(x), static_cast<const T*>(delta), A, static_cast<const T*>(B),
                      static_cast<const T*>(C), D, static_cast<const T*>(z), static_cast<T*>(y), n_seq,
                      d_inner, pa);
@@ -1111,50 +1166,34 @@ jscan_status check_prologue(const jscan_prologue* pro, int64_t nseq, int64_t d_i
   return JSCAN_OK;
 }
 
-// Normalises delta (over d_inner) and the B, C rows (over d_state) per token
-// into stream-ordered scratch and points delta, B, C at the results; the
-// caller frees *scratch after the scan.
-jscan_status apply_rms(const jscan_prologue* pro, jscan_io io, int64_t nseq, int64_t L, int64_t d_inner,
-                       const void** delta, const void** B, const void** C, void** scratch, hipStream_t st) {
-  *scratch = nullptr;
-  if (!has_rms(pro) || nseq == 0 || L == 0 || d_inner == 0) return JSCAN_OK;
-  const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
-  const int64_t rows = nseq * L;
-  const size_t dbytes = pro->rms_dt_weight ? round_up((size_t)rows * (size_t)d_inner * es) : 0;
-  const size_t rbytes = (pro->rms_B_weight || pro->rms_C_weight) ? round_up((size_t)rows * NSTATE * es) : 0;
-  char* p = nullptr;
-  hipError_t e;
-  if ((e = hipMallocAsync(reinterpret_cast<void**>(&p), dbytes + 2 * rbytes, st)) != hipSuccess)
-    return hip_fail(e, "hipMallocAsync(rmsnorm scratch)");
-  *scratch = p;
-  const unsigned grid_rows = (unsigned)std::min<int64_t>(rows, 1 << 20);
-  if (pro->rms_dt_weight) {
-    if (io == JSCAN_IO_BF16)
-      hipLaunchKernelGGL((k_rms_dt<uint16_t>), dim3(grid_rows), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(*delta), pro->rms_dt_weight, pro->rms_eps,
-                         reinterpret_cast<uint16_t*>(p), rows, d_inner);
-    else
-      hipLaunchKernelGGL((k_rms_dt<float>), dim3(grid_rows), dim3(256), 0, st, static_cast<const float*>(*delta),
-                         pro->rms_dt_weight, pro->rms_eps, reinterpret_cast<float*>(p), rows, d_inner);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
-    *delta = p;
-  }
-  if (rbytes) {
-    char* bo = p + dbytes;
-    char* co = bo + rbytes;
-    const unsigned grid = (unsigned)std::min<int64_t>((2 * rows + 255) / 256, 1 << 20);
-    if (io == JSCAN_IO_BF16)
-      hipLaunchKernelGGL((k_rms_rows<uint16_t>), dim3(grid), dim3(256), 0, st, static_cast<const uint16_t*>(*B),
-                         static_cast<const uint16_t*>(*C), pro->rms_B_weight, pro->rms_C_weight, pro->rms_eps,
-                         reinterpret_cast<uint16_t*>(bo), reinterpret_cast<uint16_t*>(co), rows);
-    else
-      hipLaunchKernelGGL((k_rms_rows<float>), dim3(grid), dim3(256), 0, st, static_cast<const float*>(*B),
-                         static_cast<const float*>(*C), pro->rms_B_weight, pro->rms_C_weight, pro->rms_eps,
-                         reinterpret_cast<float*>(bo), reinterpret_cast<float*>(co), rows);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
-    *B = bo;
-    *C = co;
-  }
+// Bytes of the RMSNorm region for `rows` token rows: the time step's inverse
+// root-mean-square per row, then the normalised B and C rows, all fp32.
+size_t rms_bytes(int64_t rows) {
+  return rows > 0 ? round_up((size_t)rows * 4) + 2 * round_up((size_t)rows * NSTATE * 4) : 0;
+}
+
+// Launches the RMSNorm pre-pass over `rows` token rows into `region`
+// (rms_bytes(rows) bytes) and points pa's RMSNorm fields at the results.
+jscan_status rms_prep(const jscan_prologue* pro, jscan_io io, int64_t rows, int64_t d_inner, const void* delta,
+                      const void* B, const void* C, char* region, ProArgs* pa, hipStream_t st) {
+  float* s_out = reinterpret_cast<float*>(region);
+  float* B_out = reinterpret_cast<float*>(region + round_up((size_t)rows * 4));
+  float* C_out = reinterpret_cast<float*>(region + round_up((size_t)rows * 4) + round_up((size_t)rows * NSTATE * 4));
+  const unsigned grid = (unsigned)std::min<int64_t>(rows, 1 << 20);
+  if (io == JSCAN_IO_BF16)
+    hipLaunchKernelGGL((k_rms_prep<uint16_t>), dim3(grid), dim3(256), 0, st, static_cast<const uint16_t*>(delta),
+                       static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C), pro->rms_dt_weight,
+                       pro->rms_B_weight, pro->rms_C_weight, pro->rms_eps, rows, d_inner, s_out, B_out, C_out);
+  else
+    hipLaunchKernelGGL((k_rms_prep<float>), dim3(grid), dim3(256), 0, st, static_cast<const float*>(delta),
+                       static_cast<const float*>(B), static_cast<const float*>(C), pro->rms_dt_weight,
+                       pro->rms_B_weight, pro->rms_C_weight, pro->rms_eps, rows, d_inner, s_out, B_out, C_out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+  pa->rms_s = s_out;
+  pa->rms_w = pro->rms_dt_weight;
+  pa->rms_B = B_out;
+  pa->rms_C = C_out;
   return JSCAN_OK;
 }
 
@@ -1230,7 +1269,8 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
     plan.subs = 1;
     plan.sub_len = std::max<int64_t>(L, 1);
   }
-  const size_t need = ws_layout(batch, L, d_inner, plan).total;
+  const size_t rec_bytes = ws_layout(batch, L, d_inner, plan).total;
+  const size_t need = rec_bytes + (has_rms(pro) ? rms_bytes(batch * L) : 0);
   if (noalloc && need > kScratchBytes)
     return fail(JSCAN_ERR_WORKSPACE, "jscan_prefill_noalloc: this problem needs " + std::to_string(need) +
                                          " bytes of scratch, more than its " + std::to_string(kScratchBytes));
@@ -1265,12 +1305,12 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
     if (L == 0 && batch > 0 && d_inner > 0) {
       if (hT && hT != h0) {
         const int64_t n = batch * d_inner * NSTATE;
-        hipLaunchKernelGGL(k_copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, h0, hT, n);
+        hipLaunchKernelGGL(k_copy_state, dim3(copy_grid(n)), dim3(256), 0, st, h0, hT, n);
         if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "state copy launch");
       }
       if (pa.hist_out && pa.hist_out != pa.hist && pa.width > 1) {
         const int64_t n = batch * (pa.width - 1) * d_inner;
-        hipLaunchKernelGGL(k_copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pa.hist,
+        hipLaunchKernelGGL(k_copy_state, dim3(copy_grid(n)), dim3(256), 0, st, pa.hist,
                            pa.hist_out, n);
         if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "history copy launch");
       }
@@ -1278,38 +1318,30 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
     t_ev_before = t_ev_after = nullptr;
     return JSCAN_OK;
   }
-  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
+  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr, rms = has_rms(pro);
   if (noalloc && need > 0 && (s = scratch_address(&workspace)) != JSCAN_OK) return s;
-  const void *dl = delta, *Bs = B, *Cs = C;
-  void* rms_scratch = nullptr;
-  if ((s = apply_rms(pro, io, batch, L, d_inner, &dl, &Bs, &Cs, &rms_scratch, st)) != JSCAN_OK) {
-    if (rms_scratch) (void)hipFreeAsync(rms_scratch, st);
-    return s;
-  }
   char* ws = static_cast<char*>(workspace);
   bool owned = false;
   if (!ws && need > 0) {
-    if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess) {
-      if (rms_scratch) (void)hipFreeAsync(rms_scratch, st);
+    if ((e = hipMallocAsync(reinterpret_cast<void**>(&ws), need, st)) != hipSuccess)
       return hip_fail(e, "hipMallocAsync(workspace)");
-    }
     owned = true;
   }
-  s = with_flags(conv, sp, tr, [&](auto cv, auto spv, auto trv) {
-    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value;
-    return io == JSCAN_IO_BF16
-               ? run_prefill<uint16_t, CV, SPV, TRV>(batch, L, d_inner, x, dl, A, Bs, Cs, D, z, h0, y, hT, ws,
-                                                     plan, pa, has_rms(pro), st)
-               : run_prefill<float, CV, SPV, TRV>(batch, L, d_inner, x, dl, A, Bs, Cs, D, z, h0, y, hT, ws,
-                                                  plan, pa, has_rms(pro), st);
-  });
+  // RMSNorm: its per-token data go after the records, in the same workspace
+  if (rms) s = rms_prep(pro, io, batch * L, d_inner, delta, B, C, ws + rec_bytes, &pa, st);
+  if (s == JSCAN_OK)
+    s = with_flags(conv, sp, tr, rms, [&](auto cv, auto spv, auto trv, auto rmv) {
+      constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value,
+                     RMV = decltype(rmv)::value;
+      return io == JSCAN_IO_BF16
+                 ? run_prefill<uint16_t, CV, SPV, TRV, RMV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT,
+                                                            ws, plan, pa, st)
+                 : run_prefill<float, CV, SPV, TRV, RMV>(batch, L, d_inner, x, delta, A, B, C, D, z, h0, y, hT, ws,
+                                                         plan, pa, st);
+    });
   if (owned) {
     e = hipFreeAsync(ws, st);
     if (s == JSCAN_OK && e != hipSuccess) s = hip_fail(e, "hipFreeAsync(workspace)");
-  }
-  if (rms_scratch) {
-    e = hipFreeAsync(rms_scratch, st);
-    if (s == JSCAN_OK && e != hipSuccess) s = hip_fail(e, "hipFreeAsync(rmsnorm scratch)");
   }
   return s;
 }
@@ -1322,9 +1354,9 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
   jscan_status s = check_common(d_state, io);
   if (s != JSCAN_OK) return s;
   int64_t t;
-  if (n_seq < 0 || d_inner < 0 || !mul_ok(n_seq, d_inner, &t) || !mul_ok(t, NSTATE * 16, &t) ||
-      t / (NSTATE * 16) > ((int64_t)1 << 37))
-    return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and fit 64-bit byte counts");
+  // four lanes per (sequence, channel) in a one-dimensional grid of at most 2^32 work-items
+  if (n_seq < 0 || d_inner < 0 || !mul_ok(n_seq, d_inner, &t) || t > kMaxStepChannels)
+    return fail(JSCAN_ERR_SHAPE, "sizes must be >= 0 and n_seq * d_inner at most 2^30 - 64");
   if (n_seq == 0 || d_inner == 0) {                       // nothing to do; the prologue is still checked
     Range in[12], out[1];
     int n_in = 0, n_out = 0;
@@ -1352,19 +1384,23 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
       JSCAN_OK)
     return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
-  const void *dl = delta, *Bs = B, *Cs = C;
-  void* rms_scratch = nullptr;
-  if ((s = apply_rms(pro, io, n_seq, 1, d_inner, &dl, &Bs, &Cs, &rms_scratch, st)) != JSCAN_OK) {
-    if (rms_scratch) (void)hipFreeAsync(rms_scratch, st);
-    return s;
+  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr, rms = has_rms(pro);
+  // RMSNorm: one row per sequence, in stream-ordered scratch (the step takes no workspace)
+  char* rms_scratch = nullptr;
+  if (rms) {
+    hipError_t e;
+    if ((e = hipMallocAsync(reinterpret_cast<void**>(&rms_scratch), rms_bytes(n_seq), st)) != hipSuccess)
+      return hip_fail(e, "hipMallocAsync(rmsnorm scratch)");
+    s = rms_prep(pro, io, n_seq, d_inner, delta, B, C, rms_scratch, &pa, st);
   }
-  s = with_flags(conv, sp, tr, [&](auto cv, auto spv, auto trv) {
-    constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value;
-    return io == JSCAN_IO_BF16
-               ? run_step<uint16_t, CV, SPV, TRV>(n_seq, d_inner, state, x, dl, A, Bs, Cs, D, z, y, pa, st)
-               : run_step<float, CV, SPV, TRV>(n_seq, d_inner, state, x, dl, A, Bs, Cs, D, z, y, pa, st);
-  });
+  if (s == JSCAN_OK)
+    s = with_flags(conv, sp, tr, rms, [&](auto cv, auto spv, auto trv, auto rmv) {
+      constexpr bool CV = decltype(cv)::value, SPV = decltype(spv)::value, TRV = decltype(trv)::value,
+                     RMV = decltype(rmv)::value;
+      return io == JSCAN_IO_BF16
+                 ? run_step<uint16_t, CV, SPV, TRV, RMV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st)
+                 : run_step<float, CV, SPV, TRV, RMV>(n_seq, d_inner, state, x, delta, A, B, C, D, z, y, pa, st);
+    });
   if (rms_scratch) {
     const hipError_t e = hipFreeAsync(rms_scratch, st);
     if (s == JSCAN_OK && e != hipSuccess) s = hip_fail(e, "hipFreeAsync(rmsnorm scratch)");
@@ -1425,7 +1461,8 @@ size_t jscan_prefill_workspace_size(int64_t batch, int64_t L, int64_t d_inner, i
                                     jscan_io io) {
   if (d_state != NSTATE || (io != JSCAN_IO_F32 && io != JSCAN_IO_BF16)) return 0;
   if (!sizes_ok(batch, L, d_inner)) return 0;
-  return ws_layout(batch, L, d_inner, choose_plan(batch, L, d_inner)).total;
+  // the records of the plan, and the RMSNorm region a fused call may need
+  return ws_layout(batch, L, d_inner, choose_plan(batch, L, d_inner)).total + rms_bytes(batch * L);
 }
 
 jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,

@@ -635,8 +635,8 @@ __global__ __launch_bounds__(256) void k_reduce_ad(const float* __restrict__ dAp
 
 __global__ __launch_bounds__(256) void k_copy_or_zero(const float* __restrict__ src, float* __restrict__ dst,
                                                       int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) dst[i] = src ? src[i] : 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = src ? src[i] : 0.0f;
 }
 
 // ------------------------------------------------------------------ host
@@ -654,7 +654,9 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   const size_t B = (size_t)batch, C = (size_t)p.subs, Dn = (size_t)d_inner;
   const size_t G = (size_t)((d_inner + 63) / 64);
   const size_t blocks = (size_t)((p.sub_len + kTok - 1) / kTok);
-  w.fwd = ws_layout(batch, L, d_inner, p).total;
+  // the size of a prefill's workspace (its records and RMSNorm region), so a
+  // backward reusing one needs jscan_prefill_workspace_size() bytes less
+  w.fwd = ws_layout(batch, L, d_inner, p).total + rms_bytes(batch * L);
   if (p.subs > 1) {
     w.hs = round_up(B * C * NSTATE * Dn * 4);
     w.M = round_up(B * C * NSTATE * Dn * 4);
@@ -678,10 +680,12 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
   const BwdLayout w = bwd_layout(batch, L, d_inner, p);
   // The sub-chunk starting states, derived from the records a prefill left
   // in its workspace (`saved`) or from records recomputed into this one.
+  // (records are recomputed, and need their region, only without saved ones
+  // and with more than one sub-chunk)
   char* q = ws;
   float* hstart = reinterpret_cast<float*>(q); q += w.hs;
-  char* rec = saved ? nullptr : q;
-  if (!saved) q += w.fwd;
+  char* rec = !saved && p.subs > 1 ? q : nullptr;
+  if (rec) q += w.fwd;
   float* M = reinterpret_cast<float*>(q); q += w.M;
   float* dsum = reinterpret_cast<float*>(q); q += w.dsum;
   float* ck = reinterpret_cast<float*>(q); q += w.ck;
@@ -752,17 +756,19 @@ jscan_status backward_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
   const BwdLayout bl = bwd_layout(batch, L, d_inner, plan);
   // With saved chunk states the front of the workspace (the prefill's part) is not needed.
   const bool use_saved = saved && work && plan.subs > 1;
-  const size_t need = use_saved ? bl.total - bl.fwd : bl.total;
-  const WsLayout fl = ws_layout(batch, L, d_inner, plan);
+  // a saved-state call needs jscan_prefill_workspace_size() bytes less in every plan
+  const size_t need = saved ? bl.total - bl.fwd : bl.total;
+  // the prefill's workspace: jscan_prefill_workspace_size() bytes (records and RMSNorm region)
+  const size_t pws_need = ws_layout(batch, L, d_inner, plan).total + rms_bytes(batch * L);
   if (use_saved && !prefill_ws)
     return fail(JSCAN_ERR_NULL, "this plan runs in chunks: the prefill's workspace is required");
   if (use_saved && !aligned16(prefill_ws))
     return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
-  if (use_saved && prefill_ws_bytes < fl.total)
+  if (use_saved && prefill_ws_bytes < pws_need)
     return fail(JSCAN_ERR_WORKSPACE, "prefill workspace smaller than jscan_prefill_workspace_size()");
   const Range in[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {dy, tok, "dy"}, {B, rowb, "B"},
                       {C, rowb, "C"}, {A, pd, "A"}, {D, (size_t)d_inner * 4, "D"}, {h0, stb, "h0"},
-                      {dhT, stb, "dhT"}, {use_saved ? prefill_ws : nullptr, use_saved ? fl.total : 0,
+                      {dhT, stb, "dhT"}, {use_saved ? prefill_ws : nullptr, use_saved ? pws_need : 0,
                                           "prefill workspace"}};
   const Range out[] = {{dx, tok, "dx"}, {ddelta, tok, "ddelta"}, {dz, tok, "dz"}, {dA, pd, "dA"},
                        {dB, row4, "dB"}, {dC, row4, "dC"}, {dD, (size_t)d_inner * 4, "dD"}, {dh0, stb, "dh0"},
@@ -771,7 +777,7 @@ jscan_status backward_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
       JSCAN_OK)
     return s;
   if (workspace && workspace_bytes < need)
-    return fail(JSCAN_ERR_WORKSPACE, use_saved ? "workspace smaller than jscan_backward_workspace_size() - "
+    return fail(JSCAN_ERR_WORKSPACE, saved ? "workspace smaller than jscan_backward_workspace_size() - "
                                                  "jscan_prefill_workspace_size()"
                                                : "workspace smaller than jscan_backward_workspace_size()");
 
@@ -786,7 +792,7 @@ jscan_status backward_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
     }
     if (dh0 && batch > 0 && d_inner > 0) {
       const int64_t n = batch * d_inner * NSTATE;
-      hipLaunchKernelGGL(k_copy_or_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dhT, dh0, n);
+      hipLaunchKernelGGL(k_copy_or_zero, dim3(copy_grid(n)), dim3(256), 0, st, dhT, dh0, n);
       if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dh0 copy launch");
     }
     return JSCAN_OK;

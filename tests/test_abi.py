@@ -153,11 +153,29 @@ def test_noalloc_rejects_problems_beyond_its_scratch(lib):
     assert js.plan(1, 65536, 8192)[1] * 8192 * 136 + 5 * 256 <= (64 << 20)
 
 
+def rms_region(rows):
+    """Bytes of a prefill workspace's RMSNorm region: per token the time step's
+    inverse root-mean-square and the normalised B and C rows, fp32, each part
+    rounded up to 256 bytes."""
+    up = lambda v: (v + 255) // 256 * 256
+    return up(rows * 4) + 2 * up(rows * 16 * 4)
+
+
 def test_prefill_workspace_too_small(lib):
+    """jscan_prefill_workspace_size covers every variant: a plain call needs the
+    records of its plan, a call with RMSNorm also the RMSNorm region."""
     L, d = 65536, 8192
     ws = js.workspace_size(1, L, d)
-    assert ws > 0
-    assert call_prefill(lib, prefill_args(L=L, d_inner=d, workspace=fake(10), ws_bytes=ws - 1)) == WS
+    rec = ws - rms_region(L)
+    assert rec > 0
+    assert call_prefill(lib, prefill_args(L=L, d_inner=d, workspace=fake(10), ws_bytes=rec - 1)) == WS
+    base = dict(conv_weight=None, conv_bias=None, conv_state_in=None, conv_state_out=None, dt_bias=None)
+    pro = prologue(**base, rms_dt_weight=fake(24))
+    a = prefill_args(L=L, d_inner=d, workspace=fake(10), ws_bytes=ws - 1)
+    assert call_prefill_fused(lib, a, pro) == WS
+    # a one-chunk plan records nothing, but RMSNorm still needs its region
+    assert js.plan(64, 100, 8192)[1] == 1
+    assert js.workspace_size(64, 100, 8192) == rms_region(6400)
 
 
 def test_workspace_size_formula(lib):
@@ -289,7 +307,7 @@ def test_prefill_fused_in_place_history_is_allowed(lib):
     # conv_state_out == conv_state_in passes the alias check; the call then
     # stops at the (deliberately short) workspace, before any launch.
     L, d = 65536, 8192
-    ws = js.workspace_size(1, L, d)
+    ws = js.workspace_size(1, L, d) - rms_region(L)     # the records (no RMSNorm here)
     a = prefill_args(L=L, d_inner=d, workspace=fake(10), ws_bytes=ws - 1)
     assert call_prefill_fused(lib, a, prologue(conv_state_out=fake(13))) == WS
     assert call_prefill_fused(lib, a, prologue()) == WS
