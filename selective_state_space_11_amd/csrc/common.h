@@ -34,9 +34,15 @@ __device__ __forceinline__ float silu(float zv) {
 
 // softplus(v) = log(1 + exp(v)), through v_exp_f32 / v_log_f32 (base 2).  For
 // v > 15 it equals v to fp32 precision; for tiny exp(v) log(1 + e) ~ e - e^2/2.
+// Both candidates are evaluated before the selects: a select with v_log on
+// one side would otherwise become a divergent branch, and the basic blocks it
+// makes let the compiler pull the softplus and B-row loads of a whole token
+// block ahead of the state updates (rows piling up in SGPRs).
 __device__ __forceinline__ float softplus(float v) {
   const float e = fast_exp2(v * kLog2e);
-  const float r = e < 1.0e-3f ? e - 0.5f * e * e : __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
+  const float big = __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
+  const float small = e - 0.5f * e * e;
+  const float r = e < 1.0e-3f ? small : big;
   return v > 15.0f ? v : r;
 }
 

@@ -75,7 +75,7 @@ constexpr float kSettled = 0x1p-24f;
 // trapezoidal scan needs 129 without a bound (3 waves); held to 4 waves it
 // fits 121 without spilling VGPRs and runs its 64K prefill about 6% faster.
 template <class T, bool CONV, bool SP, bool TR, bool RMS, int MODE>
-constexpr int scan_waves() { return sizeof(T) == 2 && TR && MODE == kWhole ? 4 : 1; }
+constexpr int scan_waves() { return sizeof(T) == 2 && (TR || MODE != kWhole) ? 4 : 1; }
 
 // One float from a wave-uniform address, as a scalar load.
 __device__ __forceinline__ float load_uniform(const float* p) { return __uint_as_float(*uniform_ptr<uint32_t>(p)); }
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
   const int lo = (int)std::min<int64_t>(lane, d_inner - 1 - gbase);
   const int64_t d = gbase + lo;
 
-  float a2[NSTATE], h[NSTATE], hs[MODE == kFix ? NSTATE : 1];
+  float a2[NSTATE], h[NSTATE];
   load_a2(a2, A, d);
   bool can_exit = true;
   // kLocal: chunk 0 (from the true h0) writes all its y; a later chunk starts
@@ -367,12 +367,17 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
   }
   // kFix: the first token from which pass 1 wrote y for this wave's channels
   const int fix_from = MODE == kFix ? aux.from[(b * aux.chunks + (int64_t)blockIdx.y + 1) * aux.groups + blockIdx.x] : 0;
+  // kFix: the carry pass 1 missed is exp(A * sum delta) * h_start, at most
+  // exp2(fix_a2 * sum delta) * fix_h with the slowest state's A' and the
+  // largest |h_start|.
+  float fix_a2 = -__builtin_inff(), fix_h = 0.0f;
   if constexpr (MODE == kFix) {
     const float* hi = aux.H + ((b * aux.chunks + c) * NSTATE) * d_inner + d;
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) {
       h[n] = hi[(int64_t)n * d_inner];
-      hs[n] = h[n];
+      fix_h = fmaxf(fix_h, fabsf(h[n]));
+      fix_a2 = fmaxf(fix_a2, a2[n]);
       can_exit = can_exit && a2[n] <= 0.0f;
     }
     can_exit = can_exit && aux.neg[(b * aux.chunks + c) * d_inner + d] == 0;
@@ -453,7 +458,7 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
 
   // B of the next token is prefetched a token ahead; C is needed only after
   // the token's state updates, so it is loaded at the token's start.
-  Row<RT, NSTATE> Bc, Bn, Cv;
+  Row<RT, NSTATE> Bc, Cv;
   double dacc = 0.0;                 // kLocal: delta sum since the chunk start
   float fsum = 0.0f;                 // kFix: delta sum since the chunk start
   uint32_t negbits = 0;              // kLocal: OR of the time steps' bits (sign bit)
@@ -496,11 +501,11 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       if constexpr (EMIT) Cv.load(crow + (int64_t)std::min(bb + j, nt - 1) * NSTATE);
-      Bn.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
       if constexpr (RMS) s_next = load_uniform(srow + std::min(bb + j + 1, nt - 1));
       // A padding token's delta reads 0; softplus would turn that into a
       // positive step, so it is forced back to 0 (a wave-uniform select).
-      const float dt = TR ? dtv[j] : SP ? (bb + j < nt ? pro.dt(raw_dt(dq[j])) : 0.0f) : raw_dt(dq[j]);
+      const float dts = SP ? pro.dt(raw_dt(dq[j])) : 0.0f;     // evaluated unconditionally: a select, no branch
+      const float dt = TR ? dtv[j] : SP ? (bb + j < nt ? dts : 0.0f) : raw_dt(dq[j]);
       const float xv = pro.xin(widen(xx[j]));
       float dx = dt * xv, wn = 0.0f;
       if constexpr (TR) {
@@ -511,6 +516,9 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
       if constexpr (MODE == kLocal && !SP) negbits |= __float_as_uint(dt);
 #pragma unroll
       for (int n = 0; n < NSTATE; ++n) h[n] = fmaf(fast_exp2(dt * a2[n]), h[n], dx * Bc[n]);
+      // The next token's B row goes into the registers this token's row
+      // held, while C . h and the epilogue run.
+      Bc.load(brow + (int64_t)std::min(bb + j + 1, nt - 1) * NSTATE);
       if constexpr (EMIT) {
         float acc = 0.0f;
 #pragma unroll
@@ -519,7 +527,6 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
           acc = fmaf(-wn, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbl), 8 * j)), acc);
         finish(ry, bb, j, acc, xv, widen(zz[j]));
       }
-      Bc = Bn;
       if constexpr (RMS) s_cur = s_next;
       // Keep each token's scalar B/C loads in its own token: hoisting them
       // across tokens would hold several rows in SGPRs at once and spill.
@@ -531,14 +538,12 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
     }
     if constexpr (MODE == kFix) {
       fsum += bsum;
-      // The part of the state pass 1 missed: exp(A * sum delta) * h_start,
-      // sum delta since the chunk start (exp2 of very negative arguments is 0).
-      float dm = 0.0f, hm = 0.0f;
+      // A bound on the part of the state pass 1 missed (exp2 of very
+      // negative arguments is 0); sum delta counts from the chunk start.
+      const float dm = fast_exp2(fix_a2 * fsum) * fix_h;
+      float hm = 0.0f;
 #pragma unroll
-      for (int n = 0; n < NSTATE; ++n) {
-        dm = fmaxf(dm, fast_exp2(a2[n] * fsum) * fabsf(hs[n]));
-        hm = fmaxf(hm, fabsf(h[n]));
-      }
+      for (int n = 0; n < NSTATE; ++n) hm = fmaxf(hm, fabsf(h[n]));
       // never before the point from which pass 1 wrote y
       const bool settled = can_exit && bb + kTok >= fix_from && dm <= hm * kSettled;    // false for NaN
       return __builtin_amdgcn_ballot_w64(!settled) == 0;
@@ -552,8 +557,6 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
   T dB[kTok], xB[kTok], zB[kTok], lB[kTok], dnB, lnB;
   Pair<T> pbA, pcA, pbB, pcB;
   load_block(0, dA, xA, zA, lA, dnA, lnA, pbA, pcA);
-  Bc.load(brow);
-  if constexpr (RMS) s_cur = load_uniform(srow);
   __builtin_amdgcn_s_waitcnt(0);
   // Prefetches past the chunk's end are clamped to its last block (valid rows,
   // values unused), so every row offset below stays non-negative.
@@ -568,6 +571,11 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
   auto pairs = [&](auto emit_tag) __attribute__((always_inline)) {
     constexpr bool EMIT = decltype(emit_tag)::value;
     for (; base < nt; base += 2 * kTok) {
+      // The pair's first B row (and RMSNorm scale) is loaded here, not
+      // carried over the loop's back edge: a row carried there is copied
+      // into VGPRs, 16 of them for fp32 rows.
+      Bc.load(brow + (int64_t)base * NSTATE);
+      if constexpr (RMS) s_cur = load_uniform(srow + base);
       if constexpr (MODE != kFix) prio.set(base);
       load_block(std::min(base + kTok, last), dB, xB, zB, lB, dnB, lnB, pbB, pcB);
       const bool settled = do_block(emit_tag, base, dA, xA, zA, lA, dnA, lnA, pbA, pcA);
