@@ -104,7 +104,7 @@ jscan_status jscan_prefill(int64_t batch, int64_t L, int64_t d_inner, int64_t d_
  * Same arguments and results as jscan_prefill without a workspace; the
  * chunked plan's records (per sequence, forward chunk and channel: 16 fp32
  * end states, a delta sum, a flag and 16 fp32 starting states, 136 bytes;
- * per sequence, chunk and 64-channel group a 4-byte token index; a 256-byte
+ * per sequence, chunk and 64-channel group two 4-byte token indices; a 256-byte
  * tag; each region rounded up to 256 bytes) live in a scratch
  * array of 64 MiB that the library holds on each GPU it runs on until the
  * process ends: batch * chunks * d_inner up to about 493 000 (at batch 1 and
@@ -336,21 +336,43 @@ const char* jscan_status_string(jscan_status status);
 const char* jscan_last_error(void);
 
 /*
- * Launch plan the prefill uses for these sizes: the number of waves that share
- * one group of 64 channels (each owning 16/waves states) and the number of
- * sequence chunks scanned in parallel (1 = single pass; more = chunk-local
- * pass, carry combine, and rescan).  Returns JSCAN_ERR_SHAPE for invalid sizes.
+ * Launch plan the prefill uses for these sizes (on the calling thread, after
+ * any override): the number of waves that share one group of 64 channels
+ * (always 1: one wave owns all 16 states of its 64 channels) and the number
+ * of sequence chunks scanned in parallel.  One chunk is a single pass; more
+ * is pass 1 (every chunk from a zero state, recording its end state), the
+ * carry combine, and pass 2 (chunks after the first rescanned from their true
+ * starting state until the carried-in part has decayed below fp32 resolution;
+ * the recurrence's Ā = exp(Δ·A) is the "Jamba lesson" "一页讲完 SSM" step).
+ * Returns JSCAN_ERR_SHAPE for invalid sizes.
  */
 jscan_status jscan_prefill_plan(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
                                 int* waves_per_group, int* chunks);
 
 /*
  * Override the launch plan for the prefill calls (and workspace sizes) of the
- * calling thread: waves_per_group in {1, 2, 4, 8}, chunks >= 1 (clamped to L).
- * (0, 0) restores the automatic plan.  Results do not depend on the plan
- * beyond floating-point rounding; this exists to test and tune every variant.
+ * calling thread: waves_per_group must be 1 and chunks in [1, 4096] (chunks
+ * longer than L - 1 tokens collapse to fewer); (0, 0) restores the automatic
+ * plan.  Results do not depend on the plan beyond floating-point rounding;
+ * this exists to test and tune every variant.  Any other pair returns
+ * JSCAN_ERR_UNSUPPORTED.
  */
 jscan_status jscan_set_plan_override(int waves_per_group, int chunks);
+
+/*
+ * How much of the work of a chunked prefill fell to which pass, read from the
+ * records the last prefill of these sizes left in `workspace` (a workspace
+ * passed to jscan_prefill or jscan_prefill_fused on this thread's current
+ * plan).  Synchronous: it copies the records to the host on `stream` and
+ * waits for them.  stats (host, 3 doubles): [0] the fraction of the tokens of
+ * chunks after the first that pass 1 scanned without writing y (before its
+ * predicted point of decay), [1] the fraction pass 2 rescanned, [2] the number
+ * of chunks.  A single-chunk plan gives 0, 0, 1.  JSCAN_ERR_WORKSPACE when the
+ * workspace is smaller than the plan's records or holds no records of a
+ * prefill of these sizes and plan; JSCAN_ERR_NULL, JSCAN_ERR_SHAPE as usual.
+ */
+jscan_status jscan_prefill_stats(const void* workspace, size_t workspace_bytes, int64_t batch, int64_t L,
+                                 int64_t d_inner, double* stats, void* stream);
 
 /*
  * Measurement hook.  When both events are non-NULL, the next jscan_prefill

@@ -44,7 +44,7 @@ EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_prefill_noall
            "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
            "jscan_set_plan_override", "jscan_time_next_prefill", "jscan_prefill_fused",
            "jscan_step_batch_fused", "jscan_backward_workspace_size", "jscan_backward", "jscan_prefill_trap",
-           "jscan_step_batch_trap", "jscan_backward_saved")
+           "jscan_step_batch_trap", "jscan_backward_saved", "jscan_prefill_stats")
 
 
 class Trap(ctypes.Structure):
@@ -110,6 +110,8 @@ def load_library(path: str = LIB_PATH):
         lib.jscan_set_plan_override.restype = st
         lib.jscan_time_next_prefill.argtypes = [vp, vp]
         lib.jscan_time_next_prefill.restype = None
+        lib.jscan_prefill_stats.argtypes = [vp, sz, i64, i64, i64, ctypes.POINTER(ctypes.c_double), vp]
+        lib.jscan_prefill_stats.restype = st
         pp = ctypes.POINTER(Prologue)
         lib.jscan_prefill_fused.argtypes = [i64, i64, i64, i64, st, vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, pp, vp,
                                             sz, vp]
@@ -190,6 +192,17 @@ def plan(batch, L, d_inner, d_state=D_STATE):
 def set_plan_override(waves_per_group=0, chunks=0):
     """Force the prefill's launch plan on this thread; (0, 0) restores the automatic one."""
     _check(load_library().jscan_set_plan_override(int(waves_per_group), int(chunks)))
+
+
+def prefill_stats(workspace, batch, L, d_inner, stream=None):
+    """(state-only fraction of pass 1, rescanned fraction of pass 2, chunks) of
+    the last chunked prefill of these sizes that used ``workspace`` (a device
+    uint8 tensor); the fractions are of the tokens of the chunks after the first."""
+    out = (ctypes.c_double * 3)()
+    _dev(workspace, "workspace")
+    _check(load_library().jscan_prefill_stats(_ptr(workspace), workspace.numel() * workspace.element_size(), batch,
+                                              L, d_inner, out, _stream(stream)))
+    return out[0], out[1], int(out[2])
 
 
 def time_next_prefill(before, after):

@@ -51,6 +51,7 @@
 #include <mutex>
 #include <string>
 #include <type_traits>
+#include <vector>
 
 #include "jscan.h"
 
@@ -366,7 +367,10 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
     settle_sum = a2max < 0.0f ? 24.0 / -(double)a2max : __builtin_inf();
   }
   // kFix: the first token from which pass 1 wrote y for this wave's channels
-  const int fix_from = MODE == kFix ? aux.from[(b * aux.chunks + (int64_t)blockIdx.y + 1) * aux.groups + blockIdx.x] : 0;
+  // progress record of this wave's (sequence, chunk, channel group): the
+  // token from which pass 1 wrote y, and the token where pass 2 stopped
+  int32_t* const prog = MODE == kWhole ? nullptr : aux.from + 2 * ((b * aux.chunks + c) * aux.groups + blockIdx.x);
+  const int fix_from = MODE == kFix ? prog[0] : 0;
   // kFix: the carry pass 1 missed is exp(A * sum delta) * h_start, at most
   // exp2(fix_a2 * sum delta) * fix_h with the slowest state's A' and the
   // largest |h_start|.
@@ -608,7 +612,13 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
   }
   if constexpr (MODE == kLocal) {
     if (lo == lane) aux.neg[(b * aux.chunks + c) * d_inner + d] = (negbits & 0x80000000u) ? 1 : 0;
-    if (lane == 0) aux.from[(b * aux.chunks + c) * aux.groups + blockIdx.x] = emit ? emit_from : nt;
+    if (lane == 0) {
+      prog[0] = emit ? emit_from : nt;
+      prog[1] = 0;
+    }
+  }
+  if constexpr (MODE == kFix) {
+    if (lane == 0) prog[1] = std::min(base + 2 * kTok, nt);
   }
   if constexpr (MODE == kWhole) {
     if (aux.hT && lo == lane) {
@@ -953,7 +963,7 @@ WsLayout ws_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
     w.eS = round_up(B * C * NSTATE * Dn * sizeof(float));
     w.eL = round_up(B * C * Dn * sizeof(float));
     w.neg = round_up(B * C * Dn * sizeof(int32_t));
-    w.from = round_up(B * C * (size_t)((d_inner + 63) / 64) * sizeof(int32_t));
+    w.from = round_up(B * C * (size_t)((d_inner + 63) / 64) * 2 * sizeof(int32_t));
     w.H = round_up(B * C * NSTATE * Dn * sizeof(float));
     if (p.subs > 1) {
       w.sS = round_up(B * (size_t)p.subs * NSTATE * Dn * sizeof(float));
@@ -1462,6 +1472,46 @@ jscan_status jscan_prefill_plan(int64_t batch, int64_t L, int64_t d_inner, int64
   const Plan p = choose_plan(batch, L, d_inner);
   if (waves_per_group) *waves_per_group = 1;
   if (chunks) *chunks = p.chunks;
+  return JSCAN_OK;
+}
+
+jscan_status jscan_prefill_stats(const void* workspace, size_t workspace_bytes, int64_t batch, int64_t L,
+                                 int64_t d_inner, double* stats, void* stream) {
+  if (!workspace || !stats) return fail(JSCAN_ERR_NULL, "workspace and stats are required");
+  if (!sizes_ok(batch, L, d_inner) || batch == 0 || L == 0 || d_inner == 0)
+    return fail(JSCAN_ERR_SHAPE, "invalid sizes");
+  const Plan p = choose_plan(batch, L, d_inner);
+  stats[0] = stats[1] = 0.0;
+  stats[2] = (double)p.chunks;
+  if (p.chunks <= 1) return JSCAN_OK;
+  const WsLayout w = ws_layout(batch, L, d_inner, p);
+  if (workspace_bytes < w.total) return fail(JSCAN_ERR_WORKSPACE, "workspace smaller than the plan's records");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Tag tag;
+  const int64_t groups = (d_inner + 63) / 64;
+  std::vector<int32_t> prog((size_t)(batch * p.chunks * groups * 2));
+  hipError_t e;
+  if ((e = hipMemcpyAsync(&tag, workspace, sizeof(tag), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+      (e = hipMemcpyAsync(prog.data(), static_cast<const char*>(workspace) + w.off_from(),
+                          prog.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+      (e = hipStreamSynchronize(st)) != hipSuccess)
+    return hip_fail(e, "copy of the progress records");
+  const Tag want = make_tag(batch, L, d_inner, p, 0);
+  for (int i = 0; i < 6; ++i)     // magic, sizes and plan; any variant
+    if (tag.w[i] != want.w[i]) return fail(JSCAN_ERR_WORKSPACE, "workspace holds no records of a prefill of these sizes");
+  double total = 0, state_only = 0, rescanned = 0;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int c = 1; c < p.chunks; ++c) {
+      const double nt = (double)std::min<int64_t>(p.chunk_len, L - (int64_t)c * p.chunk_len);
+      for (int64_t g = 0; g < groups; ++g) {
+        const int32_t* r = &prog[(size_t)(((b * p.chunks + c) * groups + g) * 2)];
+        total += nt;
+        state_only += r[0];
+        rescanned += r[1];
+      }
+    }
+  stats[0] = state_only / total;
+  stats[1] = rescanned / total;
   return JSCAN_OK;
 }
 

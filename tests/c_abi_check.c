@@ -27,7 +27,7 @@ int main(void) {
       (fn)&jscan_prefill_trap,           (fn)&jscan_step_batch_trap,  (fn)&jscan_backward_workspace_size,
       (fn)&jscan_backward,               (fn)&jscan_backward_saved,   (fn)&jscan_status_string,
       (fn)&jscan_last_error,             (fn)&jscan_prefill_plan,     (fn)&jscan_set_plan_override,
-      (fn)&jscan_time_next_prefill};
+      (fn)&jscan_time_next_prefill,      (fn)&jscan_prefill_stats};
   size_t i;
   int waves = 0, chunks = 0;
   for (i = 0; i < sizeof(entry) / sizeof(entry[0]); ++i) CHECK(entry[i] != NULL);
@@ -44,6 +44,10 @@ int main(void) {
                       NULL, 0, NULL) == JSCAN_ERR_UNSUPPORTED);
   CHECK(strlen(jscan_last_error()) > 0);
   CHECK(jscan_set_plan_override(3, 1) == JSCAN_ERR_UNSUPPORTED);
+  {
+    double stats[3];
+    CHECK(jscan_prefill_stats(NULL, 0, 1, 65536, 8192, stats, NULL) == JSCAN_ERR_NULL);
+  }
   printf("c abi ok: %d waves, %d chunks at 1 x 65536 x 8192\n", waves, chunks);
   return 0;
 }

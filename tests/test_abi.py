@@ -460,3 +460,22 @@ def test_prologue_rmsnorm_validation(lib):
     t = js.Trap()
     keys = ("batch", "L", "d_inner", "d_state", "io", "x", "delta", "A", "B", "C", "D", "z", "h0", "y", "hT")
     assert lib.jscan_prefill_trap(*(a[k] for k in keys), ctypes.byref(t), ctypes.byref(q), None, 0, None) == UNSUP
+
+
+def test_prefill_stats_arguments(lib):
+    """jscan_prefill_stats checks its arguments before it touches the workspace:
+    a single-chunk plan reads nothing, and a workspace smaller than the plan's
+    records is refused."""
+    ST = {v: k for k, v in js.STATUS_NAMES.items()}
+    out = (ctypes.c_double * 3)()
+    fake = ctypes.c_void_p(0x1000)       # never dereferenced on these paths
+    assert lib.jscan_prefill_stats(None, 0, 1, 65536, 8192, out, None) == ST["JSCAN_ERR_NULL"]
+    assert lib.jscan_prefill_stats(fake, 1 << 30, 1, 65536, 8192, None, None) == ST["JSCAN_ERR_NULL"]
+    assert lib.jscan_prefill_stats(fake, 1 << 30, -1, 65536, 8192, out, None) == ST["JSCAN_ERR_SHAPE"]
+    assert lib.jscan_prefill_stats(fake, 1 << 30, 1, 0, 8192, out, None) == ST["JSCAN_ERR_SHAPE"]
+    assert js.plan(1, 64, 128)[1] == 1
+    assert lib.jscan_prefill_stats(fake, 0, 1, 64, 128, out, None) == js.JSCAN_OK
+    assert tuple(out) == (0.0, 0.0, 1.0)
+    assert js.plan(1, 65536, 8192)[1] > 1
+    need = js.workspace_size(1, 65536, 8192) - rms_region(65536)
+    assert lib.jscan_prefill_stats(fake, need - 1, 1, 65536, 8192, out, None) == ST["JSCAN_ERR_WORKSPACE"]

@@ -216,15 +216,43 @@ def test_carry_that_does_not_settle(case, chunks):
     inp = _decay_case(case, synth.prefill_inputs(2, 3000, 200, seed=80, io=synth.IO_BF16, h0=True))
     t = to_device(inp)
     yr, hr = oracle_full(inp)
+    ws = torch.empty(js.workspace_size(2, 3000, 200), dtype=torch.uint8, device="cuda")
     try:
         if chunks:
             js.set_plan_override(1, chunks)
         assert js.plan(2, 3000, 200)[1] > 1
-        y, hT = run_prefill(t)
+        y, hT = run_prefill(t, workspace=ws)
+        state_only, rescanned, n = js.prefill_stats(ws, 2, 3000, 200)
     finally:
         js.set_plan_override(0, 0)
     assert_y(y, yr, bf16=True)
     assert_state(hT, hr, "hT")
+    # pass 2 never stops before the token from which pass 1 wrote y
+    assert n > 1 and 0.0 <= state_only <= rescanned <= 1.0
+    if case != "negdt":     # no state-only prefix can be predicted to decay: whole chunks
+        assert state_only == 1.0 and rescanned == 1.0
+
+
+def test_pass_work_fractions_fast_decay():
+    """With the workloads' time steps (softplus(N(0,1) - 2)) and A in [-16, -1]
+    the carry decays within about a hundred tokens: pass 1 writes y for most
+    of each chunk and pass 2 rescans only a prefix (batch 1 x 8192 x 512,
+    forced 8 chunks of 1024 tokens), and y matches the oracle."""
+    print_case("pass work fractions, fast decay")
+    inp = synth.prefill_inputs(1, 8192, 512, seed=5, io=synth.IO_BF16)
+    t = to_device(inp)
+    yr, hr = oracle_full(inp, use_h0=False)
+    ws = torch.empty(js.workspace_size(1, 8192, 512), dtype=torch.uint8, device="cuda")
+    try:
+        js.set_plan_override(1, 8)
+        y, hT = run_prefill(t, h0=False, workspace=ws)
+        state_only, rescanned, n = js.prefill_stats(ws, 1, 8192, 512)
+    finally:
+        js.set_plan_override(0, 0)
+    assert_y(y, yr, bf16=True)
+    assert_state(hT, hr, "hT")
+    print(f"state-only {state_only:.3f}, rescanned {rescanned:.3f} of chunks 1..{n - 1}", flush=True)
+    assert n == 8 and 0.0 < state_only <= rescanned < 0.5
 
 
 def test_nan_stays_in_its_channel():
