@@ -455,6 +455,7 @@ def run_all_configs(log):
     prefill_cases = [("jamba prefill batch 2 x 4096", 2, 4096, 1), ("64K context batch 1", 1, 65536, 2),
                      ("256K context batch 1 (single call)", 1, 262144, 2)]
     for name, batch, L, seed in prefill_cases:
+        log(f"[all-configs] generating {name}")
         inp = synth.prefill_inputs(batch, L, 8192, seed=seed)
         x, dl, z, B, C = (dio(inp[k]) for k in ("x", "delta", "z", "B", "C"))
         A, D = dio(inp["A"]), dio(inp["D"])
@@ -493,6 +494,7 @@ def run_all_configs(log):
     # hybrid block: seven independent Mamba layers, batch 8 x 16384
     layers = []
     for l in range(7):
+        log(f"[all-configs] generating hybrid-block layer {l}")
         inp = synth.prefill_inputs(8, 16384, 8192, seed=40 + l)
         layers.append(tuple(dio(inp[k]) for k in ("x", "delta", "z", "B", "C", "A", "D")))
         if l == 0:
