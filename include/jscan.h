@@ -142,6 +142,11 @@ jscan_status jscan_step(int64_t d_inner, int64_t d_state, jscan_io io, float* st
  *   state : [n_seq][d_inner][d_state] fp32
  *   x, delta, z, y : [n_seq][d_inner] (io);  B, C : [n_seq][d_state] (io)
  *   A, D shared by all sequences, as above.
+ *
+ * n_seq * d_inner may be at most 2^30 - 64 (a 64 GiB state): the step runs
+ * four lanes per (sequence, channel) in a one-dimensional grid, which holds at
+ * most 2^32 work-items.  Larger products, and negative sizes, return
+ * JSCAN_ERR_SHAPE before any GPU work; so do the fused and trapezoidal steps.
  */
 jscan_status jscan_step_batch(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
                               float* state, const void* x, const void* delta, const float* A,

@@ -479,3 +479,31 @@ def test_prefill_stats_arguments(lib):
     assert js.plan(1, 65536, 8192)[1] > 1
     need = js.workspace_size(1, 65536, 8192) - rms_region(65536)
     assert lib.jscan_prefill_stats(fake, need - 1, 1, 65536, 8192, out, None) == ST["JSCAN_ERR_WORKSPACE"]
+
+
+def test_step_size_limit(lib):
+    """The decode step's one-dimensional grid (four lanes per sequence-channel)
+    holds at most 2^32 work-items: n_seq * d_inner up to 2^30 - 64 passes the
+    size check (and then fails on the NULL pointers, before any GPU work), one
+    more is JSCAN_ERR_SHAPE, for the plain, fused and trapezoidal steps."""
+    ST = {v: k for k, v in js.STATUS_NAMES.items()}
+    limit = (1 << 30) - 64
+    args = [None] * 9 + [None]
+
+    def plain(n, d):
+        return lib.jscan_step_batch(n, d, 16, js.IO_BF16, *args)
+
+    def fused(n, d):
+        return lib.jscan_step_batch_fused(n, d, 16, js.IO_BF16, *([None] * 9), None, None)
+
+    def trap(n, d):
+        return lib.jscan_step_batch_trap(n, d, 16, js.IO_BF16, *([None] * 9), None, None, None)
+
+    for call in (plain, fused, trap):
+        assert call(1, limit) == ST["JSCAN_ERR_NULL"]
+        assert call(1, limit + 1) == ST["JSCAN_ERR_SHAPE"]
+        assert call(limit // 8192 + 1, 8192) == ST["JSCAN_ERR_SHAPE"]
+        assert call(-1, 8192) == ST["JSCAN_ERR_SHAPE"]
+        assert call(1 << 40, 1 << 40) == ST["JSCAN_ERR_SHAPE"]      # the product overflows
+    # jscan_step is the one-sequence case of the same check
+    assert lib.jscan_step(limit + 1, 16, js.IO_BF16, *([None] * 9), None) == ST["JSCAN_ERR_SHAPE"]
