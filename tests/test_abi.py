@@ -507,3 +507,27 @@ def test_step_size_limit(lib):
         assert call(1 << 40, 1 << 40) == ST["JSCAN_ERR_SHAPE"]      # the product overflows
     # jscan_step is the one-sequence case of the same check
     assert lib.jscan_step(limit + 1, 16, js.IO_BF16, *([None] * 9), None) == ST["JSCAN_ERR_SHAPE"]
+
+
+def test_ubench_library_exports_its_header():
+    """libjscan_ubench.so (the VALU measurement library bench.py loads) exports
+    every function include/jscan_ubench.h declares, with C linkage."""
+    path = os.path.join(os.path.dirname(js.LIB_PATH), "libjscan_ubench.so")
+    if not os.path.exists(path):
+        from selective_state_space_11_amd import build
+        build.build()
+    text = open(os.path.join(os.path.dirname(HEADER), "jscan_ubench.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(jscan_[a-z_]+)\s*\(", text)))
+    assert names == ["jscan_ubench_valu"]
+    ub = ctypes.CDLL(path)
+    for name in names:
+        assert hasattr(ub, name), name
+    # argument checks return before any GPU work
+    d = ctypes.c_double()
+    fn = ub.jscan_ubench_valu
+    fn.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int] + [ctypes.POINTER(ctypes.c_double)] * 5
+    ptrs = [ctypes.byref(d)] * 5
+    assert fn(9, 4, 1, *ptrs) == 1          # unknown kind
+    assert fn(0, 6, 1, *ptrs) == 1          # waves not a multiple of 4
+    assert fn(0, 4, 0, *ptrs) == 1          # no iterations
