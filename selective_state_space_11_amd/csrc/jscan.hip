@@ -109,17 +109,36 @@ __device__ __forceinline__ void write_record(float* __restrict__ S, float* __res
 // token `end`: the chunk's end record when the block ends the chunk, and the
 // record of sub-chunk s when the block ends at the sub-chunk boundary
 // (s + 1) * sub_len inside the sequence.
+// The next sub-chunk boundary after a wave's position and the record slot it
+// fills.  Chunk starts and sub-chunk lengths are multiples of the block
+// length, so every boundary is a block end; the cursor moves on by one
+// sub-chunk at each (no division in the token loop).
+struct SubCursor {
+  int next;        // chunk-local token of the next boundary (INT32_MAX: none)
+  int slot;        // its record slot
+  int step;        // the sub-chunk length
+  bool seq_end;    // the chunk ends the sequence (no boundary at its end)
+};
+
 struct Records {
   float* eS; float* eL;        // [b][chunks][16][d], [b][chunks][d]
   float* sS; float* sL;        // [b][subs][16][d], [b][subs][d], or null (one sub-chunk)
   int64_t sub_len;
   int chunks, subs;
-  __device__ __forceinline__ void after_block(int end, int nt, int64_t t0, int64_t L, int64_t b, int c,
-                                              const float (&h)[NSTATE], double dacc, int64_t d_inner,
-                                              int64_t gbase, bool real, uint32_t lb4) const {
-    const int64_t g = t0 + end;                    // global token the block ends at (exclusive)
-    if (sS && g < L && g % sub_len == 0 && real)
-      write_record(sS, sL, h, dacc, b * subs + g / sub_len - 1, d_inner, gbase, lb4);
+  __device__ __forceinline__ SubCursor cursor(int64_t t0, int nt, int64_t L, int64_t b) const {
+    if (!sS) return SubCursor{INT32_MAX, 0, 0, false};
+    const int64_t k = t0 / sub_len + 1;            // the first boundary after t0
+    return SubCursor{(int)(k * sub_len - t0), (int)(b * subs + k - 1), (int)sub_len, t0 + nt >= L};
+  }
+  // After the block ending at chunk-local token `end` (exclusive).
+  __device__ __forceinline__ void after_block(int end, int nt, int64_t b, int c, const float (&h)[NSTATE],
+                                              double dacc, int64_t d_inner, int64_t gbase, bool real,
+                                              uint32_t lb4, SubCursor& cur) const {
+    if (end == cur.next) {
+      if (real && !(end >= nt && cur.seq_end)) write_record(sS, sL, h, dacc, cur.slot, d_inner, gbase, lb4);
+      cur.next += cur.step;
+      ++cur.slot;
+    }
     if (end >= nt && real) write_record(eS, eL, h, dacc, b * chunks + c, d_inner, gbase, lb4);
   }
 };
@@ -178,6 +197,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ x, co
   const uint32_t rowb = (uint32_t)(d_inner * sizeof(T));
   const int last = (nt - 1) / kTok * kTok;
   const ProgressPrio prio(nt);
+  SubCursor cur = rec.cursor(t0, nt, L, b);
 
   auto load_block = [&](int bb, T (&dd)[kTok], T (&xx)[kTok]) {
     const int64_t o = (int64_t)bb * d_inner;
@@ -204,7 +224,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ x, co
       __builtin_amdgcn_sched_barrier(0);
     }
     dacc += (double)bsum;
-    rec.after_block(bb + kTok, nt, t0, L, b, c, h, dacc, d_inner, gbase, lo == lane, (uint32_t)lo * 4);
+    rec.after_block(bb + kTok, nt, b, c, h, dacc, d_inner, gbase, lo == lane, (uint32_t)lo * 4, cur);
   };
   T dA[kTok], xA[kTok], dB[kTok], xB[kTok];
   load_block(0, dA, xA);
@@ -394,6 +414,8 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
 
   const int64_t t0 = (int64_t)c * aux.chunk_len;
   const int nt = (int)std::min<int64_t>(aux.chunk_len, L - t0);   // >= 1 for every chunk
+  SubCursor sub_cur{};               // kLocal: the next sub-chunk record
+  if constexpr (MODE == kLocal) sub_cur = aux.rec.cursor(t0, nt, L, b);
   const int64_t row0 = (b * L + t0) * d_inner + gbase;
   const T* xrow = x + row0;
   const T* drow = delta + row0;
@@ -441,6 +463,9 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
     const int64_t o = (int64_t)bb * d_inner;
     const auto rd = rsrc(drow + o), rx = rsrc(xrow + o), rz = rsrc(zrow + o), r0 = rsrc(drow, 0);
     const auto rl = TR && pa.lam ? rsrc(lrow + o) : r0;
+    // Token by token, so that a token's loads are consumed in issue order and
+    // its wait covers only the loads before it (the barrier keeps the
+    // compiler from regrouping them by stream).
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
       const uint32_t so = (uint32_t)(std::min(bb + j, nt - 1) - bb) * rowb;
@@ -448,6 +473,7 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
       buf_load(xx[j], rx, lb, so);
       buf_load(zz[j], rz, lb, so);
       if constexpr (TR) buf_load(ll[j], rl, lb, so);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (TR) {
       const bool next = t0 + bb + kTok < L;
@@ -538,7 +564,7 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
     }
     if constexpr (MODE == kLocal) {
       dacc += (double)bsum;
-      aux.rec.after_block(bb + kTok, nt, t0, L, b, c, h, dacc, d_inner, gbase, lo == lane, (uint32_t)lo * 4);
+      aux.rec.after_block(bb + kTok, nt, b, c, h, dacc, d_inner, gbase, lo == lane, (uint32_t)lo * 4, sub_cur);
     }
     if constexpr (MODE == kFix) {
       fsum += bsum;
