@@ -430,7 +430,7 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
     brow = Bm + (b * L + t0) * NSTATE;
     crow = Cm + (b * L + t0) * NSTATE;
   }
-  // RMSNorm: delta * w[d] * s[t], s read a token ahead like the B row
+  // RMSNorm: delta * w[d] * s[t], s of the next token loaded during the token before it
   const float* srow = RMS ? pa.rms_s + b * L + t0 : nullptr;
   const float wdt = RMS && pa.rms_w ? pa.rms_w[d] : 1.0f;
   float s_cur = 1.0f, s_next = 1.0f;
@@ -486,8 +486,9 @@ __global__ __launch_bounds__(64, (scan_waves<T, CONV, SP, TR, RMS, MODE>())) voi
     }
   };
 
-  // B of the next token is prefetched a token ahead; C is needed only after
-  // the token's state updates, so it is loaded at the token's start.
+  // A token's B row is loaded during the token before it (right after that
+  // token's state update, into the same registers); C is needed only after
+  // the state updates, so it is loaded at the token's start.
   Row<RT, NSTATE> Bc, Cv;
   double dacc = 0.0;                 // kLocal: delta sum since the chunk start
   float fsum = 0.0f;                 // kFix: delta sum since the chunk start
