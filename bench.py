@@ -20,7 +20,8 @@ sources, else null.
 
 Further legs (each printed inside the same JSON line): the decode step of 256
 sequences at HBM (seven 128 MiB state pools stepped in turn with fresh
-inputs) and with its state resident in the last-level cache, the prefill with
+inputs; also with the fused prologue and with the trapezoidal recurrence)
+and with its state resident in the last-level cache, the prefill with
 the fused input prologue, with RMSNorm, with the exponential-trapezoidal
 recurrence, the backward scan, and the fp64 CPU oracle on a bounded sample.
 
@@ -67,6 +68,18 @@ def alg_bytes_prefill(batch, L, d_inner, io_bytes=2, h0=False, hT=True):
 def alg_bytes_step(n_seq, d_inner, io_bytes=2):
     return (2 * n_seq * d_inner * D_STATE * 4 + n_seq * d_inner * io_bytes * 4
             + n_seq * D_STATE * io_bytes * 2 + d_inner * D_STATE * 4 + d_inner * 4)
+
+
+def alg_bytes_step_fused(n_seq, d_inner, width=4, io_bytes=2):
+    """The decode step with the prologue: the conv history (width - 1 fp32 per
+    sequence-channel) read and written, the conv weights and bias, dt_bias."""
+    return (alg_bytes_step(n_seq, d_inner, io_bytes) + 2 * n_seq * d_inner * (width - 1) * 4
+            + d_inner * (width + 2) * 4)
+
+
+def alg_bytes_step_trap(n_seq, d_inner, io_bytes=2):
+    """The trapezoidal decode step: lam and the previous token's x and B as well."""
+    return alg_bytes_step(n_seq, d_inner, io_bytes) + 2 * n_seq * d_inner * io_bytes + n_seq * D_STATE * io_bytes
 
 
 def source_digest():
@@ -550,6 +563,40 @@ def bench_decode(torch, js, synth, dio, dev, copy_gbs, log, n_pools=7, n_sets=32
                            "frac_of_measured_copy": round(gbs / copy_gbs, 4),
                            "traffic": traffic["hbm_bytes_per_launch"] if traffic else None}}
     log(f"[bench] decode at HBM {us_step:.2f} us/step ({gbs:.0f} GB/s)")
+
+    # The fused step (conv width 4 + SiLU with each layer's own conv history,
+    # softplus(delta + dt_bias)) and the trapezoidal step (lam per
+    # sequence-channel, the previous step's x and B), at HBM like the above.
+    pro = synth.prologue_params(d_inner, 4, seed=3, batch=n_seq)
+    cw, cb, dtb = (torch.from_numpy(pro[k]).to(dev) for k in ("conv_weight", "conv_bias", "dt_bias"))
+    hists = [torch.from_numpy(pro["conv_state"]).to(dev).clone() for _ in range(n_pools)]
+
+    def fused_run():
+        for k in range(steps):
+            dx, dd, dz, dB, dC = sets[k % n_sets]
+            js.step_batch_fused(pools[k % n_pools], dx, dd, Ad, dB, dC, Dd, dz, conv_weight=cw, conv_bias=cb,
+                                conv_state=hists[k % n_pools], dt_bias=dtb, softplus=True, y=yd)
+    us_fused = _timed(torch, fused_run, 1, warm_s=0.0) * 1e3 / steps
+    lam = dio(synth.trap_inputs(n_seq, 1, d_inner, seed=3)[0][:, 0, :])
+
+    def trap_run():
+        for k in range(steps):
+            dx, dd, dz, dB, dC = sets[k % n_sets]
+            px, _, _, pB, _ = sets[(k - 1) % n_sets]
+            js.step_batch_trap(pools[k % n_pools], dx, dd, Ad, dB, dC, Dd, dz, lam=lam, x_prev=px, B_prev=pB, y=yd)
+    us_trap = _timed(torch, trap_run, 1, warm_s=0.0) * 1e3 / steps
+    fb, tb = alg_bytes_step_fused(n_seq, d_inner), alg_bytes_step_trap(n_seq, d_inner)
+    decode["fused_prologue"] = {"workload": "the same steps with conv width 4 + SiLU (each pool with its own conv "
+                                            "history, updated in place) and softplus(delta + dt_bias)",
+                                "us_per_step": round(us_fused, 3),
+                                "alg_GBps": round(fb / (us_fused * 1e-6) / 1e9, 1),
+                                "frac_of_hbm_peak": round(fb / (us_fused * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    decode["trapezoidal"] = {"workload": "the same steps with the exponential-trapezoidal recurrence",
+                             "us_per_step": round(us_trap, 3),
+                             "alg_GBps": round(tb / (us_trap * 1e-6) / 1e9, 1),
+                             "frac_of_hbm_peak": round(tb / (us_trap * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del hists, lam
+    log(f"[bench] decode at HBM: fused prologue {us_fused:.2f} us/step, trapezoidal {us_trap:.2f} us/step")
 
     # cache-resident: 128 of the sequences (a 64 MiB state) with one input set
     # replayed, so that state and inputs stay in the 256 MB last-level cache
