@@ -504,6 +504,37 @@ def run_all_configs(log):
         del x, dl, z, y, inp
         torch.cuda.empty_cache()
 
+    # decode: 256 sequences, 1024 steps with per-step seeded inputs (32
+    # input sets in turn over seven 128 MiB state pools, as in the default
+    # run), and the oracle's decode rate on 256 channels of every sequence
+    # over the first 16 steps
+    n_seq = 256
+    st_np = synth.decode_state(n_seq, 8192, seed=3)
+    A_np, D_np, _ = synth.params(8192, seed=3)
+    chans = np.linspace(0, 8191, 256).astype(int)
+    s64 = st_np[:, chans].astype(np.float64)
+    A64, D64 = A_np[chans].astype(np.float64), D_np[chans].astype(np.float64)
+    toks = []
+    for k in range(16):
+        di = synth.decode_inputs(n_seq, 8192, seed=3, step=k)
+        toks.append([synth.widen(di[n][..., chans]) if n in ("x", "delta", "z") else synth.widen(di[n])
+                     for n in ("x", "delta", "z", "B", "C")])
+    t0 = time.time()
+    for (ox, od, oz, oB, oC) in toks:
+        _, s64 = oracle.step(s64, ox, od, A64, oB, oC, D64, oz)
+    cpu_dec = n_seq * len(chans) * len(toks) / (time.time() - t0)
+    del toks, st_np
+    csrc = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    copy_gbs = 2 * csrc.numel() * 4 / (_timed(torch, lambda: cdst.copy_(csrc), 10) * 1e-3) / 1e9
+    del csrc, cdst
+    dec = bench_decode(torch, js, synth, dio, dev, copy_gbs, log)
+    emit("decode 256 sequences x 1024 steps (fresh inputs, seven 128 MiB state pools)", n_seq * 8192 * 1024,
+         dec["us_per_step"] * 1024e-3, 1024 * alg_bytes_step(n_seq, 8192), cpu_dec,
+         {"us_per_step": dec["us_per_step"], "fused_prologue_us_per_step": dec["fused_prologue"]["us_per_step"],
+          "trapezoidal_us_per_step": dec["trapezoidal"]["us_per_step"],
+          "cache_resident_128_seq_us_per_step": dec["cache_resident"]["us_per_step"]})
+
     # hybrid block: seven independent Mamba layers, batch 8 x 16384
     layers = []
     for l in range(7):
@@ -651,8 +682,8 @@ def main():
     ap.add_argument("--leg-steps", type=int, default=10, help="timed calls of each further prefill leg")
     ap.add_argument("--backward-steps", type=int, default=5, help="timed backward calls (0: skip)")
     ap.add_argument("--all-configs", action="store_true",
-                    help="time every workload (batch 2 x 4K, 64K, 256K single and chained, 7-layer hybrid "
-                         "block) with the oracle on a sample; one JSON line each")
+                    help="time every workload (batch 2 x 4K, 64K, 256K single and chained, decode of 256 "
+                         "sequences, 7-layer hybrid block) with the oracle on a sample; one JSON line each")
     ap.add_argument("--valu-ceiling", action="store_true",
                     help="only measure the VALU rates of this GPU for the scan's instruction mixes "
                          "(libjscan_ubench.so); --out writes a summary (and a .json beside it)")
