@@ -134,3 +134,23 @@ def test_prefill_million_tokens_bit_exact():
     expect = torch.zeros_like(hT)
     expect[:, :, int(n_star(torch.tensor(L - 1)))] = x[:, L - 1, :].float()
     assert torch.equal(hT, expect)
+
+
+def test_decode_many_sequences():
+    """70002 sequences (more than the prefill's largest batch) x d_inner 72
+    (not a multiple of 64): y and the state after one step against the
+    oracle's decode step."""
+    n_seq, d = 70002, 72
+    print_case(f"decode {n_seq} sequences x {d}")
+    st_np = synth.decode_state(n_seq, d, seed=79)
+    A_np, D_np, _ = synth.params(d, seed=79)
+    tok = synth.decode_inputs(n_seq, d, seed=79, step=0)
+    state = torch.from_numpy(st_np).cuda()
+    y = js.step_batch(state, *(dev_io(tok[k]) for k in ("x", "delta")), torch.from_numpy(A_np).cuda(),
+                      dev_io(tok["B"]), dev_io(tok["C"]), torch.from_numpy(D_np).cuda(), dev_io(tok["z"]))
+    torch.cuda.synchronize()
+    yr, sr = oracle.step(st_np.astype(np.float64), *(synth.widen(tok[k]) for k in ("x", "delta")),
+                         A_np.astype(np.float64), synth.widen(tok["B"]), synth.widen(tok["C"]),
+                         D_np.astype(np.float64), synth.widen(tok["z"]))
+    assert_y(y, yr, bf16=True, what="decode y")
+    assert_state(state, sr, "state after decode")
