@@ -1,6 +1,6 @@
 """HIP-graph capture of libjscan calls (torch.cuda.CUDAGraph): decode steps,
-fused decode steps, a chunked prefill, the trapezoidal prefill and the
-backward, given caller workspaces, launch only kernels on the caller's
+fused decode steps, a chunked prefill, the fused prefill with RMSNorm, the
+trapezoidal prefill and the backward, given caller workspaces, launch only kernels on the caller's
 stream, so they can be captured once and replayed.
 
 Each graph is replayed several times from the same starting state, with eager
@@ -167,5 +167,47 @@ def test_backward_and_trapezoidal_prefill_replayed():
             for k in g_ref:
                 assert torch.equal(g[k], g_ref[k]), (rep, k)
             assert torch.equal(y, y_ref) and torch.equal(hT, h_ref), rep
+    finally:
+        js.set_plan_override(0, 0)
+
+
+def test_fused_rmsnorm_prefill_replayed():
+    """The prefill with the whole prologue (conv width 4 + SiLU, softplus, and
+    RMSNorm of delta, B and C) given a caller workspace, in a forced 4-chunk
+    plan: the RMSNorm pre-pass writes its per-token region inside the
+    workspace, so the call allocates nothing and replays bit for bit."""
+    print_case("graph fused prefill with RMSNorm chunks=4")
+    b, L, d = 2, 1000, 256
+    inp = synth.prefill_inputs(b, L, d, seed=93, io=synth.IO_BF16, h0=True)
+    t = to_device(inp)
+    pro = synth.prologue_params(d, 4, seed=93, batch=b)
+    cw, cb, cs, dtb = (torch.from_numpy(pro[k]).cuda() for k in ("conv_weight", "conv_bias", "conv_state",
+                                                                 "dt_bias"))
+    rms = tuple(torch.from_numpy(w).cuda() for w in synth.rms_weights(d, seed=93)) + (1e-5,)
+    try:
+        js.set_plan_override(1, 4)
+        ws = torch.empty(js.workspace_size(b, L, d), dtype=torch.uint8, device="cuda")
+        cso_ref = torch.empty_like(cs)
+
+        def call(y=None, hT=None, cso=cso_ref):
+            return js.prefill_fused(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], y=y,
+                                    hT=hT, workspace=ws, conv_weight=cw, conv_bias=cb, conv_state_in=cs,
+                                    conv_state_out=cso, dt_bias=dtb, softplus=True, rms=rms)
+        y_ref, h_ref = call()
+        torch.cuda.synchronize()
+        y, hT, cso = torch.empty_like(y_ref), torch.empty_like(h_ref), torch.empty_like(cs)
+        g = capture(lambda: call(y, hT, cso))
+        for rep in range(REPLAYS):
+            y.zero_()
+            hT.zero_()
+            cso.zero_()
+            ws.zero_()
+            js.prefill(t["x"][:1], t["delta"][:1], t["A"], t["B"][:1], t["C"][:1], t["D"], t["z"][:1])
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_ref), rep
+            assert torch.equal(hT, h_ref), rep
+            assert torch.equal(cso, cso_ref), rep
     finally:
         js.set_plan_override(0, 0)
