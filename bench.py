@@ -82,11 +82,36 @@ def alg_bytes_step_trap(n_seq, d_inner, io_bytes=2):
     return alg_bytes_step(n_seq, d_inner, io_bytes) + 2 * n_seq * d_inner * io_bytes + n_seq * D_STATE * io_bytes
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed (a comment
+    does not change a kernel)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] in "\"'":                     # string and character literals pass through
+            q, j = text[i], i + 1
+            while j < n and text[j] != q:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest():
-    """Digest of the sources the forward kernels and their plan are compiled from."""
+    """Digest of the code (comments aside) the forward kernels and their plan
+    are compiled from."""
     h = hashlib.sha256()
     for f in ("jscan.hip", "common.h", "host.h"):
-        h.update(open(os.path.join(ROOT, "selective_state_space_11_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "selective_state_space_11_amd", "csrc", f), encoding="utf-8").read()
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -16,25 +16,28 @@
 //   are widened by a scalar shift or mask) and fed to the VALU as scalar
 //   operands, with no LDS traffic and no VGPRs.
 // * The scan is bound by the fp32 VALU, not by HBM: per channel-token it
-//   moves 8 bytes but issues about 92 VALU instructions (16 decays exp2 and
+//   moves 8 bytes but issues about 93 VALU instructions (16 decays exp2 and
 //   4 plain operations per state, plus the epilogue).  The chip therefore
 //   needs every SIMD busy, and at batch 1 the 8192 channels are only 128
 //   waves: the sequence is cut into chunks scanned in parallel.
 // * Chunked prefill, two passes and a combine:
-//   - pass 1 scans every chunk from a zero state (chunk 0 from h0), writes
-//     y, and records the chunk-local state and the delta sum at the end of
-//     each sub-chunk (the last record of a chunk is its end);
+//   - pass 1 scans every chunk from a zero state (chunk 0 from h0) and
+//     records the chunk-local state and the delta sum at the end of each
+//     sub-chunk (the last record of a chunk is its end).  The part of a later
+//     chunk's state it misses is the carried-in state decayed by
+//     exp(A * sum delta), at most exp2(A'max * sum delta) * |h_start| for the
+//     slowest state: once sum delta reaches 24 / |A'max| in every lane of the
+//     wave that is below fp32 resolution, so pass 1 scans state-only up to
+//     that token and writes y from it on (chunk 0, being exact, writes all);
 //   - the combine folds the chunks' (decay, end state) pairs in order,
 //     h <- exp2(A' * sum delta) * h + S, giving each chunk's true starting
 //     state and the final state;
-//   - pass 2 rescans each later chunk from its true starting state while
-//     carrying the part of the state that pass 1 missed, d = exp(A * sum
-//     delta) * h_start (one multiply per state: the decays are shared), and
-//     stops as soon as that part is below fp32 resolution of the state in
-//     every lane of the wave; pass 1's outputs stand for the rest of the
-//     chunk.  The carried part only decays when A <= 0 and delta >= 0, so a
-//     wave that sees A > 0 or a chunk with a negative time step rescans its
-//     whole chunk.
+//   - pass 2 rescans each later chunk from its true starting state and writes
+//     y, until the same bound, now with the true |h_start|, is below fp32
+//     resolution of the state in every lane of the wave, and never before the
+//     token from which pass 1 wrote y.  The carried part only decays when
+//     A <= 0 and delta >= 0, so a wave that sees A > 0, or a chunk with a
+//     negative time step, rescans its whole chunk.
 // * exp(delta*A) is computed as exp2(delta * (A*log2 e)), with A*log2 e
 //   formed once per call in registers.
 //
@@ -340,7 +343,8 @@ struct ScanAux {
   float* hT;              // kWhole
   Records rec;            // kLocal: chunk-end and sub-chunk records
   int32_t* neg;           // kLocal writes, kFix reads: a negative time step in [b][chunk][d]
-  int32_t* from;          // kLocal writes, kFix reads: first token pass 1 wrote y for, [b][chunk][group]
+  int32_t* from;          // progress records [b][chunk][group][2]: the first token pass 1 wrote y for
+                          // (kLocal writes, kFix reads) and the token where pass 2 stopped (kFix)
   const float* H;         // kFix: chunk starting states [b][chunk][n][d]
   int64_t L, d_inner, chunk_len;
   int chunks, groups;

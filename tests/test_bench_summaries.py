@@ -100,3 +100,13 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_code_digest_ignores_comments_only():
+    """The counters in profiles/traffic.json stay valid across comment edits of
+    the kernel sources and lapse on any change to the code itself."""
+    code = 'h[n] = fmaf(e, h[n], dx * B[n]);  // state\n/* a note */ const char* s = "// kept";\n'
+    assert bench._code_only(code) == bench._code_only(code.replace("// state", "// the state update"))
+    assert bench._code_only(code) == bench._code_only(code.replace("/* a note */", "/* another\n note */"))
+    assert bench._code_only(code) != bench._code_only(code.replace("dx * B[n]", "dx * C[n]"))
+    assert bench._code_only(code) != bench._code_only(code.replace('"// kept"', '"// changed"'))
