@@ -598,3 +598,25 @@ def test_random_shapes_and_plans(case):
         js.set_plan_override(0, 0)
     assert_y(y, yr, bf16=c["io"] == synth.IO_BF16)
     assert_state(hT, hr, "hT")
+
+
+def test_prefill_stats_refuse_a_workspace_of_other_sizes():
+    """jscan_prefill_stats reads the tag a chunked prefill left in the
+    workspace and refuses records written for other sizes (or none)."""
+    print_case("prefill stats, foreign workspace")
+    inp = synth.prefill_inputs(1, 2048, 128, seed=17, io=synth.IO_BF16)
+    t = to_device(inp)
+    try:
+        js.set_plan_override(1, 4)
+        ws = torch.zeros(js.workspace_size(1, 4096, 128), dtype=torch.uint8, device=DEV)
+        with pytest.raises(js.JscanError) as e:          # nothing written yet: no tag
+            js.prefill_stats(ws, 1, 2048, 128)
+        assert "JSCAN_ERR_WORKSPACE" in str(e.value)
+        run_prefill(t, h0=False, workspace=ws)
+        state_only, rescanned, n = js.prefill_stats(ws, 1, 2048, 128)
+        assert n == 4 and 0.0 <= state_only <= rescanned <= 1.0
+        with pytest.raises(js.JscanError) as e:          # records of 1 x 2048 x 128, asked as 1 x 4096 x 128
+            js.prefill_stats(ws, 1, 4096, 128)
+        assert "JSCAN_ERR_WORKSPACE" in str(e.value)
+    finally:
+        js.set_plan_override(0, 0)
