@@ -831,7 +831,7 @@ def main():
     # first.  Run as batch 2 x L/2 (the same channel-tokens and chunk length)
     # so that its kernels have a grid of their own in a kernel trace.
     A0 = torch.zeros_like(A)
-    wb, wL = 2 * batch, L // 2
+    wb, wL = (2 * batch, L // 2) if L % 2 == 0 else (batch, L)
     xw, dw, zw, Bw, Cw = (t.view(wb, wL, -1) for t in (x, delta, z, B, C))
     yw, hw = y.view(wb, wL, -1), torch.empty(wb, d_inner, D_STATE, device=dev)
     wws = torch.empty(max(1, js.workspace_size(wb, wL, d_inner)), dtype=torch.uint8, device=dev)
