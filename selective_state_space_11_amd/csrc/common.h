@@ -142,6 +142,30 @@ __device__ __forceinline__ const __attribute__((address_space(4))) V* uniform_pt
   return (const __attribute__((address_space(4))) V*)(uintptr_t)u;
 }
 
+// A wave-uniform pointer the compiler cannot see through: it can then no
+// longer tie a load through it to the condition that chose it (and so place
+// the load behind a branch), nor merge it with an earlier load of the same
+// address.
+template <class T>
+__device__ __forceinline__ const T* opaque_ptr(const T* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
+// The same for a pointer into global memory, kept in the global address
+// space so that loads through it stay global (not flat) loads.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* opaque_global(const T* p) {
+  auto g = (const __attribute__((address_space(1))) T*)p;
+  asm volatile("" : "+s"(g));
+  return g;
+}
+
+// Marks v as used here: the load that produced it is then issued and waited
+// for before this point, not moved behind a later branch that is the only
+// other place its value is used.
+__device__ __forceinline__ void keep(float v) { asm volatile("" ::"v"(v)); }
+
 // Four dwords as a plain vector type (HIP's uint4 cannot be copied out of the
 // constant address space).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -747,6 +747,13 @@ __global__ __launch_bounds__(256) void k_copy_state(const float* __restrict__ sr
 // (pa.hist[s][j][d], width-1 raw x) is read first and the shifted history,
 // ending with this token's x, written by the quad's first lane (in place
 // allowed).
+//
+// The step is bound by memory latency as much as by bandwidth: each wave
+// makes one access to each array.  So every load is issued first, with no
+// branch among them, and the wave waits for memory once.  An optional array
+// that is absent is read at a valid address of a required array of the same
+// or larger size, and its value is replaced by the default with a
+// wave-uniform select.
 template <class T, bool CONV = false, bool SP = false, bool TR = false, bool RMS = false>
 __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T* __restrict__ x,
                                               const T* __restrict__ delta, const float* __restrict__ A,
@@ -761,68 +768,137 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
   const int64_t sd = g >> 2;
   const int64_t s = sd / d_inner;
   const int64_t d = sd - s * d_inner;
+  using RT = std::conditional_t<RMS, float, T>;
 
   float4 hv = reinterpret_cast<const float4*>(state)[g];
   const float4 av = reinterpret_cast<const float4*>(A)[d * 4 + q];
-  Prologue<CONV, SP> pro;
-  pro.init(pa, d);
   const float xraw = widen(x[sd]);
-  float hist[3] = {0.f, 0.f, 0.f};              // oldest first: x[t-(width-1)] .. x[t-1]
-  const int hw = pa.width - 1;                  // history length (0..3)
-  if constexpr (CONV) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < hw && pa.hist) hist[j] = pa.hist[(s * hw + j) * d_inner + d];
-    // x[t-1], x[t-2], x[t-3] out of the history, oldest first
-    pro.h1 = hw == 3 ? hist[2] : hw == 2 ? hist[1] : hw == 1 ? hist[0] : 0.f;
-    pro.h2 = hw == 3 ? hist[1] : hw == 2 ? hist[0] : 0.f;
-    pro.h3 = hw == 3 ? hist[0] : 0.f;
-  }
-  const float xv = pro.xin(xraw);
+  float dtr = widen(delta[sd]);
+  const float zv = widen(z[sd]);
+  const float Dd = D[d];
   // RMSNorm (prepared by k_rms_prep, one row per sequence): delta * w[d] *
   // s[seq], and the normalised fp32 B and C rows
-  using RT = std::conditional_t<RMS, float, T>;
-  float dtr = widen(delta[sd]);
   const RT* Bs;
   const RT* Cs;
   if constexpr (RMS) {
-    dtr = dtr * (pa.rms_w ? pa.rms_w[d] : 1.0f) * pa.rms_s[s];
     Bs = pa.rms_B + s * NSTATE + 4 * q;
     Cs = pa.rms_C + s * NSTATE + 4 * q;
   } else {
     Bs = B + s * NSTATE + 4 * q;
     Cs = C + s * NSTATE + 4 * q;
   }
+  float bq[4], cq[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    bq[k] = widen(Bs[k]);
+    cq[k] = widen(Cs[k]);
+  }
+  // The prologue's and the trapezoidal form's inputs, as loaded (an absent
+  // array read at a fallback address).
+  const int hw = pa.width - 1;                  // history length (0..3)
+  const bool use_hist = CONV && pa.hist && hw > 0;
+  float tap[4] = {0.f, 0.f, 0.f, 0.f}, cb_raw = 0.f, hist_raw[3] = {0.f, 0.f, 0.f};
+  float dtb_raw = 0.f, rw_raw = 1.f, rs_raw = 1.f, lam_raw = 0.f, xp_raw = 0.f;
+  float bp[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (CONV) {
+    // tap k of the caller's width-W filter goes to slot 4 - W + k (as in
+    // Prologue::init); slots before the filter read tap 0 and are zeroed below
+    const int W = pa.width;
+    const float* wr = pa.conv_w + d * W;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tap[m] = wr[std::max(m + W - 4, 0)];
+    cb_raw = opaque_global(pa.conv_b ? pa.conv_b : D)[d];
+    // without a history the reads go to the state (more than 3 floats per
+    // channel), and their values are dropped
+    const auto* hp = opaque_global<float>(use_hist ? pa.hist : state);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) hist_raw[j] = hp[(s * hw + std::max(std::min(j, hw - 1), 0)) * d_inner + d];
+  }
+  if constexpr (SP) dtb_raw = opaque_global(pa.dt_bias ? pa.dt_bias : D)[d];
+  if constexpr (RMS) {
+    rw_raw = opaque_global(pa.rms_w ? pa.rms_w : D)[d];
+    rs_raw = pa.rms_s[s];
+  }
+  if constexpr (TR) {
+    // lam and x_prev are [n_seq][d_inner] like x, B_prev [n_seq][16] like B
+    lam_raw = widen(opaque_global(pa.lam ? static_cast<const T*>(pa.lam) : x)[sd]);
+    xp_raw = widen(opaque_global(pa.x_prev ? static_cast<const T*>(pa.x_prev) : x)[sd]);
+    const auto* Bq = opaque_global(pa.B_prev ? static_cast<const T*>(pa.B_prev) : B) + s * NSTATE + 4 * q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bp[k] = widen(Bq[k]);
+  }
+  // Every load is in flight: wait for them together (values used only
+  // under a branch would otherwise be loaded there, after this wait).
+  keep(zv);
+  keep(Dd);
+  if constexpr (CONV) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) keep(tap[m]);
+    keep(cb_raw);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) keep(hist_raw[j]);
+  }
+  if constexpr (SP) keep(dtb_raw);
+  if constexpr (RMS) {
+    keep(rw_raw);
+    keep(rs_raw);
+  }
+  if constexpr (TR) {
+    keep(lam_raw);
+    keep(xp_raw);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) keep(bp[k]);
+  }
+
+  Prologue<CONV, SP> pro;
+  float hist[3] = {0.f, 0.f, 0.f};              // oldest first: x[t-(width-1)] .. x[t-1]
+  if constexpr (CONV) {
+    const int W = pa.width;
+    pro.w0 = W >= 4 ? tap[0] : 0.f;
+    pro.w1 = W >= 3 ? tap[1] : 0.f;
+    pro.w2 = W >= 2 ? tap[2] : 0.f;
+    pro.w3 = tap[3];
+    pro.cb = pa.conv_b ? cb_raw : 0.f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) hist[j] = use_hist && j < hw ? hist_raw[j] : 0.f;
+    // x[t-1], x[t-2], x[t-3] out of the history, oldest first
+    pro.h1 = hw == 3 ? hist[2] : hw == 2 ? hist[1] : hw == 1 ? hist[0] : 0.f;
+    pro.h2 = hw == 3 ? hist[1] : hw == 2 ? hist[0] : 0.f;
+    pro.h3 = hw == 3 ? hist[0] : 0.f;
+  }
+  if constexpr (SP) pro.dtb = pa.dt_bias ? dtb_raw : 0.f;
+  if constexpr (RMS) dtr = dtr * (pa.rms_w ? rw_raw : 1.0f) * rs_raw;
+  const float lam = TR && pa.lam ? lam_raw : 0.5f;
+  const float xp = TR && pa.x_prev ? xp_raw : 0.f;
+
+  const float xv = pro.xin(xraw);
   const float dt = pro.dt(dtr);
   float dx = dt * xv;
   if constexpr (TR) {
     // h = a (h + w B_prev) + v B with w = dt (1 - lam) x_prev, v = dt lam x
-    const float lam = pa.lam ? widen(static_cast<const T*>(pa.lam)[sd]) : 0.5f;
-    const float xp = pa.x_prev ? widen(static_cast<const T*>(pa.x_prev)[sd]) : 0.0f;
-    const T* Bq = pa.B_prev ? static_cast<const T*>(pa.B_prev) + s * NSTATE + 4 * q : nullptr;
     const float wv = dt * (1.0f - lam) * xp;
     dx *= lam;
-    if (Bq) {
-      hv.x = fmaf(wv, widen(Bq[0]), hv.x);
-      hv.y = fmaf(wv, widen(Bq[1]), hv.y);
-      hv.z = fmaf(wv, widen(Bq[2]), hv.z);
-      hv.w = fmaf(wv, widen(Bq[3]), hv.w);
+    if (pa.B_prev) {
+      hv.x = fmaf(wv, bp[0], hv.x);
+      hv.y = fmaf(wv, bp[1], hv.y);
+      hv.z = fmaf(wv, bp[2], hv.z);
+      hv.w = fmaf(wv, bp[3], hv.w);
     }
   }
-  hv.x = fmaf(fast_exp2(dt * (av.x * kLog2e)), hv.x, dx * widen(Bs[0]));
-  hv.y = fmaf(fast_exp2(dt * (av.y * kLog2e)), hv.y, dx * widen(Bs[1]));
-  hv.z = fmaf(fast_exp2(dt * (av.z * kLog2e)), hv.z, dx * widen(Bs[2]));
-  hv.w = fmaf(fast_exp2(dt * (av.w * kLog2e)), hv.w, dx * widen(Bs[3]));
-  float part = widen(Cs[0]) * hv.x;
-  part = fmaf(widen(Cs[1]), hv.y, part);
-  part = fmaf(widen(Cs[2]), hv.z, part);
-  part = fmaf(widen(Cs[3]), hv.w, part);
+  hv.x = fmaf(fast_exp2(dt * (av.x * kLog2e)), hv.x, dx * bq[0]);
+  hv.y = fmaf(fast_exp2(dt * (av.y * kLog2e)), hv.y, dx * bq[1]);
+  hv.z = fmaf(fast_exp2(dt * (av.z * kLog2e)), hv.z, dx * bq[2]);
+  hv.w = fmaf(fast_exp2(dt * (av.w * kLog2e)), hv.w, dx * bq[3]);
+  float part = cq[0] * hv.x;
+  part = fmaf(cq[1], hv.y, part);
+  part = fmaf(cq[2], hv.z, part);
+  part = fmaf(cq[3], hv.w, part);
   part += __shfl_xor(part, 1, 4);
   part += __shfl_xor(part, 2, 4);
   if (active) {
     reinterpret_cast<float4*>(state)[g] = hv;
     if (q == 0) {
-      store_io(y + sd, fmaf(D[d], xv, part) * silu(widen(z[sd])));
+      store_io(y + sd, fmaf(Dd, xv, part) * silu(zv));
       if constexpr (CONV) {
         if (pa.hist_out) {
 #pragma unroll

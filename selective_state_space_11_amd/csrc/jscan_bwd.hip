@@ -69,15 +69,6 @@ __device__ __forceinline__ float opaque(float v) {
   return v;
 }
 
-// A wave-uniform pointer the compiler cannot see through: B rows read again
-// in the reverse step are then loaded again into SGPRs instead of being kept
-// (widened, in VGPRs) from the recompute.
-template <class T>
-__device__ __forceinline__ const T* opaque_ptr(const T* p) {
-  asm volatile("" : "+s"(p));
-  return p;
-}
-
 // Sum of v[n] over the 64 lanes of the wave for each n; lane i returns the sum
 // for n = i >> 2.  Each step pairs every lane with a partner, keeps half of
 // its values and adds the partner's copy of them:
