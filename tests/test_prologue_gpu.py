@@ -223,6 +223,41 @@ def test_step_fused_matches_oracle_steps():
         assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
 
 
+@pytest.mark.parametrize("absent", ["conv_bias", "history", "dt_bias", "all"])
+def test_step_fused_optional_inputs_absent(absent):
+    """Fused decode steps (width 4, softplus) with optional inputs left out:
+    no conv bias (0), no conv history (zeros, nothing written back), no
+    dt_bias (0).  Three chained steps of 5 sequences against the oracle."""
+    print_case(f"fused decode without {absent}")
+    n_seq, d, width = 5, 200, 4
+    no = lambda k: absent in (k, "all")
+    pro = synth.prologue_params(d, width, seed=23, batch=n_seq)
+    A, D, _ = synth.params(d, seed=23)
+    st64 = synth.decode_state(n_seq, d, seed=23).astype(np.float64)
+    cs64 = None if no("history") else pro["conv_state"].astype(np.float64)
+    state = dev_f32(synth.decode_state(n_seq, d, seed=23))
+    cs = None if no("history") else dev_f32(pro["conv_state"])
+    cb = None if no("conv_bias") else pro["conv_bias"]
+    dtb = None if no("dt_bias") else pro["dt_bias"]
+    for k in range(3):
+        s = synth.decode_inputs(n_seq, d, seed=23, step=k)
+        s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=300 + k)[:, 0, :]
+        xc, dt, cs_next = oracle.prologue(synth.widen(s["x"])[:, None, :], synth.widen(s["delta"])[:, None, :],
+                                          pro["conv_weight"], cb, cs64, dtb, True)
+        if cs64 is not None:
+            cs64 = cs_next
+        yr, st64 = oracle.step(st64, xc[:, 0, :], dt[:, 0, :], A.astype(np.float64), synth.widen(s["B"]),
+                               synth.widen(s["C"]), D.astype(np.float64), synth.widen(s["z"]))
+        y = js.step_batch_fused(state, dev_io(s["x"]), dev_io(s["delta"]), dev_f32(A), dev_io(s["B"]),
+                                dev_io(s["C"]), dev_f32(D), dev_io(s["z"]), conv_weight=dev_f32(pro["conv_weight"]),
+                                conv_bias=dev_f32(cb), conv_state=cs, dt_bias=dev_f32(dtb), softplus=True)
+        torch.cuda.synchronize()
+        assert_y(y, yr, bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+        if cs is not None:
+            assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
+
+
 @pytest.mark.parametrize("width", [4, 2, 1])
 def test_fused_steps_continue_a_fused_prefill(width):
     """Prefill of 300 tokens then 5 fused steps equals one fused prefill of 305
@@ -349,12 +384,15 @@ def test_prefill_rmsnorm_row_lengths(io, d):
     assert_state(hT, hr, "hT")
 
 
-def test_step_rmsnorm_matches_oracle():
-    """Three fused decode steps with RMSNorm, conv history and softplus."""
-    print_case("rmsnorm decode")
+@pytest.mark.parametrize("which", [(True, True, True), (False, True, True), (True, False, False)],
+                         ids=["dt_B_C", "B_C", "dt"])
+def test_step_rmsnorm_matches_oracle(which):
+    """Three fused decode steps with RMSNorm, conv history and softplus; the
+    weights not in `which` are left out (that tensor is not normalised)."""
+    print_case(f"rmsnorm decode {which}")
     n_seq, d, width = 3, 200, 4
     pro = synth.prologue_params(d, width, seed=62, batch=n_seq)
-    w_dt, w_B, w_C = synth.rms_weights(d, seed=62)
+    w_dt, w_B, w_C = (w if k else None for w, k in zip(synth.rms_weights(d, seed=62), which))
     A, D, _ = synth.params(d, seed=62)
     st64 = synth.decode_state(n_seq, d, seed=62).astype(np.float64)
     cs64 = pro["conv_state"].astype(np.float64)

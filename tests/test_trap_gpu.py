@@ -137,6 +137,40 @@ def test_trap_chained_calls_and_decode():
     assert_state(state, hr, "state after decode")
 
 
+@pytest.mark.parametrize("given", ["none", "lam", "x_prev", "B_prev", "prev"])
+def test_trap_step_optional_inputs(given):
+    """Trapezoidal decode steps with the optional inputs given or left out
+    (lam: 1/2, x_prev and B_prev: zero), each step against the oracle's
+    one-token prefill from the same state.  Three steps of 7 sequences, with
+    softplus and dt_bias."""
+    print_case(f"trap decode given {given}")
+    n_seq, T, d = 7, 3, 136
+    inp, lam, xp, Bp, dtb = problem(n_seq, T, d, seed=45, io=synth.IO_BF16, softplus=True)
+    use_lam = given == "lam"
+    use_x = given in ("x_prev", "prev")
+    use_B = given in ("B_prev", "prev")
+    o = oracle_inputs(inp)
+    state = dev_f32(inp["h0"])
+    st64 = inp["h0"].astype(np.float64)
+    t = to_device(inp)
+    tl = dev_io(lam)
+    for k in range(T):
+        _, dt, _ = oracle.prologue(o["x"][:, k:k + 1], o["delta"][:, k:k + 1], dt_bias=dtb, softplus=True)
+        yr, st64, _, _ = oracle.prefill_trap(o["x"][:, k:k + 1], dt, o["A"], o["B"][:, k:k + 1], o["C"][:, k:k + 1],
+                                             o["D"], o["z"][:, k:k + 1], st64,
+                                             lam=synth.widen(lam[:, k:k + 1]) if use_lam else None,
+                                             x_prev=synth.widen(xp) if use_x else None,
+                                             B_prev=synth.widen(Bp) if use_B else None)
+        y = js.step_batch_trap(state, t["x"][:, k].contiguous(), t["delta"][:, k].contiguous(), t["A"],
+                               t["B"][:, k].contiguous(), t["C"][:, k].contiguous(), t["D"],
+                               t["z"][:, k].contiguous(), lam=tl[:, k].contiguous() if use_lam else None,
+                               x_prev=dev_io(xp) if use_x else None, B_prev=dev_io(Bp) if use_B else None,
+                               dt_bias=dev_f32(dtb), softplus=True)
+        torch.cuda.synchronize()
+        assert_y(y, yr[:, 0], bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+
+
 def test_trap_64k_sampled():
     """The 64K-token prefill (batch 1, d_inner 8192, bf16) with lam and the
     token before the first, automatic plan; 24 sampled channels over all tokens."""
