@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void k_adj_combine(const float* __restrict__ A
   const int64_t b = blockIdx.y;
   const int64_t per_seq = d_inner * NSTATE;
   if (i >= per_seq) return;
-  const int64_t n = i / d_inner;
+  const int64_t n = (uint32_t)i / (uint32_t)d_inner;       // 32-bit: i < 16 d_inner <= 2^28
   const int64_t d = i - n * d_inner;
   const float a2 = A[d * NSTATE + n] * kLog2e;
   float mu = dhT ? dhT[(b * d_inner + d) * NSTATE + n] : 0.0f;
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(256) void k_reduce_ad(const float* __restrict__ dAp
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per = d_inner * NSTATE;
   if (i >= per) return;
-  const int64_t n = i / d_inner;
+  const int64_t n = (uint32_t)i / (uint32_t)d_inner;       // 32-bit: i < 16 d_inner <= 2^28
   const int64_t d = i - n * d_inner;
   float sa = 0.0f, sd = 0.0f;
   // unrolled so that several loads are in flight; the adds keep their order
