@@ -189,9 +189,14 @@ typedef struct {
   /* RMSNorm before everything above, v_i / sqrt(mean_j v_j^2 + rms_eps) * w_i:
    * of delta over its d_inner channels per token, and of the B and C rows
    * over their d_state entries per token (NULL weight: not normalised).  The
-   * normalised values are rounded to the I/O dtype, as a separate layer would
-   * store them, into scratch the library allocates and frees stream-ordered.
-   * Not combined with the trapezoidal form (JSCAN_ERR_UNSUPPORTED). */
+   * normalised values are not rounded to the I/O dtype: a pre-pass writes,
+   * in fp32, each token's inverse root-mean-square of delta and its
+   * normalised B and C rows (132 bytes per token), and the scan applies
+   * delta * w[d] * s[t] as it loads delta.  The prefill keeps these in its
+   * workspace (jscan_prefill_workspace_size counts them); the decode step
+   * in the workspace of jscan_step_batch_fused_ws, or else in scratch it
+   * allocates and frees stream-ordered.  Not combined with the trapezoidal
+   * form (JSCAN_ERR_UNSUPPORTED). */
   const float* rms_dt_weight; /* [d_inner] */
   const float* rms_B_weight;  /* [d_state] */
   const float* rms_C_weight;  /* [d_state] */
@@ -218,6 +223,29 @@ jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_st
                                     float* state, const void* x, const void* delta, const float* A,
                                     const void* B, const void* C, const float* D, const void* z,
                                     void* y, const jscan_prologue* prologue, void* stream);
+
+/*
+ * Bytes of device workspace jscan_step_batch_fused_ws needs for this
+ * prologue: the RMSNorm rows of n_seq sequences (132 bytes per sequence,
+ * rounded up), or 0 when the prologue normalises nothing (or d_state != 16,
+ * or n_seq is outside 1 .. 2^30 - 64).
+ */
+size_t jscan_step_workspace_size(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
+                                 const jscan_prologue* prologue);
+
+/*
+ * jscan_step_batch_fused with a caller workspace (16-byte aligned, device
+ * memory, owned by the caller, not overlapping any other argument): with
+ * RMSNorm the step then calls no allocator and can be captured in a HIP
+ * graph.  workspace NULL: as jscan_step_batch_fused.  A workspace smaller
+ * than jscan_step_workspace_size() returns JSCAN_ERR_WORKSPACE.  The
+ * workspace holds nothing between calls.
+ */
+jscan_status jscan_step_batch_fused_ws(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
+                                       float* state, const void* x, const void* delta, const float* A,
+                                       const void* B, const void* C, const float* D, const void* z, void* y,
+                                       const jscan_prologue* prologue, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /*
  * Exponential-trapezoidal recurrence (Mamba-3's discretisation).  The "AI

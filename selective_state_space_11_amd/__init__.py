@@ -22,8 +22,9 @@ Entry points mirror the C ABI in ``include/jscan.h``:
   gradients dx, ddelta, dz, dA, dB, dC, dD, dh0
 * ``selective_scan(x, delta, A, B, C, D, z, h0=None)`` -> ``(y, hT)`` with
   torch autograd support: forward through jscan_prefill, backward through
-  jscan_backward (recomputing the forward states; nothing else is saved)
-* ``workspace_size``, ``plan``, ``set_plan_override``, ``time_next_prefill``
+  jscan_backward_saved (the forward's workspace is kept for its chunk states)
+* ``workspace_size``, ``step_workspace_size``, ``plan``, ``set_plan_override``,
+  ``time_next_prefill``, ``prefill_stats``
 """
 from __future__ import annotations
 
@@ -44,7 +45,8 @@ EXPORTS = ("jscan_prefill_workspace_size", "jscan_prefill", "jscan_prefill_noall
            "jscan_status_string", "jscan_last_error", "jscan_prefill_plan",
            "jscan_set_plan_override", "jscan_time_next_prefill", "jscan_prefill_fused",
            "jscan_step_batch_fused", "jscan_backward_workspace_size", "jscan_backward", "jscan_prefill_trap",
-           "jscan_step_batch_trap", "jscan_backward_saved", "jscan_prefill_stats")
+           "jscan_step_batch_trap", "jscan_backward_saved", "jscan_prefill_stats", "jscan_step_workspace_size",
+           "jscan_step_batch_fused_ws")
 
 
 class Trap(ctypes.Structure):
@@ -118,6 +120,11 @@ def load_library(path: str = LIB_PATH):
         lib.jscan_prefill_fused.restype = st
         lib.jscan_step_batch_fused.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, pp, vp]
         lib.jscan_step_batch_fused.restype = st
+        lib.jscan_step_workspace_size.argtypes = [i64, i64, i64, st, pp]
+        lib.jscan_step_workspace_size.restype = sz
+        lib.jscan_step_batch_fused_ws.argtypes = [i64, i64, i64, st, fp, vp, vp, fp, vp, vp, fp, vp, vp, pp, vp, sz,
+                                                  vp]
+        lib.jscan_step_batch_fused_ws.restype = st
         tp = ctypes.POINTER(Trap)
         lib.jscan_prefill_trap.argtypes = [i64, i64, i64, i64, st, vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, tp, pp, vp,
                                            sz, vp]
@@ -388,10 +395,17 @@ def prefill_fused(x, delta, A, B, C, D, z, h0=None, *, conv_weight=None, conv_bi
     return y, hT
 
 
+def step_workspace_size(n_seq, d_inner, rms=None, io=IO_BF16) -> int:
+    """Bytes of workspace step_batch_fused needs with this RMSNorm argument (0 without one)."""
+    pro = _prologue(n_seq, d_inner, None, None, None, None, None, False, rms)
+    return int(load_library().jscan_step_workspace_size(n_seq, d_inner, D_STATE, io, ctypes.byref(pro)))
+
+
 def step_batch_fused(state, x, delta, A, B, C, D, z, *, conv_weight=None, conv_bias=None, conv_state=None,
-                     dt_bias=None, softplus=False, rms=None, y=None, stream=None):
+                     dt_bias=None, softplus=False, rms=None, y=None, workspace=None, stream=None):
     """step_batch with the input prologue; conv_state [n_seq, width-1, d_inner] holds the last
-    width-1 raw x of each sequence and is updated in place, like state."""
+    width-1 raw x of each sequence and is updated in place, like state.  With RMSNorm, a
+    workspace of step_workspace_size() bytes keeps the step free of allocations."""
     torch = _torch()
     lib = load_library()
     _dev(state, "state", torch.float32)
@@ -409,9 +423,16 @@ def step_batch_fused(state, x, delta, A, B, C, D, z, *, conv_weight=None, conv_b
     if y is None:
         y = torch.empty_like(x)
     _dev(y, "y", x.dtype, x.shape)
-    _check(lib.jscan_step_batch_fused(n_seq, d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
-                                      _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), ctypes.byref(pro),
-                                      _stream(stream)))
+    if workspace is None:
+        _check(lib.jscan_step_batch_fused(n_seq, d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), ctypes.byref(pro),
+                                          _stream(stream)))
+    else:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib.jscan_step_batch_fused_ws(n_seq, d_inner, D_STATE, io, _ptr(state), _ptr(x), _ptr(delta),
+                                             _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                                             ctypes.byref(pro), _ptr(workspace), ws_bytes, _stream(stream)))
     return y
 
 

@@ -1473,10 +1473,13 @@ jscan_status prefill_impl(int64_t batch, int64_t L, int64_t d_inner, int64_t d_s
   return s;
 }
 
+// workspace: the RMSNorm rows' region (rms_bytes(n_seq) bytes), or null to
+// allocate it stream-ordered; unused without RMSNorm.
 jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io, float* state,
                        const void* x, const void* delta, const float* A, const void* B, const void* C,
                        const float* D, const void* z, void* y, const jscan_prologue* pro,
-                       const jscan_trap* trap, void* stream) {
+                       const jscan_trap* trap, void* stream, void* workspace = nullptr,
+                       size_t workspace_bytes = 0) {
   t_last_error.clear();
   jscan_status s = check_common(d_state, io);
   if (s != JSCAN_OK) return s;
@@ -1493,32 +1496,42 @@ jscan_status step_impl(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io
   }
   if (!state || !x || !delta || !A || !B || !C || !D || !z || !y)
     return fail(JSCAN_ERR_NULL, "every pointer is required");
-  const void* ptrs[] = {state, x, delta, A, B, C, D, z, y};
+  const void* ptrs[] = {state, x, delta, A, B, C, D, z, y, workspace};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    if (p && !aligned16(p)) return fail(JSCAN_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  const bool rms = has_rms(pro);
+  const size_t need = rms ? rms_bytes(n_seq) : 0;
   const size_t es = io == JSCAN_IO_BF16 ? 2 : 4;
   const size_t tok = (size_t)n_seq * (size_t)d_inner * es;
   const size_t rowb = (size_t)n_seq * NSTATE * es;
   const size_t stb = (size_t)n_seq * (size_t)d_inner * NSTATE * 4;
   Range in[20] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, tok, "z"}, {B, rowb, "B"}, {C, rowb, "C"},
                   {A, (size_t)d_inner * NSTATE * 4, "A"}, {D, (size_t)d_inner * 4, "D"}};
-  Range out[3] = {{y, tok, "y"}, {state, stb, "state"}};
+  Range out[4] = {{y, tok, "y"}, {state, stb, "state"}};
   int n_in = 7, n_out = 2;
+  if (workspace && need) out[n_out++] = Range{workspace, need, "workspace"};
   ProArgs pa;
   if ((s = check_prologue(pro, n_seq, d_inner, &pa, in, &n_in, out, &n_out)) != JSCAN_OK) return s;
-  if ((s = check_trap(trap, has_rms(pro), n_seq, 1, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
+  if ((s = check_trap(trap, rms, n_seq, 1, d_inner, es, &pa, in, &n_in)) != JSCAN_OK) return s;
   if ((s = check_ranges(in, n_in, out, n_out, pa.hist_out && pa.hist_out == pa.hist ? pa.hist : nullptr)) !=
       JSCAN_OK)
     return s;
+  if (workspace && workspace_bytes < need)
+    return fail(JSCAN_ERR_WORKSPACE, "workspace smaller than jscan_step_workspace_size()");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr, rms = has_rms(pro);
-  // RMSNorm: one row per sequence, in stream-ordered scratch (the step takes no workspace)
+  const bool conv = pa.conv_w != nullptr, sp = pro && pro->dt_softplus, tr = trap != nullptr;
+  // RMSNorm: one row per sequence, in the caller's workspace or in
+  // stream-ordered scratch
   char* rms_scratch = nullptr;
   if (rms) {
-    hipError_t e;
-    if ((e = hipMallocAsync(reinterpret_cast<void**>(&rms_scratch), rms_bytes(n_seq), st)) != hipSuccess)
-      return hip_fail(e, "hipMallocAsync(rmsnorm scratch)");
-    s = rms_prep(pro, io, n_seq, d_inner, delta, B, C, rms_scratch, &pa, st);
+    char* region = static_cast<char*>(workspace);
+    if (!region) {
+      hipError_t e;
+      if ((e = hipMallocAsync(reinterpret_cast<void**>(&rms_scratch), need, st)) != hipSuccess)
+        return hip_fail(e, "hipMallocAsync(rmsnorm scratch)");
+      region = rms_scratch;
+    }
+    s = rms_prep(pro, io, n_seq, d_inner, delta, B, C, region, &pa, st);
   }
   if (s == JSCAN_OK)
     s = with_flags(conv, sp, tr, rms, [&](auto cv, auto spv, auto trv, auto rmv) {
@@ -1670,6 +1683,23 @@ jscan_status jscan_step_batch_fused(int64_t n_seq, int64_t d_inner, int64_t d_st
                                     const void* B, const void* C, const float* D, const void* z,
                                     void* y, const jscan_prologue* prologue, void* stream) {
   return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, prologue, nullptr, stream);
+}
+
+size_t jscan_step_workspace_size(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
+                                 const jscan_prologue* prologue) {
+  (void)d_inner;
+  (void)io;
+  if (d_state != NSTATE || n_seq <= 0 || n_seq > kMaxStepChannels || !has_rms(prologue)) return 0;
+  return rms_bytes(n_seq);
+}
+
+jscan_status jscan_step_batch_fused_ws(int64_t n_seq, int64_t d_inner, int64_t d_state, jscan_io io,
+                                       float* state, const void* x, const void* delta, const float* A,
+                                       const void* B, const void* C, const float* D, const void* z, void* y,
+                                       const jscan_prologue* prologue, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  return step_impl(n_seq, d_inner, d_state, io, state, x, delta, A, B, C, D, z, y, prologue, nullptr, stream,
+                   workspace, workspace_bytes);
 }
 
 jscan_status jscan_prefill_trap(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, jscan_io io,

@@ -27,7 +27,8 @@ int main(void) {
       (fn)&jscan_prefill_trap,           (fn)&jscan_step_batch_trap,  (fn)&jscan_backward_workspace_size,
       (fn)&jscan_backward,               (fn)&jscan_backward_saved,   (fn)&jscan_status_string,
       (fn)&jscan_last_error,             (fn)&jscan_prefill_plan,     (fn)&jscan_set_plan_override,
-      (fn)&jscan_time_next_prefill,      (fn)&jscan_prefill_stats};
+      (fn)&jscan_time_next_prefill,      (fn)&jscan_prefill_stats,    (fn)&jscan_step_workspace_size,
+      (fn)&jscan_step_batch_fused_ws};
   size_t i;
   int waves = 0, chunks = 0;
   for (i = 0; i < sizeof(entry) / sizeof(entry[0]); ++i) CHECK(entry[i] != NULL);
@@ -47,6 +48,16 @@ int main(void) {
   {
     double stats[3];
     CHECK(jscan_prefill_stats(NULL, 0, 1, 65536, 8192, stats, NULL) == JSCAN_ERR_NULL);
+  }
+  {
+    /* the decode step's workspace: only RMSNorm needs one */
+    jscan_prologue pro;
+    memset(&pro, 0, sizeof pro);
+    CHECK(jscan_step_workspace_size(256, 8192, 16, JSCAN_IO_BF16, &pro) == 0);
+    CHECK(jscan_step_workspace_size(256, 8192, 16, JSCAN_IO_BF16, NULL) == 0);
+    pro.rms_B_weight = (const float*)(size_t)256;   /* only tested against NULL here */
+    CHECK(jscan_step_workspace_size(256, 8192, 16, JSCAN_IO_BF16, &pro) >= 256 * 132);
+    CHECK(jscan_step_workspace_size(256, 8192, 15, JSCAN_IO_BF16, &pro) == 0);
   }
   printf("c abi ok: %d waves, %d chunks at 1 x 65536 x 8192\n", waves, chunks);
   return 0;

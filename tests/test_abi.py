@@ -333,6 +333,32 @@ def test_step_fused_validation(lib):
                                       ctypes.byref(prologue(conv_width=9)), None) == UNSUP
 
 
+def test_step_fused_workspace_validation(lib):
+    """jscan_step_batch_fused_ws: the RMSNorm rows need jscan_step_workspace_size()
+    bytes; the workspace is checked like any other output buffer; without
+    RMSNorm it needs none."""
+    a = step_args()
+    rms = prologue(rms_B_weight=fake(24), rms_C_weight=fake(25))
+    need = lib.jscan_step_workspace_size(a["n_seq"], a["d_inner"], 16, BF16, ctypes.byref(rms))
+    assert need >= a["n_seq"] * 132
+    assert lib.jscan_step_workspace_size(a["n_seq"], a["d_inner"], 16, BF16, ctypes.byref(prologue())) == 0
+    assert lib.jscan_step_workspace_size(a["n_seq"], a["d_inner"], 16, BF16, None) == 0
+    assert lib.jscan_step_workspace_size(0, a["d_inner"], 16, BF16, ctypes.byref(rms)) == 0
+
+    def call(pro, ws, ws_bytes):
+        return lib.jscan_step_batch_fused_ws(a["n_seq"], a["d_inner"], a["d_state"], a["io"], a["state"], a["x"],
+                                             a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["y"],
+                                             ctypes.byref(pro), ws, ws_bytes, a["stream"])
+    assert call(rms, fake(30), need - 1) == WS
+    assert call(rms, ctypes.c_void_p(fake(30).value + 8), need) == ALIGN
+    assert call(rms, fake(0, 256), need) == ALIAS                  # workspace inside the state
+    assert call(rms, fake(1), need) == ALIAS                       # over x
+    assert call(prologue(conv_width=7), fake(30), need) == UNSUP
+    # no RMSNorm: the workspace is not needed, so a short one is accepted (nothing to
+    # launch here would fail only on the GPU, so only the rejected calls are made)
+    assert call(prologue(conv_weight=None), fake(30), 0) == NULL
+
+
 # ------------------------------------------------------------------ backward
 def bwd_args(batch=1, L=64, d_inner=128, d_state=16, io=BF16, **over):
     a = dict(batch=batch, L=L, d_inner=d_inner, d_state=d_state, io=io, x=fake(0), delta=fake(1), A=fake(2),

@@ -48,11 +48,13 @@ def decode_tokens(n_seq, d, T, seed):
     return [{k: dev_io(v[k]) for k in ("x", "delta", "z", "B", "C")} for v in toks]
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_decode_steps_replayed(fused):
-    """Eight decode steps of 4 sequences x 256 channels (plain, or with the
-    conv(4) + SiLU and softplus prologue and its conv history in place)."""
-    print_case(f"graph decode fused={fused}")
+@pytest.mark.parametrize("variant", ["plain", "fused", "rmsnorm"])
+def test_decode_steps_replayed(variant):
+    """Eight decode steps of 4 sequences x 256 channels: plain; with the
+    conv(4) + SiLU and softplus prologue and its conv history in place; and
+    the same with RMSNorm of delta, B and C, given a step workspace."""
+    print_case(f"graph decode {variant}")
+    fused = variant != "plain"
     n_seq, d, T = 4, 256, 8
     A, D, _ = synth.params(d, seed=90)
     A, D = dev_f32(A), dev_f32(D)
@@ -62,6 +64,11 @@ def test_decode_steps_replayed(fused):
     cs0 = dev_f32(pro["conv_state"])
     kw = dict(conv_weight=dev_f32(pro["conv_weight"]), conv_bias=dev_f32(pro["conv_bias"]),
               dt_bias=dev_f32(pro["dt_bias"]), softplus=True)
+    if variant == "rmsnorm":
+        kw["rms"] = tuple(dev_f32(w) for w in synth.rms_weights(d, seed=90)) + (1e-5,)
+        kw["workspace"] = torch.empty(js.step_workspace_size(n_seq, d, kw["rms"]), dtype=torch.uint8,
+                                      device="cuda")
+        assert kw["workspace"].numel() > 0
 
     def steps(st, cs, ys):
         for k, t in enumerate(toks):

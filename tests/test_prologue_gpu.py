@@ -418,6 +418,38 @@ def test_step_rmsnorm_matches_oracle(which):
         assert np.array_equal(host64(cs), cs64)
 
 
+def test_step_rmsnorm_workspace_equals_scratch():
+    """The RMSNorm decode step given a workspace (jscan_step_batch_fused_ws)
+    equals the step that allocates its scratch, bit for bit: two steps of 3
+    sequences, then one of 2 in the same workspace."""
+    print_case("rmsnorm decode workspace")
+    d = 200
+    A, D, _ = synth.params(d, seed=64)
+    tA, tD = dev_f32(A), dev_f32(D)
+    pro = synth.prologue_params(d, 4, seed=64, batch=3)
+    rms = tuple(dev_f32(w) for w in synth.rms_weights(d, seed=64)) + (EPS,)
+    ws = torch.empty(js.step_workspace_size(3, d, rms), dtype=torch.uint8, device="cuda")
+    assert ws.numel() >= 3 * 132 and js.step_workspace_size(2, d, rms) <= ws.numel()
+    st_a = dev_f32(synth.decode_state(3, d, seed=64))
+    st_b = st_a.clone()
+    cs_a = dev_f32(pro["conv_state"])
+    cs_b = cs_a.clone()
+    for k, n_seq in enumerate((3, 3, 2)):
+        s = synth.decode_inputs(n_seq, d, seed=64, step=k)
+        s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=400 + k)[:, 0, :]
+        t = {key: dev_io(s[key]) for key in ("x", "delta", "z", "B", "C")}
+        kw = dict(conv_weight=dev_f32(pro["conv_weight"]), conv_bias=dev_f32(pro["conv_bias"]),
+                  dt_bias=dev_f32(pro["dt_bias"]), softplus=True, rms=rms)
+        sa, ca, sb, cb = st_a[:n_seq], cs_a[:n_seq], st_b[:n_seq], cs_b[:n_seq]
+        ya = js.step_batch_fused(sa, t["x"], t["delta"], tA, t["B"], t["C"], tD, t["z"], conv_state=ca, **kw)
+        yb = js.step_batch_fused(sb, t["x"], t["delta"], tA, t["B"], t["C"], tD, t["z"], conv_state=cb,
+                                 workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb), k
+        assert torch.equal(sa, sb), k
+        assert torch.equal(ca, cb), k
+
+
 def test_prefill_rmsnorm_jamba_shape():
     """Batch 2 x 4096 x 8192 bf16 with RMSNorm and softplus: every output."""
     print_case("rmsnorm 2x4096x8192")
