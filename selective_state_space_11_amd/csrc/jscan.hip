@@ -768,7 +768,7 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
   const int64_t g = active ? gid : total - 1;   // whole quads stay together: total % 4 == 0
   const int q = (int)(g & 3);
   const int64_t sd = g >> 2;
-  const int64_t s = sd / d_inner;
+  const int64_t s = (uint32_t)sd / (uint32_t)d_inner;   // 32-bit: sd < n_seq * d_inner < 2^30
   const int64_t d = sd - s * d_inner;
   using RT = std::conditional_t<RMS, float, T>;
 
