@@ -336,14 +336,17 @@ jscan_status jscan_backward(int64_t batch, int64_t L, int64_t d_inner, int64_t d
  * jscan_backward for a training step that kept the workspace of its forward
  * call: prefill_workspace is the workspace a jscan_prefill call used (the
  * plain prefill, not the fused or trapezoidal one) with the same x, delta, A,
- * B, h0 and sizes, on the same thread's launch plan, unchanged since.  When
- * the plan runs in chunks, that workspace holds the state before every chunk
- * (the forward's chunk-local pass and combine), and the backward reads them
- * there instead of recomputing them; single-chunk plans ignore it (it may then
- * be NULL).  The gradients equal jscan_backward's bit for bit.
+ * B, h0 and sizes, on the same thread's launch plan, unchanged since.  The
+ * backward runs its sweeps on sub-chunks of the sequence whenever the batch's
+ * channel groups alone cannot fill the GPU (every chunked prefill plan and
+ * some single-chunk ones).  The prefill then records, in that workspace, the
+ * chunk-local state at every sub-chunk boundary and the true state before
+ * every chunk, and the backward derives each sub-chunk's starting state from
+ * them instead of running a state-only pass over the sequence.  Otherwise the
+ * workspace is not read.  The gradients equal jscan_backward's bit for bit.
  *
  * prefill_workspace: at least jscan_prefill_workspace_size() bytes (read
- * only; JSCAN_ERR_NULL if NULL for a chunked plan).  workspace: NULL or at
+ * only; JSCAN_ERR_NULL if it is needed and NULL).  workspace: NULL or at
  * least jscan_backward_workspace_size() - jscan_prefill_workspace_size()
  * bytes.  Otherwise as jscan_backward; nothing may overlap prefill_workspace.
  *
