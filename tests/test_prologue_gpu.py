@@ -223,6 +223,46 @@ def test_step_fused_matches_oracle_steps():
         assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
 
 
+@pytest.mark.parametrize("n_seq,d", [(1, 1), (1, 8), (7, 1), (300, 3), (2, 65)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_edge_sizes(n_seq, d, fused):
+    """Decode steps at degenerate sizes: one channel (each quad of a wave is
+    another sequence), one sequence, and channel counts that leave a wave
+    part-filled; plain or with the conv(4) + softplus prologue.  Two chained
+    steps against the oracle."""
+    print_case(f"decode edge n_seq={n_seq} d={d} fused={fused}")
+    pro = synth.prologue_params(d, 4, seed=31, batch=n_seq)
+    A, D, _ = synth.params(d, seed=31)
+    st64 = synth.decode_state(n_seq, d, seed=31).astype(np.float64)
+    cs64 = pro["conv_state"].astype(np.float64)
+    state = dev_f32(synth.decode_state(n_seq, d, seed=31))
+    cs = dev_f32(pro["conv_state"])
+    tA, tD = dev_f32(A), dev_f32(D)
+    for k in range(2):
+        s = synth.decode_inputs(n_seq, d, seed=31, step=k)
+        if fused:
+            s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=500 + k)[:, 0, :]
+            xc, dt, cs64 = oracle.prologue(synth.widen(s["x"])[:, None, :], synth.widen(s["delta"])[:, None, :],
+                                           pro["conv_weight"], pro["conv_bias"], cs64, pro["dt_bias"], True)
+            xo, do = xc[:, 0, :], dt[:, 0, :]
+        else:
+            xo, do = synth.widen(s["x"]), synth.widen(s["delta"])
+        yr, st64 = oracle.step(st64, xo, do, A.astype(np.float64), synth.widen(s["B"]), synth.widen(s["C"]),
+                               D.astype(np.float64), synth.widen(s["z"]))
+        t = {key: dev_io(s[key]) for key in ("x", "delta", "z", "B", "C")}
+        if fused:
+            y = js.step_batch_fused(state, t["x"], t["delta"], tA, t["B"], t["C"], tD, t["z"],
+                                    conv_weight=dev_f32(pro["conv_weight"]), conv_bias=dev_f32(pro["conv_bias"]),
+                                    conv_state=cs, dt_bias=dev_f32(pro["dt_bias"]), softplus=True)
+        else:
+            y = js.step_batch(state, t["x"], t["delta"], tA, t["B"], t["C"], tD, t["z"])
+        torch.cuda.synchronize()
+        assert_y(y, yr, bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+        if fused:
+            assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
+
+
 @pytest.mark.parametrize("absent", ["conv_bias", "history", "dt_bias", "all"])
 def test_step_fused_optional_inputs_absent(absent):
     """Fused decode steps (width 4, softplus) with optional inputs left out:

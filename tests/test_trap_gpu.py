@@ -171,6 +171,33 @@ def test_trap_step_optional_inputs(given):
         assert_state(state, st64, f"state step {k}")
 
 
+@pytest.mark.parametrize("n_seq,d", [(1, 1), (7, 1), (300, 3), (2, 65)])
+def test_trap_step_edge_sizes(n_seq, d):
+    """Trapezoidal decode steps at degenerate sizes (one channel, one sequence,
+    part-filled waves), every optional input given; each step against the
+    oracle's one-token prefill from the same state."""
+    print_case(f"trap decode edge n_seq={n_seq} d={d}")
+    inp, lam, xp, Bp, dtb = problem(n_seq, 2, d, seed=46, io=synth.IO_BF16, softplus=True)
+    o = oracle_inputs(inp)
+    state = dev_f32(inp["h0"])
+    st64 = inp["h0"].astype(np.float64)
+    t = to_device(inp)
+    tl = dev_io(lam)
+    for k in range(2):
+        _, dt, _ = oracle.prologue(o["x"][:, k:k + 1], o["delta"][:, k:k + 1], dt_bias=dtb, softplus=True)
+        yr, st64, _, _ = oracle.prefill_trap(o["x"][:, k:k + 1], dt, o["A"], o["B"][:, k:k + 1], o["C"][:, k:k + 1],
+                                             o["D"], o["z"][:, k:k + 1], st64, lam=synth.widen(lam[:, k:k + 1]),
+                                             x_prev=synth.widen(xp), B_prev=synth.widen(Bp))
+        # fresh copies: a one-channel slice is contiguous but not 16-byte aligned
+        tok = lambda v: v[:, k].clone()
+        y = js.step_batch_trap(state, tok(t["x"]), tok(t["delta"]), t["A"], tok(t["B"]), tok(t["C"]), t["D"],
+                               tok(t["z"]), lam=tok(tl), x_prev=dev_io(xp), B_prev=dev_io(Bp), dt_bias=dev_f32(dtb),
+                               softplus=True)
+        torch.cuda.synchronize()
+        assert_y(y, yr[:, 0], bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+
+
 def test_trap_64k_sampled():
     """The 64K-token prefill (batch 1, d_inner 8192, bf16) with lam and the
     token before the first, automatic plan; 24 sampled channels over all tokens."""
