@@ -1,4 +1,4 @@
-"""HIP-graph capture of libjscan calls (torch.cuda.CUDAGraph): decode steps,
+"""HIP-graph capture of libjscan calls (torch.cuda.CUDAGraph): decode steps (plain, fused, RMSNorm, trapezoidal),
 fused decode steps, a chunked prefill, the fused prefill with RMSNorm, the
 trapezoidal prefill and the backward, given caller workspaces, launch only kernels on the caller's
 stream, so they can be captured once and replayed.
@@ -48,13 +48,14 @@ def decode_tokens(n_seq, d, T, seed):
     return [{k: dev_io(v[k]) for k in ("x", "delta", "z", "B", "C")} for v in toks]
 
 
-@pytest.mark.parametrize("variant", ["plain", "fused", "rmsnorm"])
+@pytest.mark.parametrize("variant", ["plain", "fused", "rmsnorm", "trapezoidal"])
 def test_decode_steps_replayed(variant):
     """Eight decode steps of 4 sequences x 256 channels: plain; with the
-    conv(4) + SiLU and softplus prologue and its conv history in place; and
-    the same with RMSNorm of delta, B and C, given a step workspace."""
+    conv(4) + SiLU and softplus prologue and its conv history in place; the
+    same with RMSNorm of delta, B and C, given a step workspace; and the
+    exponential-trapezoidal step (lam, and the previous token's x and B row)."""
     print_case(f"graph decode {variant}")
-    fused = variant != "plain"
+    fused = variant in ("fused", "rmsnorm")
     n_seq, d, T = 4, 256, 8
     A, D, _ = synth.params(d, seed=90)
     A, D = dev_f32(A), dev_f32(D)
@@ -70,11 +71,17 @@ def test_decode_steps_replayed(variant):
                                       device="cuda")
         assert kw["workspace"].numel() > 0
 
+    lam = [dev_io(synth.trap_inputs(n_seq, 1, d, seed=90 + k)[0][:, 0, :]) for k in range(T)]
+
     def steps(st, cs, ys):
         for k, t in enumerate(toks):
             if fused:
                 js.step_batch_fused(st, t["x"], t["delta"], A, t["B"], t["C"], D, t["z"], conv_state=cs, y=ys[k],
                                     **kw)
+            elif variant == "trapezoidal":
+                prev = toks[k - 1] if k else toks[T - 1]
+                js.step_batch_trap(st, t["x"], t["delta"], A, t["B"], t["C"], D, t["z"], lam=lam[k], x_prev=prev["x"],
+                                   B_prev=prev["B"], y=ys[k])
             else:
                 js.step_batch(st, t["x"], t["delta"], A, t["B"], t["C"], D, t["z"], y=ys[k])
 
