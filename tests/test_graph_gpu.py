@@ -1,7 +1,8 @@
-"""HIP-graph capture of libjscan calls (torch.cuda.CUDAGraph): decode steps (plain, fused, RMSNorm, trapezoidal),
-fused decode steps, a chunked prefill, the fused prefill with RMSNorm, the
-trapezoidal prefill and the backward, given caller workspaces, launch only kernels on the caller's
-stream, so they can be captured once and replayed.
+"""HIP-graph capture of libjscan calls (torch.cuda.CUDAGraph): decode steps
+(plain, fused, fused with RMSNorm, trapezoidal), a chunked prefill, the fused
+prefill with RMSNorm, the trapezoidal prefill and the backward, given caller
+workspaces, launch only kernels on the caller's stream, so they can be
+captured once and replayed.
 
 Each graph is replayed several times from the same starting state, with eager
 library work and synchronisations between the replays, and every replay must
