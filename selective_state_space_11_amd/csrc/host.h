@@ -92,13 +92,20 @@ constexpr int64_t kTagMagic = 0x6a7363616e746167LL;
 struct Tag { int64_t w[kTagWords]; };
 Tag make_tag(int64_t batch, int64_t L, int64_t d_inner, const Plan& p, int variant);
 
-// Starting states of the sub-chunks of plan p (p.subs > 1), for the
-// backward: hstart[b][s][n][d] = the true state before sub-chunk s's first
-// token.  With `saved` (a plain prefill's workspace, as jscan_prefill leaves
-// it) they are derived from its records; otherwise a state-only pass and the
-// combine first write the records into `rec` (ws_layout(...).total bytes).
-jscan_status sub_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
+// The records the backward derives its sub-chunk starting states from (plan
+// p with p.subs > 1): the chunk-local state and delta sum at every sub-chunk
+// boundary, sS[b][s][n][d] and sL[b][s][d] (boundary s + 1 of sequence b),
+// and the true starting state of every forward chunk, H[b][c][n][d].  With
+// `saved` (a plain prefill's workspace, as jscan_prefill leaves it) they are
+// there already; otherwise a state-only pass and the combine write them into
+// `rec` (ws_layout(...).total bytes).
+struct SubRecords {
+  const float* sS;
+  const float* sL;
+  const float* H;
+};
+jscan_status backward_records(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
                               const void* delta, const float* A, const void* B, const float* h0, char* rec,
-                              const char* saved, float* hstart, const Plan& p, hipStream_t st);
+                              const char* saved, const Plan& p, hipStream_t st, SubRecords* out);
 
 }  // namespace jscan_detail

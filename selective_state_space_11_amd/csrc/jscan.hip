@@ -304,40 +304,6 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ A, co
   }
 }
 
-// Starting states of the sub-chunks (for the backward), one lane per
-// (b, s, n, d): sub-chunk 0 starts at h0 (or zero); sub-chunk s >= 1 starts
-// at the boundary g = s * sub_len, inside forward chunk c = (g - 1) /
-// chunk_len, where the true state is P * H[c] + S from the boundary's record
-// (for c = 0 the record itself, which began at h0).
-__global__ __launch_bounds__(256) void k_substarts(const float* __restrict__ A, const float* __restrict__ sS,
-                                                   const float* __restrict__ sL, const float* __restrict__ H,
-                                                   const float* __restrict__ h0, float* __restrict__ hs,
-                                                   int64_t d_inner, int chunks, int subs, int64_t chunk_len,
-                                                   int64_t sub_len) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int s = blockIdx.y;
-  const int64_t b = blockIdx.z;
-  const int64_t per_seq = d_inner * NSTATE;
-  if (i >= per_seq) return;
-  const int64_t n = (uint32_t)i / (uint32_t)d_inner;       // 32-bit: i < 16 d_inner <= 2^28
-  const int64_t d = i - n * d_inner;
-  float v;
-  if (s == 0) {
-    v = h0 ? h0[(b * d_inner + d) * NSTATE + n] : 0.0f;
-  } else {
-    const int64_t j = s - 1;
-    const int64_t c = (uint32_t)(s * sub_len - 1) / (uint32_t)chunk_len;   // 32-bit: below L < 2^31
-    const float S = sS[((b * subs + j) * NSTATE + n) * d_inner + d];
-    if (c == 0) {
-      v = S;
-    } else {
-      const float a2 = A[d * NSTATE + n] * kLog2e;
-      v = fmaf(fast_exp2(a2 * sL[(b * subs + j) * d_inner + d]), H[((b * chunks + c) * NSTATE + n) * d_inner + d], S);
-    }
-  }
-  hs[((b * subs + s) * NSTATE + n) * d_inner + d] = v;
-}
-
 // ----------------------------------------------------------------- main scan
 // Extra arguments of the main scan (pointers into the workspace).
 struct ScanAux {
@@ -1156,42 +1122,41 @@ jscan_status run_prefill(int64_t batch, int64_t L, int64_t d_inner, const void* 
 }
 
 template <class T>
-jscan_status sub_starts_t(int64_t batch, int64_t L, int64_t d_inner, const void* x, const void* delta,
-                          const float* A, const void* B, const float* h0, char* rec, const char* saved,
-                          float* hstart, const Plan& p, hipStream_t st) {
+jscan_status records_t(int64_t batch, int64_t L, int64_t d_inner, const void* x, const void* delta, const float* A,
+                       const void* B, const float* h0, char* rec, const Plan& p, hipStream_t st) {
   const WsLayout w = ws_layout(batch, L, d_inner, p);
+  const Records r = records_in(rec, w, p);
   hipError_t e;
-  const char* base = saved ? saved : rec;
-  if (!saved) {
-    const Records r = records_in(rec, w, p);
-    dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)p.chunks, (unsigned)batch);
-    hipLaunchKernelGGL((k_chunk_state<T>), g1, dim3(256), 0, st, static_cast<const T*>(x),
-                       static_cast<const T*>(delta), A, static_cast<const T*>(B), h0, r, L, d_inner, p.chunk_len);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
-    if (p.chunks > 1) {
-      dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
-      hipLaunchKernelGGL((k_combine<T>), g2, dim3(256), 0, st, A, r.eS, r.eL, reinterpret_cast<float*>(rec + w.off_H()),
-                         nullptr, d_inner, p.chunks, static_cast<const T*>(x), L,
-                         ProArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 1}, nullptr, Tag{});
-      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
-    }
+  dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)p.chunks, (unsigned)batch);
+  hipLaunchKernelGGL((k_chunk_state<T>), g1, dim3(256), 0, st, static_cast<const T*>(x),
+                     static_cast<const T*>(delta), A, static_cast<const T*>(B), h0, r, L, d_inner, p.chunk_len);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "chunk-state launch");
+  if (p.chunks > 1) {
+    dim3 g2((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)batch);
+    hipLaunchKernelGGL((k_combine<T>), g2, dim3(256), 0, st, A, r.eS, r.eL, reinterpret_cast<float*>(rec + w.off_H()),
+                       nullptr, d_inner, p.chunks, static_cast<const T*>(x), L,
+                       ProArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 1}, nullptr, Tag{});
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "combine launch");
   }
-  dim3 g3((unsigned)((d_inner * NSTATE + 255) / 256), (unsigned)p.subs, (unsigned)batch);
-  hipLaunchKernelGGL(k_substarts, g3, dim3(256), 0, st, A, reinterpret_cast<const float*>(base + w.off_sS()),
-                     reinterpret_cast<const float*>(base + w.off_sL()),
-                     reinterpret_cast<const float*>(base + w.off_H()), h0, hstart, d_inner, p.chunks, p.subs,
-                     p.chunk_len, p.sub_len);
-  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "sub-chunk starts launch");
   return JSCAN_OK;
 }
 
-jscan_status sub_chunk_starts(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
+jscan_status backward_records(jscan_io io, int64_t batch, int64_t L, int64_t d_inner, const void* x,
                               const void* delta, const float* A, const void* B, const float* h0, char* rec,
-                              const char* saved, float* hstart, const Plan& p, hipStream_t st) {
+                              const char* saved, const Plan& p, hipStream_t st, SubRecords* out) {
+  *out = SubRecords{};
   if (p.subs <= 1) return JSCAN_OK;
-  return io == JSCAN_IO_BF16
-             ? sub_starts_t<uint16_t>(batch, L, d_inner, x, delta, A, B, h0, rec, saved, hstart, p, st)
-             : sub_starts_t<float>(batch, L, d_inner, x, delta, A, B, h0, rec, saved, hstart, p, st);
+  if (!saved) {
+    const jscan_status s = io == JSCAN_IO_BF16
+                               ? records_t<uint16_t>(batch, L, d_inner, x, delta, A, B, h0, rec, p, st)
+                               : records_t<float>(batch, L, d_inner, x, delta, A, B, h0, rec, p, st);
+    if (s != JSCAN_OK) return s;
+  }
+  const char* base = saved ? saved : rec;
+  const WsLayout w = ws_layout(batch, L, d_inner, p);
+  *out = SubRecords{reinterpret_cast<const float*>(base + w.off_sS()), reinterpret_cast<const float*>(base + w.off_sL()),
+                    reinterpret_cast<const float*>(base + w.off_H())};
+  return JSCAN_OK;
 }
 
 // Calls f(integral_constant<bool, CONV>, integral_constant<bool, SP>,

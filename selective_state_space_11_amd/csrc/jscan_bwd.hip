@@ -19,8 +19,10 @@
 //
 // Work decomposition (one lane per channel, 64 channels per wave, as in the
 // forward):
-// 1. Forward chunk starting states: the forward's chunk-local pass and
-//    combine (chunked plans only).
+// 1. Records of the forward's chunk-local pass and combine (chunked plans
+//    only): the chunk-local state at every sub-chunk boundary and the true
+//    state before every forward chunk, from which the forward sweep of
+//    step 4 derives its sub-chunk's starting state.
 // 2. Chunk-local adjoint (k_adj_local): every chunk but the first runs the
 //    adjoint backwards from mu = 0 over its tokens; its result M_c and the
 //    chunk's delta sum give the (decay, offset) pair of the chunk.
@@ -234,7 +236,10 @@ __global__ __launch_bounds__(256) void k_adj_combine(const float* __restrict__ A
 struct BwdArgs {
   const void* x; const void* delta; const float* A; const void* B; const void* C; const float* D;
   const void* z; const void* dy;
-  const float* hinit;     // hstart[b][c][n][d] (chunked) or h0[b][d][n] (single chunk), may be null
+  const float* h0;        // [b][d][n], may be null: the state before the first (sub-)chunk
+  SubRecords rec;         // sub-chunk boundary records and forward chunk starts (chunked plans)
+  int64_t fwd_len;        // tokens per forward chunk of the records
+  int fwd_chunks;
   const float* Min;       // slot c + 1 = adjoint entering chunk c (chunked plans)
   const float* dhT;
   void* dx; void* ddelta; void* dz;
@@ -244,7 +249,7 @@ struct BwdArgs {
   float* ck;               // [b][chunk][block][16][d] states before each kTok-token block
   int64_t L, d_inner, chunk_len;
   int n_chunks;
-  const int64_t* tag;      // the tag of the prefill whose chunk states hinit are (saved states), or null
+  const int64_t* tag;      // the tag of the prefill whose records `rec` are (saved states), or null
   Tag expect;              // the tag a plain prefill of these sizes and plan writes
 };
 
@@ -324,12 +329,26 @@ __global__ __launch_bounds__(64) void k_bwd_fwd(BwdArgs a, const T* __restrict__
   w.init<T>(a);
   float a2[NSTATE], h[NSTATE];
   load_a2(a2, a.A, w.d);
-  if (a.n_chunks > 1) {
-    const float* hi = a.hinit + ((w.b * a.n_chunks + w.c) * NSTATE) * a.d_inner + w.d;
+  if (a.n_chunks > 1 && w.c > 0) {
+    // The true state before sub-chunk c: its boundary's last token lies in
+    // forward chunk fc, which started from H[fc] (chunk 0 from h0, where the
+    // record is exact); the record holds the chunk-local state there and the
+    // delta sum since fc's start.
+    const int64_t slot = w.b * a.n_chunks + w.c - 1;
+    const int64_t fc = (uint32_t)(w.c * a.chunk_len - 1) / (uint32_t)a.fwd_len;   // 32-bit: below L < 2^31
+    const float* S = a.rec.sS + (slot * NSTATE) * a.d_inner + w.d;
+    if (fc == 0) {
 #pragma unroll
-    for (int n = 0; n < NSTATE; ++n) h[n] = hi[(int64_t)n * a.d_inner];
+      for (int n = 0; n < NSTATE; ++n) h[n] = S[(int64_t)n * a.d_inner];
+    } else {
+      const float lsum = a.rec.sL[slot * a.d_inner + w.d];
+      const float* Hc = a.rec.H + ((w.b * a.fwd_chunks + fc) * NSTATE) * a.d_inner + w.d;
+#pragma unroll
+      for (int n = 0; n < NSTATE; ++n)
+        h[n] = fmaf(fast_exp2(a2[n] * lsum), Hc[(int64_t)n * a.d_inner], S[(int64_t)n * a.d_inner]);
+    }
   } else {
-    const float* hi = a.hinit ? a.hinit + (w.b * a.d_inner + w.d) * NSTATE : nullptr;
+    const float* hi = a.h0 ? a.h0 + (w.b * a.d_inner + w.d) * NSTATE : nullptr;
 #pragma unroll
     for (int n = 0; n < NSTATE; ++n) h[n] = hi ? hi[n] : 0.0f;
   }
@@ -631,12 +650,11 @@ __global__ __launch_bounds__(256) void k_copy_or_zero(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ host
-// Backward workspace: the sub-chunk starting states (the backward's chunks
-// are the plan's sub-chunks), then the records a prefill would have left
-// (written here only when they are recomputed), then the adjoint carries,
-// state checkpoints and partial sums.
+// Backward workspace: the records a prefill would have left (written here
+// only when they are recomputed; the backward's chunks are the plan's
+// sub-chunks), then the adjoint carries, state checkpoints and partial sums.
 struct BwdLayout {
-  size_t hs, fwd, M, dsum, ck, dBp, dCp, dAp, dDp, total;
+  size_t fwd, M, dsum, ck, dBp, dCp, dAp, dDp, total;
 };
 
 BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
@@ -649,7 +667,6 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   // backward reusing one needs jscan_prefill_workspace_size() bytes less
   w.fwd = ws_layout(batch, L, d_inner, p).total + rms_bytes(batch * L);
   if (p.subs > 1) {
-    w.hs = round_up(B * C * NSTATE * Dn * 4);
     w.M = round_up(B * C * NSTATE * Dn * 4);
     w.dsum = round_up(B * C * Dn * 4);
   }
@@ -658,7 +675,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t d_inner, const Plan& p) {
   w.dCp = w.dBp;
   w.dAp = round_up(B * C * NSTATE * Dn * 4);
   w.dDp = round_up(B * C * Dn * 4);
-  w.total = w.hs + w.fwd + w.M + w.dsum + w.ck + w.dBp + w.dCp + w.dAp + w.dDp;
+  w.total = w.fwd + w.M + w.dsum + w.ck + w.dBp + w.dCp + w.dAp + w.dDp;
   return w;
 }
 
@@ -669,12 +686,11 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
                           float* dA, float* dB, float* dC, float* dD, float* dh0, char* ws,
                           const char* saved, const Plan& p, hipStream_t st) {
   const BwdLayout w = bwd_layout(batch, L, d_inner, p);
-  // The sub-chunk starting states, derived from the records a prefill left
-  // in its workspace (`saved`) or from records recomputed into this one.
-  // (records are recomputed, and need their region, only without saved ones
-  // and with more than one sub-chunk)
+  // The forward sweep derives each sub-chunk's starting state from the
+  // records a prefill left in its workspace (`saved`) or from records
+  // recomputed into this one (which need their region only without saved
+  // ones and with more than one sub-chunk).
   char* q = ws;
-  float* hstart = reinterpret_cast<float*>(q); q += w.hs;
   char* rec = !saved && p.subs > 1 ? q : nullptr;
   if (rec) q += w.fwd;
   float* M = reinterpret_cast<float*>(q); q += w.M;
@@ -689,8 +705,9 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
   hipError_t e;
   jscan_status s;
 
+  SubRecords recs{};
   if (chunks > 1) {
-    if ((s = sub_chunk_starts(io, batch, L, d_inner, x, delta, A, B, h0, rec, saved, hstart, p, st)) != JSCAN_OK)
+    if ((s = backward_records(io, batch, L, d_inner, x, delta, A, B, h0, rec, saved, p, st, &recs)) != JSCAN_OK)
       return s;
     dim3 g1((unsigned)((d_inner + 255) / 256), (unsigned)(chunks - 1), (unsigned)batch);
     hipLaunchKernelGGL((k_adj_local<T>), g1, dim3(256), 0, st, static_cast<const T*>(delta), A,
@@ -701,7 +718,7 @@ jscan_status run_backward(int64_t batch, int64_t L, int64_t d_inner, jscan_io io
     hipLaunchKernelGGL(k_adj_combine, g2, dim3(256), 0, st, A, dsum, dhT, M, d_inner, chunks);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "adjoint combine launch");
   }
-  const BwdArgs args{x, delta, A, B, C, D, z, dy, chunks > 1 ? hstart : h0, M, dhT, dx, ddelta, dz, dBp, dCp,
+  const BwdArgs args{x, delta, A, B, C, D, z, dy, h0, recs, p.chunk_len, p.chunks, M, dhT, dx, ddelta, dz, dBp, dCp,
                      dAp, dDp, dh0, ck, L, d_inner, p.sub_len, chunks,
                      saved ? reinterpret_cast<const int64_t*>(saved) : nullptr, make_tag(batch, L, d_inner, p, 0)};
   dim3 g3((unsigned)G, (unsigned)chunks, (unsigned)batch);
