@@ -223,6 +223,37 @@ def test_step_fused_matches_oracle_steps():
         assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
 
 
+def test_step_fused_full_size():
+    """The fused decode step at the decode workload's size, 256 sequences x
+    8192 channels (conv(4) + SiLU with its history in place, softplus with
+    dt_bias): three chained steps, every output, the state and the history
+    against the oracle."""
+    print_case("fused decode 256 x 8192")
+    n_seq, d = 256, 8192
+    pro = synth.prologue_params(d, 4, seed=33, batch=n_seq)
+    A, D, _ = synth.params(d, seed=33)
+    st64 = synth.decode_state(n_seq, d, seed=33).astype(np.float64)
+    cs64 = pro["conv_state"].astype(np.float64)
+    state = dev_f32(synth.decode_state(n_seq, d, seed=33))
+    cs = dev_f32(pro["conv_state"])
+    tA, tD = dev_f32(A), dev_f32(D)
+    kw = dict(conv_weight=dev_f32(pro["conv_weight"]), conv_bias=dev_f32(pro["conv_bias"]),
+              dt_bias=dev_f32(pro["dt_bias"]), softplus=True)
+    for k in range(3):
+        s = synth.decode_inputs(n_seq, d, seed=33, step=k)
+        s["delta"] = synth.raw_time_steps(n_seq, 1, d, seed=600 + k)[:, 0, :]
+        xc, dt, cs64 = oracle.prologue(synth.widen(s["x"])[:, None, :], synth.widen(s["delta"])[:, None, :],
+                                       pro["conv_weight"], pro["conv_bias"], cs64, pro["dt_bias"], True)
+        yr, st64 = oracle.step(st64, xc[:, 0, :], dt[:, 0, :], A.astype(np.float64), synth.widen(s["B"]),
+                               synth.widen(s["C"]), D.astype(np.float64), synth.widen(s["z"]))
+        t = {key: dev_io(s[key]) for key in ("x", "delta", "z", "B", "C")}
+        y = js.step_batch_fused(state, t["x"], t["delta"], tA, t["B"], t["C"], tD, t["z"], conv_state=cs, **kw)
+        torch.cuda.synchronize()
+        assert_y(y, yr, bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+        assert np.array_equal(host64(cs), cs64), f"conv state step {k}"
+
+
 @pytest.mark.parametrize("n_seq,d", [(1, 1), (1, 8), (7, 1), (300, 3), (2, 65)])
 @pytest.mark.parametrize("fused", [False, True])
 def test_step_edge_sizes(n_seq, d, fused):

@@ -198,6 +198,37 @@ def test_trap_step_edge_sizes(n_seq, d):
         assert_state(state, st64, f"state step {k}")
 
 
+def test_trap_step_full_size():
+    """The trapezoidal decode step at the decode workload's size, 256
+    sequences x 8192 channels, lam and the previous token given: three
+    chained steps (each step's previous token is the one before it), every
+    output and the state against the oracle's one-token prefill."""
+    n_seq, T, d = 256, 3, 8192
+    print_case(f"trap decode {n_seq} x {d}")
+    inp, lam, xp, Bp, dtb = problem(n_seq, T, d, seed=47, io=synth.IO_BF16, softplus=True)
+    o = oracle_inputs(inp)
+    state = dev_f32(inp["h0"])
+    st64 = inp["h0"].astype(np.float64)
+    t = to_device(inp)
+    tl = dev_io(lam)
+    tok = lambda v, k: v[:, k].clone()
+    for k in range(T):
+        x_prev = synth.widen(xp) if k == 0 else o["x"][:, k - 1]
+        B_prev = synth.widen(Bp) if k == 0 else o["B"][:, k - 1]
+        _, dt, _ = oracle.prologue(o["x"][:, k:k + 1], o["delta"][:, k:k + 1], dt_bias=dtb, softplus=True)
+        yr, st64, _, _ = oracle.prefill_trap(o["x"][:, k:k + 1], dt, o["A"], o["B"][:, k:k + 1], o["C"][:, k:k + 1],
+                                             o["D"], o["z"][:, k:k + 1], st64, lam=synth.widen(lam[:, k:k + 1]),
+                                             x_prev=x_prev, B_prev=B_prev)
+        gx_prev = dev_io(xp) if k == 0 else tok(t["x"], k - 1)
+        gB_prev = dev_io(Bp) if k == 0 else tok(t["B"], k - 1)
+        y = js.step_batch_trap(state, tok(t["x"], k), tok(t["delta"], k), t["A"], tok(t["B"], k), tok(t["C"], k),
+                               t["D"], tok(t["z"], k), lam=tok(tl, k), x_prev=gx_prev, B_prev=gB_prev,
+                               dt_bias=dev_f32(dtb), softplus=True)
+        torch.cuda.synchronize()
+        assert_y(y, yr[:, 0], bf16=True, what=f"y step {k}")
+        assert_state(state, st64, f"state step {k}")
+
+
 def test_trap_64k_sampled():
     """The 64K-token prefill (batch 1, d_inner 8192, bf16) with lam and the
     token before the first, automatic plan; 24 sampled channels over all tokens."""
